@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs for paged decode: host block manager plus workload
+generators.  Shared by the tests, the benchmark and the smoke check; holds no
+attention arithmetic."""
+
+from .blockmgr import BlockManager, OutOfPages  # noqa: F401
+from .configs import (  # noqa: F401
+    NAMED, Workload, beam_fork, by_name, chunk_elems, copy_probe, llama3_70b,
+    llama3_8b, long_context, make_tensors, prefix_share, tiny,
+)
