@@ -1,0 +1,277 @@
+"""Benchmark: one paged-decode step per iteration on one MI355X.
+
+A step is the whole data-parallel path over one synthetic batch: the KV
+append of every sequence's newest token, then paged decode attention over all
+cached tokens (split path: partition kernel + merge kernel).  Inputs are
+resident in HBM before timing starts.
+
+Default workload: the Llama-3-8B-shaped layer -- 64 sequences, 32 query / 8
+kv heads, head_dim 128, block 16, bf16, context lengths uniform in
+[512, 4096], pool = pages needed + 10 %, page ids randomly permuted.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is KV bytes read per step (every context
+token's K and V row once per kv head) divided by the wall time per step.
+`roofline` measures the dominant kernel alone with HIP events on the stream
+the library launches on.  `cpu_baseline` times the float64 oracle on the
+host, on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published peak
+METRIC = "paged-decode KV GB/s read (% of MI355X HBM peak) and decode seqs/sec"
+
+
+def _args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the library default (0 default, -1 single pass)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle baseline sample")
+    return ap.parse_args(argv)
+
+
+def _src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_350_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_name, workload, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _host(t):
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_baseline(w, t, target_s):
+    """Oracle (float64, host) over whole sequences of the batch until about
+    `target_s` seconds of CPU work; BLAS limited to one thread."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:          # pragma: no cover - threadpoolctl missing
+        limiter = None
+    import torch
+    bs = w.block_size
+    q = _host(t["q"])
+    kc_dev, vc_dev = t["k_cache"], t["v_cache"]
+    done, nbytes = 0, 0
+    elapsed = 0.0
+    order = list(range(w.num_seqs))
+    rounds = 0
+    while elapsed < target_s and rounds < 50:
+        for b in order:
+            L = int(w.context_lens[b])
+            n = -(-L // bs)
+            pages = w.block_tables[b, :n].astype(np.int64)
+            idx = torch.from_numpy(pages).to(kc_dev.device)
+            kc = _host(kc_dev.index_select(0, idx))
+            vc = _host(vc_dev.index_select(0, idx))
+            table = np.arange(n, dtype=np.int32)[None]
+            t0 = time.perf_counter()
+            oracle.decode(q[b:b + 1], kc, vc, table, w.context_lens[b:b + 1], w.scale, bs, w.dtype)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            nbytes += L * w.kv_bytes_per_token()
+            if elapsed >= target_s:
+                break
+        rounds += 1
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {
+        "value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s",
+        "seqs_per_s": round(done / elapsed, 3), "cores": 1, "kind": "oracle",
+        "sample": f"{done} whole sequences of the {w.name} batch ({nbytes / 1e6:.1f} MB of KV), "
+                  f"float64 numpy oracle, one BLAS thread, {elapsed:.1f} s of CPU time",
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def stream_read_gbps(torch, nbytes=2 << 30, reps=10):
+    """Achievable-read reference: torch's sum over a 2 GiB bf16 buffer."""
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        x.sum()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        x.sum()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del x
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def main(argv=None) -> int:
+    a = _args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not "
+                                   "part of this build (see the design notes on sharding)",
+                          "n_gpus": a.gpus}), flush=True)
+        return 2
+
+    import torch
+    import paged_kv_cache_350_amd as pa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        return 1
+    pa.lib()
+    torch.cuda.set_device(0)
+    w = W.by_name(a.workload)
+    ps_req = w.partition_size if a.partition_size is None else a.partition_size
+    t = W.make_tensors(w, "cuda")
+    if len(w.copy_pairs):
+        pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
+    torch.cuda.synchronize()
+
+    P = pa.decode_partition_size(w.max_context_len, ps_req)
+    split = P > 0
+    out = torch.empty_like(t["q"])
+    ws = pa.make_workspace(t["q"], w.max_context_len, P) if split else None
+    kernel_name = "decode_mfma" if (a.kernel == "mfma" or (a.kernel == "auto" and w.dtype == "bf16")) \
+        else "decode_valu"
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+        if ev is not None:
+            ev[1].record(stream)
+        if split:
+            pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                t["context_lens"], w.scale, w.max_context_len, P, ws, kernel=a.kernel)
+            if ev is not None:
+                ev[2].record(stream)
+            pa.decode_reduce(ws, t["context_lens"], out, w.max_context_len, P)
+        else:
+            pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                      w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel)
+            if ev is not None:
+                ev[2].record(stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done, timing {a.steps} steps", file=sys.stderr, flush=True)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    main_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[3]) for e in events]))
+    kv_bytes = w.algorithmic_kv_bytes()
+    ms_per_step = wall * 1e3 / a.steps
+    gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    digest = _src_digest("decode_mfma.hip" if kernel_name == "decode_mfma" else "decode_valu.hip",
+                         "pa_device.h", "pa_internal.h")
+    achieved = kv_bytes / (main_ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": _traffic(kernel_name, w.name, digest),
+        "kernel": kernel_name + ("_partition" if split else "_single"),
+        "avg_launch_us": round(main_ms * 1e3, 2),
+        "algorithmic_bytes_per_launch": kv_bytes,
+        "source_digest": digest,
+    }
+    rec = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "decode_seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "config": {
+            "workload": w.name, "description": w.description, "num_seqs": w.num_seqs,
+            "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "sum_context_tokens": int(w.context_lens.sum()),
+            "max_context_len": w.max_context_len, "num_blocks": w.num_blocks,
+            "partition_size": P, "kernel": kernel_name, "seed": w.seed,
+            "kv_bytes_per_step": kv_bytes,
+        },
+        "kernels_avg_us": {
+            "kv_append": round(append_ms * 1e3, 2),
+            (kernel_name + ("_partition" if split else "_single")): round(main_ms * 1e3, 2),
+            "decode_reduce": round(reduce_ms * 1e3, 2) if split else None,
+            "decode_total": round(decode_ms * 1e3, 2),
+        },
+        "roofline": roofline,
+    }
+    try:
+        rec["stream_read_reference_gbps"] = round(stream_read_gbps(torch), 1)
+    except Exception as exc:       # pragma: no cover - informational only
+        rec["stream_read_reference_gbps"] = None
+        print(f"[bench] stream-read reference failed: {exc}", file=sys.stderr)
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, t, a.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

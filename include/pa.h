@@ -1,0 +1,235 @@
+/*
+ * pa.h -- paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every tensor argument is a plain
+ * device pointer owned by the caller; sizes are plain integers.  The library
+ * allocates no memory, keeps no mutable global state, never synchronises and
+ * never throws: every call validates its arguments on the host, then enqueues
+ * its kernels asynchronously on `stream` (NULL = the null stream) and returns.
+ *
+ * Pages cited (title, then section):
+ *   [Glossary]  "What is PagedAttention? Definition & Virtual Memory
+ *               Architecture" (esaholic.com AI glossary)
+ *   [Internals] "PagedAttention Internals: How Memory Fragmentation in LLM
+ *               Serving Was Solved" (dailyaiworld.com)
+ *
+ * The pages fix the idea -- K/V vectors live in fixed-size blocks of 16 or 32
+ * tokens scattered through one physical pool, a per-sequence block table maps
+ * logical block i to a physical page, and the attention kernel reads K/V
+ * through that table with no gather copy [Glossary, "Technical Architecture";
+ * Internals, "How PagedAttention Works" items 1-3] -- but no memory layout.
+ * The layouts below are this library's:
+ *
+ *   X = 16 / sizeof(element)        (8 for bf16, 4 for fp32)
+ *   k_cache  [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]
+ *   q, out   [num_seqs][num_heads][head_dim]
+ *   k, v     [num_tokens][num_kv_heads][head_dim]          (new rows to append)
+ *   block_tables [num_seqs][max_blocks_per_seq] int32      (physical page ids)
+ *   context_lens [num_seqs] int32                          (tokens to attend over)
+ *   slot_mapping [num_tokens] int64                        (page*block_size + offset)
+ *   block_mapping [num_pairs][2] int64                     (src page, dst page)
+ *
+ * Token t of sequence b lives in page block_tables[b][t / block_size] at
+ * offset t % block_size.  One (page, kv head) tile of K or V is one contiguous
+ * run of head_dim * block_size elements (4 KiB for bf16, head_dim 128,
+ * block 16).  All element types of one call are the same `pa_dtype`.
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {16, 32};
+ * num_heads a multiple of num_kv_heads with num_heads / num_kv_heads <= 16.
+ *
+ * Preconditions the library cannot check without reading device memory
+ * (violating them gives unspecified output, never an out-of-bounds access):
+ * table entries used by a sequence lie in [0, num_blocks); context_lens[b]
+ * lies in [0, max_context_len]; non-negative append slots are unique; the
+ * source and destination sets of a copy are disjoint and destinations are
+ * unique.  Device-side guards clamp or skip anything out of range, so a bad
+ * index never leaves the buffers the caller described.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL */
+    PA_ERR_ARG = -2,         /* a size or count is out of range or inconsistent */
+    PA_ERR_UNSUPPORTED = -3, /* valid request outside the shapes listed above */
+    PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+    PA_ERR_HIP = -5          /* the HIP runtime refused a launch */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F32 = 0,
+    PA_BF16 = 1
+} pa_dtype;
+
+/* Which decode kernel family runs.  AUTO picks the matrix-core kernel for
+ * bf16 and the vector-ALU kernel for fp32; the two compute the same thing. */
+typedef enum pa_kernel {
+    PA_KERNEL_AUTO = 0,
+    PA_KERNEL_VALU = 1,      /* vector ALU (fp32 and bf16) */
+    PA_KERNEL_MFMA = 2       /* MFMA matrix cores for Q.K^T and P.V (bf16 only) */
+} pa_kernel;
+
+/* Human-readable text for a status code; never NULL, static storage. */
+const char* pa_status_string(pa_status status);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t pa_version(void);
+
+/*
+ * pa_kv_append -- write each new token's key and value rows into its slot.
+ *
+ * For every token i with slot_mapping[i] >= 0: page = slot / block_size,
+ * off = slot % block_size, and for every kv head h the row k[i][h][:] is
+ * copied into k_cache at (page, h, :, off, :) and v[i][h][:] into v_cache at
+ * (page, h, :, off).  A bit copy: no conversion, NaN payloads preserved.
+ * Negative slots are skipped (padding).  Slots >= num_blocks * block_size are
+ * skipped as well (out of range; documented precondition violation).
+ * [Internals, "How PagedAttention Works" item 2: pages come from the pool on
+ * demand as tokens are generated; Glossary, page-table figure: a token's
+ * place is its page plus its offset inside the block]
+ *
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim], read
+ *   slot_mapping  device, [num_tokens] int64, read
+ *   k_cache/v_cache device, layouts above, written at the given slots only
+ *   num_blocks    pool size in pages (bounds the slots)
+ * Returns PA_OK (num_tokens == 0 is a no-op), PA_ERR_NULL, PA_ERR_ARG,
+ * PA_ERR_UNSUPPORTED or PA_ERR_HIP.
+ */
+pa_status pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache,
+                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                       hipStream_t stream);
+
+/*
+ * pa_decode -- one decode step of paged attention.
+ *
+ * For each sequence b (L = context_lens[b]) and query head h
+ * (kv head g = h / (num_heads / num_kv_heads)):
+ *     s_t = scale * q[b][h] . K_b[t][g]            for t in [0, L)
+ *     out[b][h] = sum_t softmax(s)_t * V_b[t][g]
+ * where K_b[t], V_b[t] are read in place from page block_tables[b][t / bs]
+ * at offset t % bs.  L == 0 writes zeros.  Accumulation is fp32; the output
+ * is rounded once (round-to-nearest-even for bf16).
+ * [Internals, "How PagedAttention Works" item 3 (the fused kernel fetches
+ * non-contiguous K/V through the block table and runs scaled dot-product
+ * attention); Glossary, "On-the-Fly CUDA Block Fetching"]
+ *
+ * Long contexts are cut into partitions of `partition_size` tokens processed
+ * by independent workgroups, each leaving its running max, running sum and
+ * unnormalised accumulator in `workspace`; a second kernel merges them.
+ *
+ *   q             device, [num_seqs][num_heads][head_dim], read
+ *   k_cache/v_cache device, layouts above, read
+ *   block_tables  device, [num_seqs][max_blocks_per_seq] int32, read
+ *   context_lens  device, [num_seqs] int32, read
+ *   block_size    16 or 32;  num_kv_heads: kv heads per page
+ *   scale         multiplies q . k (typically 1/sqrt(head_dim))
+ *   out           device, [num_seqs][num_heads][head_dim], written
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid;
+ *                 no device-to-host read is ever made)
+ *   num_blocks    pool size in pages (device-side guard on table entries)
+ *   partition_size 0 = library default, -1 = single pass (one workgroup per
+ *                 sequence and kv head), otherwise a multiple of 32 >= 32
+ *   kernel        PA_KERNEL_AUTO / _VALU / _MFMA
+ *   workspace     device scratch of at least pa_decode_workspace_size(...)
+ *                 bytes when the split path runs (may be NULL otherwise);
+ *                 owned by the caller, contents undefined afterwards
+ * Returns PA_OK (num_seqs == 0 is a no-op), PA_ERR_NULL, PA_ERR_ARG,
+ * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE or PA_ERR_HIP.
+ */
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t block_size, int32_t num_kv_heads, float scale,
+                    void* out, hipStream_t stream,
+                    int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                    pa_kernel kernel, void* workspace, size_t workspace_bytes);
+
+/*
+ * Partition size pa_decode uses for a request: > 0 = split path with that
+ * many tokens per partition, 0 = single pass, < 0 = invalid request
+ * (PA_ERR_ARG).  Pure host arithmetic.
+ */
+int32_t pa_decode_partition_size(int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Workspace bytes pa_decode needs (0 for the single pass):
+ * num_seqs * num_heads * ceil(max_context_len / P) * (head_dim + 2) * 4,
+ * P = pa_decode_partition_size(max_context_len, partition_size).
+ * Returns 0 for invalid arguments as well.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode_partition -- first stage of the split path on its own: every
+ * (sequence, kv head, partition) workgroup writes its partials to
+ * `workspace` (fp32 running max in log2 units, running sum, unnormalised
+ * accumulator).  Together with pa_decode_reduce it is exactly what
+ * pa_decode does when partition_size > 0; callers that merge partials
+ * themselves (for example a context split across devices) use the two
+ * stages directly.  partition_size must be given explicitly here (a
+ * multiple of 32, > 0); size the workspace with pa_decode_workspace_size()
+ * for that same partition_size.  max_context_len == 0 launches nothing.
+ * Arguments otherwise as for pa_decode.
+ */
+pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t block_size, int32_t num_kv_heads, float scale,
+                              hipStream_t stream,
+                              int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                              pa_kernel kernel, void* workspace, size_t workspace_bytes);
+
+/*
+ * pa_decode_reduce -- second stage: merge the partitions of every
+ * (sequence, head) with M = max_p m_p,
+ *     out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+ * and round once to the output dtype.  Sequences with L == 0 get zeros.
+ * `workspace` must hold what pa_decode_partition wrote for the same
+ * num_seqs, num_heads, head_dim, max_context_len and partition_size (> 0).
+ */
+pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
+                           const int32_t* context_lens, void* out, hipStream_t stream,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_context_len, int32_t partition_size, pa_dtype dtype);
+
+/*
+ * pa_copy_blocks -- copy whole pages (K and V, every kv head) for
+ * copy-on-write forks: page block_mapping[i][1] becomes a bit-exact copy of
+ * page block_mapping[i][0].  Pairs act as if applied at once (sources and
+ * destinations must be disjoint, destinations unique).  Pairs naming a page
+ * outside [0, num_blocks) are skipped.
+ * [Glossary, "Copy-on-Write Memory Forking"; Internals, "Copy-on-Write and
+ * Prefix Sharing": a request that starts writing its own tokens gets a page
+ * of its own]
+ *
+ *   k_cache/v_cache device, layouts above, read and written
+ *   block_mapping device, [num_pairs][2] int64 (src, dst), read
+ * Returns PA_OK (num_pairs == 0 is a no-op), PA_ERR_NULL, PA_ERR_ARG,
+ * PA_ERR_UNSUPPORTED or PA_ERR_HIP.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,14 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+The compute lives in libpa.so (hand-written HIP kernels behind the C ABI in
+include/pa.h); this package is the thin Python binding that tests and the
+benchmark call.  Build the library with
+``python -m paged_kv_cache_350_amd.build``.
+"""
+
+from ._binding import (  # noqa: F401
+    KERNELS, LIB_PATH, PA_BF16, PA_ERR_ARG, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_UNSUPPORTED,
+    PA_ERR_WORKSPACE, PA_F32, PA_OK, PaError, copy_blocks, decode, decode_partition,
+    decode_partition_size, decode_reduce, decode_workspace_size, kv_append, lib,
+    make_workspace, status_string,
+)

@@ -1,0 +1,238 @@
+"""Thin ctypes binding over libpa.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks that
+their dtypes, shapes and devices agree with the C ABI in include/pa.h, and
+passes raw device pointers plus the current torch stream to the library.  No
+arithmetic of the method happens here; there is no fallback path -- if the
+library is missing or the GPU is absent the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_OK, PA_ERR_NULL, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4, -5
+PA_F32, PA_BF16 = 0, 1
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+_lock = threading.Lock()
+_lib_handle: Optional[ctypes.CDLL] = None
+
+
+class PaError(RuntimeError):
+    """A libpa call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+_c_int, _c_i64, _c_size, _c_float, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                          ctypes.c_float, ctypes.c_void_p)
+
+_SIGNATURES = {
+    "pa_status_string": ([_c_int], ctypes.c_char_p),
+    "pa_version": ([], _c_int),
+    "pa_decode_partition_size": ([_c_int, _c_int], _c_int),
+    "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
+    "pa_kv_append": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
+    "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
+                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                   _vp, _c_size], _c_int),
+    "pa_decode_partition": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp,
+                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                             _vp, _c_size], _c_int),
+    "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
+                         _c_int),
+    "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (once).  Raises if it has not been built."""
+    global _lib_handle
+    with _lock:
+        if _lib_handle is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"libpa.so not found at {LIB_PATH}; build it with "
+                    "`python -m paged_kv_cache_350_amd.build`")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib_handle = handle
+    return _lib_handle
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PaError(fn, status, status_string(status))
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dtype=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+
+
+def _elem_dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported element type {t.dtype} (float32 or bfloat16)")
+    return _DTYPES[t.dtype]
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """(num_blocks, num_kv_heads, head_dim, block_size) from the two cache tensors."""
+    _dev_tensor("k_cache", k_cache, ndim=5)
+    _dev_tensor("v_cache", v_cache, dtype=k_cache.dtype, ndim=4)
+    nb, hkv, nchunk, bs, x = k_cache.shape
+    if x * k_cache.element_size() != 16:
+        raise ValueError("k_cache innermost axis must span 16 bytes")
+    d = nchunk * x
+    if tuple(v_cache.shape) != (nb, hkv, d, bs):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache "
+                         f"(expected {(nb, hkv, d, bs)})")
+    if k_cache.device != v_cache.device:
+        raise ValueError("caches on different devices")
+    return nb, hkv, d, bs
+
+
+def decode_partition_size(max_context_len: int, partition_size: int = 0) -> int:
+    return lib().pa_decode_partition_size(max_context_len, partition_size)
+
+
+def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                          partition_size: int = 0) -> int:
+    return lib().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                          partition_size)
+
+
+def kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+              k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter new K/V rows [T, Hkv, D] into their slots (in place on the caches)."""
+    nb, hkv, d, bs = _cache_dims(k_cache, v_cache)
+    _dev_tensor("k", k, dtype=k_cache.dtype, ndim=3)
+    _dev_tensor("v", v, dtype=k_cache.dtype, ndim=3)
+    _dev_tensor("slot_mapping", slot_mapping, dtype=torch.int64, ndim=1)
+    T = k.shape[0]
+    if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d) or slot_mapping.shape[0] != T:
+        raise ValueError("k, v, slot_mapping shapes disagree with the caches")
+    st = lib().pa_kv_append(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                            k_cache.data_ptr(), v_cache.data_ptr(), T, hkv, d, bs, nb,
+                            _elem_dtype(k_cache), _stream(k_cache))
+    _check("pa_kv_append", st)
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy whole pages src -> dst for each row (src, dst) of block_mapping [n, 2]."""
+    nb, hkv, d, bs = _cache_dims(k_cache, v_cache)
+    _dev_tensor("block_mapping", block_mapping, dtype=torch.int64, ndim=2)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n, 2]")
+    st = lib().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
+                              block_mapping.shape[0], hkv, d, bs, nb, _elem_dtype(k_cache),
+                              _stream(k_cache))
+    _check("pa_copy_blocks", st)
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len):
+    nb, hkv, d, bs = _cache_dims(k_cache, v_cache)
+    _dev_tensor("q", q, dtype=k_cache.dtype, ndim=3)
+    _dev_tensor("block_tables", block_tables, dtype=torch.int32, ndim=2)
+    _dev_tensor("context_lens", context_lens, dtype=torch.int32, ndim=1)
+    B, hq, dq = q.shape
+    if dq != d:
+        raise ValueError(f"q head_dim {dq} != cache head_dim {d}")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens batch size disagrees with q")
+    if max_context_len is None:
+        raise ValueError("max_context_len (a host-side bound on context_lens) is required")
+    return nb, hkv, d, bs, B, hq
+
+
+def make_workspace(q: torch.Tensor, max_context_len: int, partition_size: int = 0):
+    """Allocate the split-path workspace (or None) for a decode call."""
+    B, hq, d = q.shape
+    n = decode_workspace_size(B, hq, d, max_context_len, partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n // 4, dtype=torch.float32, device=q.device)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           max_context_len: int, out: Optional[torch.Tensor] = None, partition_size: int = 0,
+           kernel: str = "auto", workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode attention; returns out [B, Hq, D] in q's dtype."""
+    nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dtype=q.dtype, ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if workspace is None:
+        workspace = make_workspace(q, max_context_len, partition_size)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().pa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                         block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv, float(scale),
+                         out.data_ptr(), _stream(q), B, hq, d, block_tables.shape[1],
+                         int(max_context_len), nb, _elem_dtype(q), int(partition_size),
+                         KERNELS[kernel], ws_ptr, ws_bytes)
+    _check("pa_decode", st)
+    return out
+
+
+def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                     max_context_len: int, partition_size: int, workspace: torch.Tensor,
+                     kernel: str = "auto") -> None:
+    """First stage of the split path only (partials into ``workspace``)."""
+    nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len)
+    _dev_tensor("workspace", workspace, dtype=torch.float32)
+    st = lib().pa_decode_partition(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,
+                                   float(scale), _stream(q), B, hq, d, block_tables.shape[1],
+                                   int(max_context_len), nb, _elem_dtype(q), int(partition_size),
+                                   KERNELS[kernel], workspace.data_ptr(), workspace.numel() * 4)
+    _check("pa_decode_partition", st)
+
+
+def decode_reduce(workspace: torch.Tensor, context_lens: torch.Tensor, out: torch.Tensor,
+                  max_context_len: int, partition_size: int) -> torch.Tensor:
+    """Second stage of the split path: merge partials into ``out`` [B, Hq, D]."""
+    _dev_tensor("workspace", workspace, dtype=torch.float32)
+    _dev_tensor("context_lens", context_lens, dtype=torch.int32, ndim=1)
+    _dev_tensor("out", out, ndim=3)
+    B, hq, d = out.shape
+    st = lib().pa_decode_reduce(workspace.data_ptr(), workspace.numel() * 4, context_lens.data_ptr(),
+                                out.data_ptr(), _stream(out), B, hq, d, int(max_context_len),
+                                int(partition_size), _elem_dtype(out))
+    _check("pa_decode_reduce", st)
+    return out

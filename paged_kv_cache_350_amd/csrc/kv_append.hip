@@ -1,0 +1,74 @@
+// KV-append scatter: each new token's K and V rows go to the slot its
+// sequence's block table gives it (page * block_size + offset).
+// [PagedAttention Internals, "How PagedAttention Works" item 2: pages are
+// taken on demand as the model generates tokens; What is PagedAttention?,
+// page-table figure: a token's place is its page plus its offset]
+//
+// One wavefront per (token, kv head) row pair.  The K row moves as 16-byte
+// chunks (one lane per chunk) into k_cache[page][h][chunk][off][:]; the V row
+// moves element by element into v_cache[page][h][d][off] (dim-major pages,
+// so the strided stores land inside one 4-8 KiB page tile).  Pure bit copy.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa_impl {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;   // four wavefronts, one row pair each
+
+template <typename E>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void kv_append_kernel(const E* __restrict__ k, const E* __restrict__ v,
+                      const int64_t* __restrict__ slot_mapping,
+                      E* __restrict__ k_cache, E* __restrict__ v_cache,
+                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    if (row >= (int64_t)num_tokens * num_kv_heads) return;
+    const int64_t tok = row / num_kv_heads;
+    const int h = (int)(row % num_kv_heads);
+    const int64_t slot = slot_mapping[tok];
+    if (slot < 0 || slot >= num_blocks * block_size) return;   // padding / out of range
+    const int64_t page = slot / block_size;
+    const int off = (int)(slot % block_size);
+
+    constexpr int X = 16 / sizeof(E);          // elements per 16-byte chunk
+    const int nchunk = head_dim / X;
+    const E* krow = k + row * head_dim;
+    const E* vrow = v + row * head_dim;
+    const int64_t tile = (page * num_kv_heads + h) * (int64_t)head_dim * block_size;
+
+    if (lane < nchunk) {
+        st16(k_cache + tile + ((int64_t)lane * block_size + off) * X, ld16(krow + lane * X));
+    }
+    for (int d = lane; d < head_dim; d += kWave) {
+        v_cache[tile + (int64_t)d * block_size + off] = vrow[d];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slot_mapping,
+                            void* k_cache, void* v_cache, int32_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+    const int64_t rows = (int64_t)num_tokens * num_kv_heads;
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    const dim3 block(kRowsPerBlock * kWave);
+    if (dtype == PA_BF16) {
+        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, block, 0, stream,
+                           (const uint16_t*)k, (const uint16_t*)v, slot_mapping,
+                           (uint16_t*)k_cache, (uint16_t*)v_cache, num_tokens,
+                           num_kv_heads, head_dim, block_size, num_blocks);
+    } else {
+        hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, block, 0, stream,
+                           (const uint32_t*)k, (const uint32_t*)v, slot_mapping,
+                           (uint32_t*)k_cache, (uint32_t*)v_cache, num_tokens,
+                           num_kv_heads, head_dim, block_size, num_blocks);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pa_impl

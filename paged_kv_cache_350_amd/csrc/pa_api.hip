@@ -1,0 +1,300 @@
+// Host side of libpa: argument validation, path selection and launches.
+// Every entry point validates on the host before any HIP call, then enqueues
+// asynchronously on the caller's stream.  Nothing is allocated, nothing is
+// synchronised, no exception leaves the library.
+#include <math.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+using pa_impl::DecodeParams;
+using pa_impl::ReduceParams;
+
+namespace {
+
+constexpr int32_t kDefaultPartition = 512;   // tokens per partition on the split path
+constexpr int32_t kChunk = 32;               // partitions are whole 32-token chunks
+constexpr int32_t kMaxGroup = 16;            // query heads per kv head
+constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+
+size_t elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+
+pa_status shape_status(int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+    if (num_kv_heads <= 0) return PA_ERR_ARG;
+    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+int32_t resolve_partition(int32_t max_context_len, int32_t partition_size) {
+    if (max_context_len < 0) return -1;
+    if (partition_size == -1) return 0;
+    if (partition_size == 0) return max_context_len > kDefaultPartition ? kDefaultPartition : 0;
+    if (partition_size < kChunk || partition_size % kChunk != 0) return -1;
+    return partition_size;
+}
+
+int32_t parts_for(int32_t max_context_len, int32_t partition) {
+    return (int32_t)(((int64_t)max_context_len + partition - 1) / partition);
+}
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_context_len, int32_t partition) {
+    if (partition <= 0) return 0;
+    const int32_t parts = parts_for(max_context_len, partition);
+    return pa_impl::ws_rows(num_seqs, num_heads, parts) * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+struct Plan {
+    DecodeParams p;
+    pa_dtype dtype;
+    bool use_mfma;
+    int32_t partition;   // 0 = single pass
+};
+
+// Shared validation of pa_decode / pa_decode_partition.  Returns PA_OK with
+// `plan` filled, or the first error found.  `need_out` is false for the
+// partition-only stage; `force_split` requires the split path.
+pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t block_size, int32_t num_kv_heads, float scale, void* out,
+                    int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                    pa_dtype dtype, int32_t partition_size, pa_kernel kernel, void* workspace,
+                    size_t workspace_bytes, bool need_out, bool force_split, Plan* plan) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
+        return PA_ERR_ARG;
+    pa_status st = shape_status(num_kv_heads, head_dim, block_size);
+    if (st != PA_OK) return st;
+    if (num_heads <= 0 || num_heads % num_kv_heads != 0) return PA_ERR_ARG;
+    if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0) return PA_ERR_ARG;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_ARG;
+    if (num_blocks > (int64_t)INT32_MAX + 1) return PA_ERR_ARG;      // table entries are int32
+    if (!isfinite(scale)) return PA_ERR_ARG;
+    int32_t partition = resolve_partition(max_context_len, partition_size);
+    if (partition < 0) return PA_ERR_ARG;
+    if (force_split && partition <= 0) return PA_ERR_ARG;
+    if (!force_split && partition > 0 && max_context_len == 0) partition = 0;   // nothing to split
+    if (kernel == PA_KERNEL_MFMA && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 0) return PA_ERR_ARG;
+
+    plan->dtype = dtype;
+    plan->partition = partition;
+    plan->use_mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && dtype == PA_BF16);
+    if (num_seqs == 0) return PA_OK;
+
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+    if (need_out && !out) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ARG;
+    if (need_out && !aligned16(out)) return PA_ERR_ARG;
+
+    const int32_t parts = partition > 0 ? parts_for(max_context_len, partition) : 1;
+    if ((uint64_t)num_seqs * (uint64_t)num_kv_heads * (uint64_t)parts >= kMaxGrid)
+        return PA_ERR_UNSUPPORTED;
+    if (partition > 0) {
+        const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, partition);
+        if (need > 0) {
+            if (!workspace) return PA_ERR_WORKSPACE;
+            if (!aligned16(workspace)) return PA_ERR_ARG;
+            if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+        }
+    }
+
+    DecodeParams& p = plan->p;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.ws = static_cast<float*>(workspace);
+    p.scale_log2 = scale * 1.4426950408889634f;     // log2(e): scores in log2 units
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.head_dim = head_dim;
+    p.block_size = block_size;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.num_blocks = num_blocks;
+    if (partition > 0) {
+        p.partition = partition;
+        p.max_parts = parts;
+        p.split = 1;
+    } else {
+        const int32_t whole = max_context_len < 1 ? 1 : max_context_len;
+        p.partition = (int32_t)(((int64_t)whole + kChunk - 1) / kChunk * kChunk);
+        p.max_parts = 1;
+        p.split = 0;
+    }
+    return PA_OK;
+}
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+pa_status launch_plan(const Plan& plan, hipStream_t stream) {
+    if ((uint64_t)plan.p.num_seqs * plan.p.num_kv_heads * plan.p.max_parts == 0) return PA_OK;
+    if (plan.use_mfma) return hip_status(pa_impl::launch_decode_mfma(plan.p, stream));
+    return hip_status(pa_impl::launch_decode_valu(plan.p, plan.dtype, stream));
+}
+
+pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out, hipStream_t stream) {
+    ReduceParams r;
+    r.ws = plan.p.ws;
+    r.context_lens = context_lens;
+    r.out = out;
+    r.num_seqs = plan.p.num_seqs;
+    r.num_heads = plan.p.num_heads;
+    r.head_dim = plan.p.head_dim;
+    r.max_context_len = plan.p.max_context_len;
+    r.partition = plan.p.partition;
+    r.max_parts = plan.p.max_parts;
+    return hip_status(pa_impl::launch_decode_reduce(r, plan.dtype, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "a required pointer is NULL";
+        case PA_ERR_ARG: return "invalid argument (size, count, alignment or option out of range)";
+        case PA_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128, block_size 16/32, "
+                                        "<= 16 query heads per kv head, bf16 for the MFMA kernel)";
+        case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_size()";
+        case PA_ERR_HIP: return "HIP runtime error while launching";
+    }
+    return "unknown status";
+}
+
+int32_t pa_version(void) { return 100; }
+
+int32_t pa_decode_partition_size(int32_t max_context_len, int32_t partition_size) {
+    return resolve_partition(max_context_len, partition_size);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0) return 0;
+    const int32_t partition = resolve_partition(max_context_len, partition_size);
+    if (partition <= 0) return 0;
+    return workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, partition);
+}
+
+pa_status pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache,
+                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                       hipStream_t stream) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    pa_status st = shape_status(num_kv_heads, head_dim, block_size);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0 || num_blocks <= 0) return PA_ERR_ARG;
+    if ((uint64_t)num_tokens * (uint64_t)num_kv_heads >= (1ull << 33)) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ARG;
+    return hip_status(pa_impl::launch_kv_append(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+                                                num_kv_heads, head_dim, block_size, num_blocks,
+                                                dtype, stream));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                         hipStream_t stream) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    pa_status st = shape_status(num_kv_heads, head_dim, block_size);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0 || num_blocks <= 0) return PA_ERR_ARG;
+    if (num_pairs >= (1 << 24)) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_kv_heads * head_dim * block_size * (int64_t)elem_bytes(dtype) > (1ll << 30))
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ARG;
+    return hip_status(pa_impl::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
+                                                  num_kv_heads, head_dim, block_size, num_blocks,
+                                                  dtype, stream));
+}
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t block_size, int32_t num_kv_heads, float scale,
+                    void* out, hipStream_t stream,
+                    int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                    pa_kernel kernel, void* workspace, size_t workspace_bytes) {
+    Plan plan;
+    pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                             num_kv_heads, scale, out, num_seqs, num_heads, head_dim,
+                             max_blocks_per_seq, max_context_len, num_blocks, dtype,
+                             partition_size, kernel, workspace, workspace_bytes,
+                             /*need_out=*/true, /*force_split=*/false, &plan);
+    if (st != PA_OK || num_seqs == 0) return st;
+    st = launch_plan(plan, stream);
+    if (st != PA_OK || plan.partition == 0) return st;
+    return launch_reduce(plan, context_lens, out, stream);
+}
+
+pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t block_size, int32_t num_kv_heads, float scale,
+                              hipStream_t stream,
+                              int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                              pa_kernel kernel, void* workspace, size_t workspace_bytes) {
+    if (partition_size <= 0) return PA_ERR_ARG;
+    Plan plan;
+    pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                             num_kv_heads, scale, nullptr, num_seqs, num_heads, head_dim,
+                             max_blocks_per_seq, max_context_len, num_blocks, dtype,
+                             partition_size, kernel, workspace, workspace_bytes,
+                             /*need_out=*/false, /*force_split=*/true, &plan);
+    if (st != PA_OK || num_seqs == 0) return st;
+    return launch_plan(plan, stream);
+}
+
+pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
+                           const int32_t* context_lens, void* out, hipStream_t stream,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_context_len, int32_t partition_size, pa_dtype dtype) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size <= 0) return PA_ERR_ARG;
+    const int32_t partition = resolve_partition(max_context_len, partition_size);
+    if (partition <= 0) return PA_ERR_ARG;
+    if ((uint64_t)num_seqs * (uint64_t)num_heads >= kMaxGrid) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!context_lens || !out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ARG;
+    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, partition);
+    if (need > 0) {
+        if (!workspace) return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PA_ERR_ARG;
+        if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    }
+    Plan plan;
+    plan.dtype = dtype;
+    plan.p.ws = static_cast<float*>(const_cast<void*>(workspace));
+    plan.p.num_seqs = num_seqs;
+    plan.p.num_heads = num_heads;
+    plan.p.head_dim = head_dim;
+    plan.p.max_context_len = max_context_len;
+    plan.p.partition = partition;
+    plan.p.max_parts = parts_for(max_context_len, partition);
+    return launch_reduce(plan, context_lens, out, stream);
+}
+
+}  // extern "C"

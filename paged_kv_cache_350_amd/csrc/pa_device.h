@@ -1,0 +1,54 @@
+// Device-side helpers shared by the libpa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa_impl {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, one L2 each
+
+// Reinterpret a 32-bit pattern as float.  Always goes through a scalar: a
+// bit cast applied directly to an element of a vector value (v[i]) has been
+// seen to read the wrong element with this compiler.
+__device__ __forceinline__ float u32_as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return u32_as_f32((uint32_t)h << 16); }
+
+// Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, (bf16_t)x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// 16-byte global load/store through a plain vector type.
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4_t v) {
+    *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+// Workgroups are handed to the XCDs round-robin (id i runs on XCD i % 8).
+// Map the hardware id to a logical id so that each XCD owns one contiguous
+// range of logical ids: work items adjacent in logical order (for example
+// the sequences sharing a prefix page) then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_local_order(uint32_t hw_id, uint32_t n) {
+    const uint32_t xcd = hw_id % kXcds;
+    const uint32_t k = hw_id / kXcds;
+    const uint32_t q0 = n / kXcds;
+    const uint32_t r = n % kXcds;          // the first r XCDs get one extra item
+    const uint32_t base = xcd < r ? xcd * (q0 + 1) : r * (q0 + 1) + (xcd - r) * q0;
+    return base + k;
+}
+
+}  // namespace pa_impl

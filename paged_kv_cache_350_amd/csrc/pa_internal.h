@@ -1,0 +1,70 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libpa.  Not installed; the public interface is include/pa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa_impl {
+
+// Everything a decode launch needs, resolved and validated on the host.
+struct DecodeParams {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    void* out;             // final output (single pass)
+    float* ws;             // partials (split): acc | m | l, see ws_* helpers
+    float scale_log2;      // scale * log2(e): scores are kept in log2 units
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t group;         // num_heads / num_kv_heads
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int64_t num_blocks;
+    int32_t partition;     // tokens per partition (single pass: covers max_context_len)
+    int32_t max_parts;     // partitions per (seq, head) in the workspace (1 = single pass)
+    int32_t split;         // 1: write partials to ws, 0: write out
+};
+
+struct ReduceParams {
+    const float* ws;
+    const int32_t* context_lens;
+    void* out;
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t head_dim;
+    int32_t max_context_len;
+    int32_t partition;
+    int32_t max_parts;
+};
+
+// Workspace layout for the split path (all fp32):
+//   acc [num_seqs][num_heads][max_parts][head_dim]   unnormalised accumulator
+//   m   [num_seqs][num_heads][max_parts]             running max (log2 units)
+//   l   [num_seqs][num_heads][max_parts]             running sum of 2^(s - m)
+__host__ __device__ inline size_t ws_rows(int32_t num_seqs, int32_t num_heads, int32_t max_parts) {
+    return (size_t)num_seqs * (size_t)num_heads * (size_t)max_parts;
+}
+
+hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slot_mapping,
+                            void* k_cache, void* v_cache, int32_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, pa_dtype dtype, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                              int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                              hipStream_t stream);
+
+hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype dtype, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_reduce(const ReduceParams& p, pa_dtype dtype, hipStream_t stream);
+
+}  // namespace pa_impl

@@ -13,3 +13,11 @@ if HERE not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) device and the built HIP library")
+
+
+@pytest.fixture(autouse=True)
+def _name_gpu_case(request):
+    """Print (and flush) the id of every GPU test before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield

@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports every symbol include/pa.h declares, and
+rejects bad arguments on the host (CPU only: no call here reaches the GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+pa = pytest.importorskip("paged_kv_cache_350_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|int32_t|const char\*)\s+(pa_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.fail("libpa.so is not built (python -m paged_kv_cache_350_amd.build)")
+    return pa.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["pa_kv_append", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_size",
+                 "pa_status_string", "pa_decode_partition", "pa_decode_reduce",
+                 "pa_decode_partition_size", "pa_version"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    raw = ctypes.CDLL(pa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert pa.status_string(code)
+    assert pa.status_string(0) == "ok"
+    assert pa.status_string(-99) == "unknown status"
+    assert L.pa_version() == 100
+
+
+def test_partition_policy_and_workspace_size(L):
+    assert pa.decode_partition_size(4096, 0) == 512
+    assert pa.decode_partition_size(512, 0) == 0          # short: single pass
+    assert pa.decode_partition_size(4096, -1) == 0
+    assert pa.decode_partition_size(4096, 256) == 256
+    assert pa.decode_partition_size(4096, 100) < 0        # not a multiple of 32
+    assert pa.decode_partition_size(4096, 16) < 0
+    # long-context workload: 8 seqs x 32 heads x 64 partitions x (128 + 2) floats
+    assert pa.decode_workspace_size(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 128, 4096, 0) == 64 * 32 * 8 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 128, 500, 0) == 0
+    assert pa.decode_workspace_size(64, 32, 128, 4096, -1) == 0
+    assert pa.decode_workspace_size(3, 4, 64, 33, 32) == 3 * 4 * 2 * 66 * 4
+
+
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _decode(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, bs=16, hkv=8, scale=0.1, out=FAKE,
+             stream=None, B=4, hq=32, d=128, maxb=16, maxctx=256, nb=100, dtype=1, part=0,
+             kernel=0, ws=None, wsb=0)
+    a.update(kw)
+    return L.pa_decode(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bs"], a["hkv"], a["scale"],
+                       a["out"], a["stream"], a["B"], a["hq"], a["d"], a["maxb"], a["maxctx"],
+                       a["nb"], a["dtype"], a["part"], a["kernel"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), pa.PA_ERR_NULL),
+    (dict(out=None), pa.PA_ERR_NULL),
+    (dict(bt=None), pa.PA_ERR_NULL),
+    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(hq=30), pa.PA_ERR_ARG),                     # not a multiple of kv heads
+    (dict(hq=136, hkv=8), pa.PA_ERR_UNSUPPORTED),     # 17 query heads per kv head
+    (dict(hkv=0), pa.PA_ERR_ARG),
+    (dict(dtype=7), pa.PA_ERR_ARG),
+    (dict(kernel=9), pa.PA_ERR_ARG),
+    (dict(dtype=0, kernel=2), pa.PA_ERR_UNSUPPORTED), # MFMA kernel is bf16 only
+    (dict(maxctx=257), pa.PA_ERR_ARG),                # beyond max_blocks_per_seq * block_size
+    (dict(maxctx=-1), pa.PA_ERR_ARG),
+    (dict(nb=0), pa.PA_ERR_ARG),
+    (dict(part=48), pa.PA_ERR_ARG),
+    (dict(part=256), pa.PA_ERR_WORKSPACE),            # split path without workspace
+    (dict(part=256, ws=FAKE, wsb=16), pa.PA_ERR_WORKSPACE),
+    (dict(q=FAKE + 4), pa.PA_ERR_ARG),                # misaligned
+    (dict(scale=float("nan")), pa.PA_ERR_ARG),
+    (dict(B=-1), pa.PA_ERR_ARG),
+])
+def test_decode_rejects_bad_arguments(L, kw, status):
+    assert _decode(L, **kw) == status
+
+
+def test_zero_sequences_is_a_no_op(L):
+    assert _decode(L, B=0, q=None, out=None, bt=None, cl=None) == pa.PA_OK
+
+
+def test_stage_entry_points_validate(L):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 0.1, None, 4, 32, 128, 16, 256, 100, 1]
+    assert L.pa_decode_partition(*args, 0, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG      # needs explicit P
+    assert L.pa_decode_partition(*args, -1, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG
+    assert L.pa_decode_partition(*args, 64, 0, None, 0) == pa.PA_ERR_WORKSPACE
+    assert L.pa_decode_reduce(FAKE, 16, FAKE, FAKE, None, 4, 32, 128, 256, 64, 1) == pa.PA_ERR_WORKSPACE
+    assert L.pa_decode_reduce(FAKE, 1 << 30, FAKE, FAKE, None, 4, 32, 128, 256, 0, 1) == pa.PA_ERR_ARG
+    assert L.pa_decode_reduce(FAKE, 1 << 30, None, FAKE, None, 4, 32, 128, 256, 64, 1) == pa.PA_ERR_NULL
+    assert L.pa_decode_reduce(FAKE, 1 << 30, FAKE, FAKE, None, 4, 32, 96, 256, 64, 1) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_append_and_copy_validate(L):
+    # pa_kv_append(k, v, slots, kc, vc, T, hkv, d, bs, nb, dtype, stream)
+    assert L.pa_kv_append(None, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 1, None) == pa.PA_ERR_NULL
+    assert L.pa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 24, 10, 1, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 10, 1, None) == pa.PA_ERR_ARG
+    assert L.pa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 0, 1, None) == pa.PA_ERR_ARG
+    assert L.pa_kv_append(FAKE + 2, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 1, None) == pa.PA_ERR_ARG
+    assert L.pa_kv_append(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == pa.PA_OK
+    # pa_copy_blocks(kc, vc, mapping, n, hkv, d, bs, nb, dtype, stream)
+    assert L.pa_copy_blocks(FAKE, FAKE, None, 3, 8, 128, 32, 10, 1, None) == pa.PA_ERR_NULL
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, 3, 8, 64, 12, 10, 1, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, -3, 8, 64, 16, 10, 1, None) == pa.PA_ERR_ARG
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, 3, 8, 64, 16, 10, 5, None) == pa.PA_ERR_ARG
+    assert L.pa_copy_blocks(None, None, None, 0, 8, 64, 16, 10, 1, None) == pa.PA_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    kc = torch.zeros(4, 2, 16, 16, 8, dtype=torch.bfloat16)
+    vc = torch.zeros(4, 2, 128, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pa.copy_blocks(kc, vc, torch.zeros(1, 2, dtype=torch.int64))

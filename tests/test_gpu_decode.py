@@ -1,0 +1,226 @@
+"""Paged decode on the GPU against the float64 oracle.
+
+Small workloads (the oracle takes seconds) cover every kernel family, path
+(single pass, split with several partition sizes, library default), dtype,
+block size, head_dim and group size, with ragged lengths around every tile
+boundary.  The named full-size workloads are checked on sampled sequences in
+the launch configuration the benchmark uses.  Invariants that need no oracle
+(page-permutation and repeat bit-identity, stage API = one call) are checked
+as well."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import bits_equal, check_close, oracle_decode, out_f64, require_gpu, say, storage_np
+from test_gpu_cache_ops import run_step_updates
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 96, 97, 100, 255, 256, 257, 513, 700]
+
+SHAPES = [  # (dtype, block_size, num_heads, num_kv_heads, head_dim)
+    ("f32", 16, 4, 4, 64),
+    ("f32", 32, 32, 8, 128),
+    ("f32", 16, 6, 3, 128),
+    ("bf16", 16, 32, 8, 128),
+    ("bf16", 32, 32, 8, 128),
+    ("bf16", 16, 64, 8, 128),
+    ("bf16", 32, 16, 1, 64),
+    ("bf16", 16, 4, 4, 64),
+    ("bf16", 16, 10, 2, 128),
+]
+PATHS = [-1, 0, 32, 96, 512]
+
+
+def _kernels(dtype):
+    return ["valu", "mfma"] if dtype == "bf16" else ["valu"]
+
+
+def run_decode(pa, w, t, kernel="auto", partition_size=None):
+    ps = w.partition_size if partition_size is None else partition_size
+    return pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                     w.scale, w.max_context_len, partition_size=ps, kernel=kernel)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_decode_small_all_paths(shape):
+    pa = require_gpu()
+    dtype, bs, hq, hkv, d = shape
+    w = W.custom("ragged", 7, dtype, RAGGED, hq, hkv, d, bs)
+    say("small", shape, w.summary())
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    ref = oracle_decode(w, t, range(w.num_seqs))
+    for kernel in _kernels(dtype):
+        for ps in PATHS:
+            say("  kernel", kernel, "partition", ps)
+            out = run_decode(pa, w, t, kernel, ps)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, dtype, f"{shape} {kernel} P={ps}")
+
+
+@pytest.mark.parametrize("figure", [False, True])
+def test_tiny_workload(figure):
+    """2 seqs of 36 and 42 tokens, fp32, D 64, 4/4 heads (one with the
+    page-table figure's pages 7, 14, 2)."""
+    pa = require_gpu()
+    w = W.tiny(figure_table=figure)
+    say("tiny", figure, w.block_tables.tolist())
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    ref = oracle_decode(w, t, range(w.num_seqs))
+    for ps in PATHS:
+        out = run_decode(pa, w, t, "auto", ps)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "f32", f"tiny P={ps}")
+
+
+def test_empty_context_gives_zeros():
+    pa = require_gpu()
+    w = W.custom("with_empty", 8, "bf16", [40, 1, 77, 600], 32, 8, 128, 16)
+    say("empty context")
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    t["context_lens"][2] = 0                 # sequence 2 has nothing to attend to
+    w.context_lens = w.context_lens.copy()
+    w.context_lens[2] = 0
+    ref = oracle_decode(w, t, range(w.num_seqs))
+    assert not ref[2].any()
+    for kernel in ("valu", "mfma"):
+        for ps in PATHS:
+            out = run_decode(pa, w, t, kernel, ps)
+            torch.cuda.synchronize()
+            got = out_f64(out)
+            assert not got[2].any()
+            check_close(got, ref, "bf16", f"empty {kernel} P={ps}")
+    # every sequence empty, max_context_len 0
+    t["context_lens"].zero_()
+    for kernel in ("valu", "mfma"):
+        for ps in (-1, 0):
+            out = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                            w.scale, 0, partition_size=ps, kernel=kernel)
+            torch.cuda.synchronize()
+            assert not out_f64(out).any()
+
+
+def _sample(w, n, seed):
+    rng = np.random.default_rng(seed)
+    order = np.argsort(w.context_lens)
+    pick = {int(order[0]), int(order[-1])}
+    rest = [b for b in range(w.num_seqs) if b not in pick]
+    pick |= set(int(b) for b in rng.choice(rest, size=min(n - 2, len(rest)), replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama3_8b", "llama3_70b", "prefix_share", "beam_fork",
+                                  "long_context"])
+def test_named_workload_full_size(name):
+    """Full-size workload, library-default launch (as benchmarked), sampled
+    sequences against the oracle; the vector-ALU kernel as a second check."""
+    pa = require_gpu()
+    w = W.by_name(name)
+    say("full", name, w.summary())
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    seqs = _sample(w, 8, 11)
+    ref = oracle_decode(w, t, seqs)
+    for kernel in ["auto", "valu"]:
+        out = run_decode(pa, w, t, kernel)
+        torch.cuda.synchronize()
+        got = out_f64(out)[seqs]
+        stats = check_close(got, ref, w.dtype, f"{name} {kernel}")
+        say("  ", kernel, stats)
+        assert np.isfinite(out_f64(out)).all()
+
+
+def test_single_pass_matches_split_at_full_size():
+    pa = require_gpu()
+    w = W.llama3_8b()
+    say("single vs split", w.summary())
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    seqs = _sample(w, 6, 12)
+    ref = oracle_decode(w, t, seqs)
+    for ps in (-1, 256, 1024):
+        out = run_decode(pa, w, t, "mfma", ps)
+        torch.cuda.synchronize()
+        check_close(out_f64(out)[seqs], ref, "bf16", f"P={ps}")
+
+
+@pytest.mark.parametrize("kernel,ps", [("mfma", 0), ("mfma", -1), ("valu", 64), ("valu", -1)])
+def test_page_permutation_is_bit_identical(kernel, ps):
+    """Moving physical pages (with the matching table edit) changes no bit:
+    the work order depends only on logical positions."""
+    pa = require_gpu()
+    w = W.llama3_8b(seed=21, num_seqs=12, len_range=(1, 1500))
+    say("permutation", kernel, ps)
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    base = run_decode(pa, w, t, kernel, ps).clone()
+    perm = torch.from_numpy(np.random.default_rng(22).permutation(w.num_blocks)).cuda()
+    kc2 = torch.empty_like(t["k_cache"])
+    vc2 = torch.empty_like(t["v_cache"])
+    kc2[perm] = t["k_cache"]
+    vc2[perm] = t["v_cache"]
+    tables2 = perm[t["block_tables"].long()].to(torch.int32).contiguous()
+    out2 = pa.decode(t["q"], kc2, vc2, tables2, t["context_lens"], w.scale, w.max_context_len,
+                     partition_size=ps, kernel=kernel)
+    again = run_decode(pa, w, t, kernel, ps)
+    torch.cuda.synchronize()
+    assert bits_equal(out2, base)
+    assert bits_equal(again, base)
+
+
+def test_stage_api_equals_one_call():
+    pa = require_gpu()
+    w = W.llama3_70b(num_seqs=16, clip=(1, 3000))
+    say("stages", w.summary())
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    for P in (64, 512):
+        one = run_decode(pa, w, t, "mfma", P)
+        ws = pa.make_workspace(t["q"], w.max_context_len, P)
+        pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                            w.scale, w.max_context_len, P, ws, kernel="mfma")
+        two = torch.empty_like(one)
+        pa.decode_reduce(ws, t["context_lens"], two, w.max_context_len, P)
+        torch.cuda.synchronize()
+        assert bits_equal(one, two)
+
+
+def test_group_of_sixteen_and_head_dim_64():
+    pa = require_gpu()
+    w = W.custom("g16", 9, "bf16", [5, 300, 1025, 2048], 32, 2, 64, 32)
+    say("g16", w.summary())
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    ref = oracle_decode(w, t, range(w.num_seqs))
+    for kernel in ("valu", "mfma"):
+        for ps in (-1, 0, 128):
+            out = run_decode(pa, w, t, kernel, ps)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, "bf16", f"g16 {kernel} P={ps}")
+
+
+def test_bad_table_entries_stay_in_bounds():
+    """Out-of-range page ids past the used entries are never read, and used
+    out-of-range ids are clamped (output unspecified, but finite memory)."""
+    pa = require_gpu()
+    w = W.custom("pad", 10, "bf16", [17, 40], 32, 8, 128, 16)
+    say("bad table entries")
+    t = W.make_tensors(w, "cuda")
+    run_step_updates(pa, w, t)
+    ref = oracle_decode(w, t, range(w.num_seqs))
+    bt = t["block_tables"].clone()
+    bt[0, 2:] = 2 ** 30          # entries past ceil(17 / 16) = 2: never read
+    out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
+                    w.max_context_len, partition_size=0, kernel="mfma")
+    torch.cuda.synchronize()
+    check_close(out_f64(out), ref, "bf16", "padding entries")
+    bt[1, 0] = -5                # a used entry out of range: guarded, no fault
+    out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
+                    w.max_context_len, partition_size=0, kernel="mfma")
+    torch.cuda.synchronize()

@@ -4,6 +4,6 @@ attention arithmetic."""
 
 from .blockmgr import BlockManager, OutOfPages  # noqa: F401
 from .configs import (  # noqa: F401
-    NAMED, Workload, beam_fork, by_name, chunk_elems, copy_probe, llama3_70b,
-    llama3_8b, long_context, make_tensors, prefix_share, tiny,
+    NAMED, Workload, beam_fork, by_name, custom, chunk_elems, copy_probe, llama3_70b,
+    llama3_8b, long_context, make_tensors, prefix_share, tiny, torch_dtype,
 )

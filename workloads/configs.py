@@ -365,6 +365,17 @@ def copy_probe(beams: int = 8, prompt: int = 32768) -> np.ndarray:
     return np.stack([src, dst], axis=1).astype(np.int64)
 
 
+def custom(name: str, seed: int, dtype: str, lens, num_heads: int, num_kv_heads: int,
+           head_dim: int, block_size: int, num_blocks: Optional[int] = None,
+           partition_size: int = 0) -> Workload:
+    """Independent sequences with explicit context lengths (each >= 1)."""
+    rng = np.random.default_rng(seed)
+    return _plain(name, seed, dtype, np.asarray(lens), num_heads, num_kv_heads, head_dim,
+                  block_size, rng, num_blocks=num_blocks, partition_size=partition_size,
+                  description=f"{len(lens)} seqs, {num_heads}/{num_kv_heads} heads, D {head_dim}, "
+                              f"bs {block_size}, {dtype}")
+
+
 # Named workloads, in the order the task lists them.
 NAMED = {
     "tiny": tiny,
