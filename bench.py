@@ -49,6 +49,9 @@ def _args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe"],
+                    help="copy_probe: time pa_copy_blocks on an eager fork of a 32,768-token "
+                         "prompt to 7 beams (7,168 pages of 32 tokens, K and V)")
     return ap.parse_args(argv)
 
 
@@ -142,6 +145,32 @@ def stream_read_gbps(torch, nbytes=2 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def copy_probe(a, torch, pa, W) -> int:
+    """Eager-fork page copy: 7 x 1024 pages (bs 32, 8 kv heads, D 128, bf16)."""
+    pairs = W.copy_probe()
+    nb = int(pairs.max()) + 1
+    kc = torch.zeros(nb, 8, 16, 32, 8, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(nb, 8, 128, 32, dtype=torch.bfloat16, device="cuda")
+    mp = torch.from_numpy(pairs).cuda()
+    for _ in range(a.warmup):
+        pa.copy_blocks(kc, vc, mp)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(a.steps):
+        pa.copy_blocks(kc, vc, mp)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / a.steps
+    page_bytes = 2 * 8 * 128 * 32 * 2          # K + V of one page
+    moved = len(pairs) * page_bytes * 2        # read + write
+    print(json.dumps({"mode": "copy_probe", "pairs": int(len(pairs)), "bytes_read": moved // 2,
+                      "bytes_written": moved // 2, "avg_us": round(us, 2),
+                      "gbps_read_plus_write": round(moved / (us * 1e-6) / 1e9, 1),
+                      "steps": a.steps}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     a = _args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +189,8 @@ def main(argv=None) -> int:
         return 1
     pa.lib()
     torch.cuda.set_device(0)
+    if a.mode == "copy_probe":
+        return copy_probe(a, torch, pa, W)
     w = W.by_name(a.workload)
     ps_req = w.partition_size if a.partition_size is None else a.partition_size
     t = W.make_tensors(w, "cuda")

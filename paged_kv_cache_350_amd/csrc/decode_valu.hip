@@ -84,13 +84,13 @@ void decode_valu_kernel(DecodeParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int w = tid / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
 
-    const uint32_t lid = xcd_local_order(blockIdx.x, gridDim.x);
-    const int b = (int)(lid % (uint32_t)p.num_seqs);
-    const uint32_t rest = lid / (uint32_t)p.num_seqs;
-    const int g = (int)(rest % (uint32_t)p.num_kv_heads);
-    const int part = (int)(rest / (uint32_t)p.num_kv_heads);
+    const WorkItem wi = decode_work_item(blockIdx.x, (uint32_t)p.num_seqs,
+                                         (uint32_t)(p.num_kv_heads * p.max_parts));
+    const int b = wi.b;
+    const int g = wi.q % p.num_kv_heads;
+    const int part = wi.q / p.num_kv_heads;
     const int G = p.group;
 
     int L = p.context_lens[b];

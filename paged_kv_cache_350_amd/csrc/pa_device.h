@@ -38,17 +38,31 @@ __device__ __forceinline__ void st16(void* p, u32x4_t v) {
     *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
-// Workgroups are handed to the XCDs round-robin (id i runs on XCD i % 8).
-// Map the hardware id to a logical id so that each XCD owns one contiguous
-// range of logical ids: work items adjacent in logical order (for example
-// the sequences sharing a prefix page) then share that XCD's L2.
-__device__ __forceinline__ uint32_t xcd_local_order(uint32_t hw_id, uint32_t n) {
-    const uint32_t xcd = hw_id % kXcds;
-    const uint32_t k = hw_id / kXcds;
-    const uint32_t q0 = n / kXcds;
-    const uint32_t r = n % kXcds;          // the first r XCDs get one extra item
-    const uint32_t base = xcd < r ? xcd * (q0 + 1) : r * (q0 + 1) + (xcd - r) * q0;
-    return base + k;
+// Decode work items are (partition-major group q = part * num_kv_heads + g,
+// sequence b).  Workgroups are handed to the XCDs round-robin (id i runs on
+// XCD i % 8).  When the number of groups nq is a multiple of 8, XCD x is given
+// exactly the groups q = x, x + 8, x + 16, ...: every XCD then sees the same
+// mix of partitions (balanced even when most late partitions are empty), and
+// all sequences of one (partition, kv head) run back to back on one XCD, so
+// pages they share (a common prefix) are served from that XCD's L2.  Other
+// grids keep the natural order, which spreads consecutive sequences across
+// the XCDs.  Both maps are bijections of [0, num_seqs * nq).
+struct WorkItem {
+    int b;
+    int q;
+};
+
+__device__ __forceinline__ WorkItem decode_work_item(uint32_t hw_id, uint32_t num_seqs, uint32_t nq) {
+    WorkItem w;
+    if (nq % kXcds == 0) {
+        const uint32_t k = hw_id / kXcds;
+        w.q = (int)(hw_id % kXcds + kXcds * (k / num_seqs));
+        w.b = (int)(k % num_seqs);
+    } else {
+        w.q = (int)(hw_id / num_seqs);
+        w.b = (int)(hw_id % num_seqs);
+    }
+    return w;
 }
 
 }  // namespace pa_impl
