@@ -44,6 +44,8 @@ def _args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--reuse", default="auto", choices=["auto", "stream", "shared"],
+                    help="K/V load path (auto: shared when the workload's sequences share pages)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the library default (0 default, -1 single pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,6 +200,8 @@ def main(argv=None) -> int:
         pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
     torch.cuda.synchronize()
 
+    # the load path a caller picks: its block manager knows whether pages are shared
+    reuse = a.reuse if a.reuse != "auto" else ("shared" if w.extra.get("shared_pages") else "stream")
     P = pa.decode_partition_size(w.max_context_len, ps_req)
     split = P > 0
     out = torch.empty_like(t["q"])
@@ -214,13 +218,15 @@ def main(argv=None) -> int:
             ev[1].record(stream)
         if split:
             pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                t["context_lens"], w.scale, w.max_context_len, P, ws, kernel=a.kernel)
+                                t["context_lens"], w.scale, w.max_context_len, P, ws, kernel=a.kernel,
+                                reuse=reuse)
             if ev is not None:
                 ev[2].record(stream)
             pa.decode_reduce(ws, t["context_lens"], out, w.max_context_len, P)
         else:
             pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                      w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel)
+                      w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel,
+                      reuse=reuse)
             if ev is not None:
                 ev[2].record(stream)
         if ev is not None:
@@ -279,7 +285,7 @@ def main(argv=None) -> int:
             "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "sum_context_tokens": int(w.context_lens.sum()),
             "max_context_len": w.max_context_len, "num_blocks": w.num_blocks,
-            "partition_size": P, "kernel": kernel_name, "seed": w.seed,
+            "partition_size": P, "kernel": kernel_name, "reuse": reuse, "seed": w.seed,
             "kv_bytes_per_step": kv_bytes,
         },
         "kernels_avg_us": {

@@ -80,6 +80,19 @@ typedef enum pa_kernel {
     PA_KERNEL_MFMA = 2       /* MFMA matrix cores for Q.K^T and P.V (bf16 only) */
 } pa_kernel;
 
+/* How the K/V pages of one decode call are reused across its sequences.
+ * It picks the load path of the decode kernels; every choice computes the
+ * same result.  Streaming loads pass pages by the caches (the fastest way to
+ * read pages that only one sequence of the batch touches); cached loads let
+ * sequences that share pages -- a common prompt prefix, forked beams --
+ * serve each other from L2 [Internals, "Copy-on-Write and Prefix Sharing";
+ * Glossary, "Copy-on-Write Memory Forking"]. */
+typedef enum pa_kv_reuse {
+    PA_KV_AUTO = 0,      /* library default: PA_KV_STREAM */
+    PA_KV_STREAM = 1,    /* no page is read by more than one sequence */
+    PA_KV_SHARED = 2     /* some pages are read by several sequences */
+} pa_kv_reuse;
+
 /* Human-readable text for a status code; never NULL, static storage. */
 const char* pa_status_string(pa_status status);
 
@@ -143,6 +156,7 @@ pa_status pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping
  *   partition_size 0 = library default, -1 = single pass (one workgroup per
  *                 sequence and kv head), otherwise a multiple of 32 >= 32
  *   kernel        PA_KERNEL_AUTO / _VALU / _MFMA
+ *   reuse         PA_KV_AUTO / _STREAM / _SHARED (load path; same result)
  *   workspace     device scratch of at least pa_decode_workspace_size(...)
  *                 bytes when the split path runs (may be NULL otherwise);
  *                 owned by the caller, contents undefined afterwards
@@ -156,7 +170,8 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                     int32_t max_blocks_per_seq, int32_t max_context_len,
                     int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
-                    pa_kernel kernel, void* workspace, size_t workspace_bytes);
+                    pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
+                    size_t workspace_bytes);
 
 /*
  * Partition size pa_decode uses for a request: > 0 = split path with that
@@ -193,7 +208,8 @@ pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_
                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                               int32_t max_blocks_per_seq, int32_t max_context_len,
                               int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
-                              pa_kernel kernel, void* workspace, size_t workspace_bytes);
+                              pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
+                              size_t workspace_bytes);
 
 /*
  * pa_decode_reduce -- second stage: merge the partitions of every

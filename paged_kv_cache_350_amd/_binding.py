@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_OK, PA_ERR_NULL, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4, -5
 PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+REUSE = {"auto": 0, "stream": 1, "shared": 2}
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
 _lock = threading.Lock()
@@ -46,10 +47,10 @@ _SIGNATURES = {
     "pa_kv_append": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
-                   _vp, _c_size], _c_int),
+                   _c_int, _vp, _c_size], _c_int),
     "pa_decode_partition": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp,
                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
-                             _vp, _c_size], _c_int),
+                             _c_int, _vp, _c_size], _c_int),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -187,8 +188,13 @@ def make_workspace(q: torch.Tensor, max_context_len: int, partition_size: int = 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
            max_context_len: int, out: Optional[torch.Tensor] = None, partition_size: int = 0,
-           kernel: str = "auto", workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Paged decode attention; returns out [B, Hq, D] in q's dtype."""
+           kernel: str = "auto", workspace: Optional[torch.Tensor] = None,
+           reuse: str = "auto") -> torch.Tensor:
+    """Paged decode attention; returns out [B, Hq, D] in q's dtype.
+
+    ``reuse`` is "stream" when no page is read by two sequences of the batch,
+    "shared" when some are (prefix sharing, beams); it only picks the load
+    path."""
     nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len)
     if out is None:
@@ -204,14 +210,14 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv, float(scale),
                          out.data_ptr(), _stream(q), B, hq, d, block_tables.shape[1],
                          int(max_context_len), nb, _elem_dtype(q), int(partition_size),
-                         KERNELS[kernel], ws_ptr, ws_bytes)
+                         KERNELS[kernel], REUSE[reuse], ws_ptr, ws_bytes)
     _check("pa_decode", st)
     return out
 
 
 def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                      max_context_len: int, partition_size: int, workspace: torch.Tensor,
-                     kernel: str = "auto") -> None:
+                     kernel: str = "auto", reuse: str = "auto") -> None:
     """First stage of the split path only (partials into ``workspace``)."""
     nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len)
@@ -220,7 +226,8 @@ def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale: flo
                                    block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,
                                    float(scale), _stream(q), B, hq, d, block_tables.shape[1],
                                    int(max_context_len), nb, _elem_dtype(q), int(partition_size),
-                                   KERNELS[kernel], workspace.data_ptr(), workspace.numel() * 4)
+                                   KERNELS[kernel], REUSE[reuse], workspace.data_ptr(),
+                                   workspace.numel() * 4)
     _check("pa_decode_partition", st)
 
 

@@ -24,10 +24,14 @@ OBJDIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are switched off: the compiler would otherwise form
-# v_pk_* float ops from ordinary float code.
+# v_pk_* float ops from ordinary float code.  MFMA results live in ordinary
+# VGPRs (gfx950 has one unified register file): the decode kernel rescales
+# its accumulators with vector ALU ops, which cannot read AGPRs, and in AGPR
+# form the compiler copies them back and forth on every loop iteration.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -13,27 +13,40 @@
 // reductions, which approaches the VALU rate at G = 8; one 16x16x32 bf16
 // MFMA retires 8192 of them.  G is padded to 16 (zero query rows).
 //
-// Work unit: a chunk of 32 tokens (two 16-token pages or one 32-token page).
-// Inside a chunk, token slot tau = 0..31 is the tau-th token of the chunk.
-//
-//   Q.K^T  v_mfma_f32_16x16x32_bf16, A = K (rows = tokens), B = Q^T
-//          (columns = heads), D/32 k-steps, two row tiles t = 0, 1.
-//          Row r of tile t holds tau = 8 (r / 4) + 4 t + r % 4.  The result
-//          layout (lane: column lane % 16, rows 4 (lane / 16) + i) then gives
-//          lane (h, j) the scores of head h for tau = 8 j .. 8 j + 7.
-//          K pages are [D/8 chunks][BS][8]: lane (r, j) of k-step s loads the
-//          16 bytes of chunk 4 s + j of its token, four 64-byte runs per
-//          quarter-wave.
+// Work unit: a chunk of 32 tokens, tau = 0..31.  Per chunk:
+//   Q.K^T  v_mfma_f32_16x16x32_bf16 on two 16-token row tiles t = 0, 1:
+//          A = K rows (tokens), B = Q^T (columns = heads), D/32 k-steps.
+//          K pages are [D/8 chunks][BS][8]: lane (r = lane % 16, j = lane / 16)
+//          of k-step s loads the 16 bytes of chunk 4 s + j of its row's token.
+//          The result gives lane (h = lane % 16, j) rows 4 j .. 4 j + 3 of
+//          each tile, i.e. 8 scores of head h.
 //   softmax per head: chunk max over the lane's 8 scores, then across the
-//          four lane groups; running max / sum rescaled by 2^(m_old - m_new).
-//   P.V    v_mfma_f32_16x16x32_bf16, A = V^T (rows = 16 dims), B = P^T
-//          (columns = heads).  Lane (h, j) already holds P for tau = 8 j ..
-//          8 j + 7 -- exactly its B operand -- and V pages are dim-major
-//          [D][BS], so the A operand is one 16-byte load of 8 consecutive
-//          tokens of dim 16 dc + lane % 16.  No data is exchanged between
-//          lanes and nothing goes through LDS inside the loop.
-// Masking of the last, partly valid chunk selects -inf scores and zero V
-// values (never multiplies a possibly-NaN slot by zero).
+//          four lane groups; the running sum and accumulator are rescaled by
+//          2^(m_old - m_new) only when the max grows by more than 8 (log2
+//          units), so normally no accumulator is touched by the vector ALU.
+//   P.V    v_mfma_f32_16x16x32_bf16, A = V^T (rows = 16 dims), B = P^T.  The
+//          k-slots of lane group j are the tokens of its 8 scores, so lane
+//          (h, j) already holds its B operand; V pages are dim-major [D][BS],
+//          so the A operand is that lane's 8 tokens of dim 16 dc + r.
+//          Nothing goes through LDS inside the loop.
+//
+// Two ways to assign tokens to rows, chosen by how the pages are reused:
+//   split (streaming: each page read by one workgroup per step) -- tile t is
+//          the 16-token half t of the chunk (two pages at block 16, two halves
+//          of one page at block 32), row r is token 16 t + r.  Every load
+//          instruction reads one half, so it is a raw buffer load whose base
+//          address (the half's page tile) sits in scalar registers and whose
+//          per-lane offset never changes: no 64-bit address math, and the
+//          loads carry the non-temporal bit.  Lane group j holds tokens
+//          4 j .. 4 j + 3 of each half; its V operand is two 8-byte loads.
+//   interleaved (shared pages: many workgroups read the same page, mostly
+//          from L2) -- row r of tile t is token 8 (r / 4) + 4 t + r % 4, so
+//          lane group j holds tokens 8 j .. 8 j + 7 and its V operand is one
+//          16-byte load.  Loads are ordinary global loads from a per-lane page
+//          base computed once per chunk; fewer, wider load instructions is
+//          what counts when the data comes from cache.
+// Masking of a partly valid chunk selects -inf scores and zero V values
+// (never multiplies a possibly-NaN slot by zero).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -43,15 +56,41 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kChunk = 32;          // tokens per MFMA step (k of the P.V product)
+constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
+constexpr int kHalf = 16;             // tokens per row tile
+constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
+
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int D, int BS>
+// Buffer resource over `bytes` bytes at `base` (raw buffer, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
+// Raw buffer loads with the streaming policy: per-lane byte offset `off` plus
+// a wave-uniform byte offset `soff` (a scalar register, so constant strides
+// cost no VGPR).
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, kPolicyStream);
+}
+__device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, kPolicyStream);
+}
+
+// Chunk-relative token of score slot 4 t + i held by lane group j.
+template <bool SPLIT>
+__device__ __forceinline__ int slot_token(int t, int i, int j) {
+    return SPLIT ? kHalf * t + 4 * j + i : 8 * j + 4 * t + i;
+}
+
+template <int D, int BS, bool SPLIT>
 __global__ __launch_bounds__(kThreads)
 void decode_mfma_kernel(DecodeParams p) {
     constexpr int KSTEPS = D / 32;   // Q.K^T k-steps
     constexpr int DC = D / 16;       // 16-dim output tiles of P.V
+    constexpr uint32_t kTileBytes = (uint32_t)D * BS * 2;
     static_assert(BS == 16 || BS == 32, "block size");
 
     extern __shared__ float smem[];
@@ -64,6 +103,7 @@ void decode_mfma_kernel(DecodeParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int hl = lane % 16;        // head (column) of this lane
     const int j = lane / 16;         // lane group
+    const int r = lane % 16;         // A-operand row of this lane
 
     const WorkItem wi = decode_work_item(blockIdx.x, (uint32_t)p.num_seqs,
                                          (uint32_t)(p.num_kv_heads * p.max_parts));
@@ -98,15 +138,21 @@ void decode_mfma_kernel(DecodeParams p) {
         }
     }
 
+    // split path: per-lane byte offsets inside a half's K / V tile (loop
+    // invariant); the k-step / dim-tile strides are scalar offsets.
+    const uint32_t kofs = (uint32_t)((j * BS + r) * 16);
+    const uint32_t vofs = (uint32_t)((r * BS + 4 * j) * 2);
+    constexpr uint32_t kStepBytes = 4u * BS * 16;     // K chunk 4 s + j -> 4 (s + 1) + j
+    constexpr uint32_t kTileStep = 16u * BS * 2;      // V dim 16 dc + r -> 16 (dc + 1) + r
+    // interleaved path: this lane's K row (tile 0) and V token group
+    const int tk = 8 * (r / 4) + (r % 4);
+    const int tv = 8 * j;
+
     const int* row = p.block_tables + (size_t)b * p.max_blocks_per_seq;
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache);
     const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache);
     const size_t tile_elems = (size_t)D * BS;
     const size_t kv_heads = (size_t)p.num_kv_heads;
-
-    const int r = lane % 16;
-    const int tau_k0 = 8 * (r / 4) + (r % 4);    // Q.K^T row r of tile 0; tile 1 adds 4
-    const int tau_v0 = 8 * j;                    // P.V k-slots of this lane: tau_v0 .. + 7
 
     float m_run = neg_inf();
     float l_run = 0.f;
@@ -117,28 +163,48 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int ci = w; ci < nchunks; ci += kWaves) {
         const int cstart = start + ci * kChunk;
         const int valid = min(kChunk, end - cstart);
+
+        // ---- pages of the chunk (wave-uniform)
         const int blk0 = cstart / BS;
         int pg0 = row[blk0];
         if ((uint32_t)pg0 >= (uint64_t)p.num_blocks) pg0 = 0;
         int pg1 = pg0;
-        if (BS == 16 && valid > 16) {
+        if (BS == 16 && valid > kHalf) {
             pg1 = row[blk0 + 1];
             if ((uint32_t)pg1 >= (uint64_t)p.num_blocks) pg1 = 0;
         }
 
-        // ---- loads: K for both row tiles, V for every 16-dim tile
+        // ---- loads: K of both row tiles, V of every 16-dim tile
         u32x4_t kraw[2][KSTEPS];
-        for (int t = 0; t < 2; ++t) {
-            const int tau = tau_k0 + 4 * t;
-            const int page = (BS == 16 && tau >= 16) ? pg1 : pg0;
-            const uint16_t* base = kc + ((size_t)page * kv_heads + g) * tile_elems + (tau % BS) * 8;
-            for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = ld16(base + (size_t)(4 * s + j) * BS * 8);
-        }
-        u32x4_t vraw[DC];
-        {
-            const int page = (BS == 16 && tau_v0 >= 16) ? pg1 : pg0;
-            const uint16_t* base = vc + ((size_t)page * kv_heads + g) * tile_elems + (tau_v0 % BS);
-            for (int dc = 0; dc < DC; ++dc) vraw[dc] = ld16(base + (size_t)(16 * dc + r) * BS);
+        u32x4_t vop[DC];                 // V^T operand, 8 bf16 per lane
+        if constexpr (SPLIT) {
+            __amdgpu_buffer_rsrc_t krs[2], vrs[2];
+            for (int t = 0; t < 2; ++t) {
+                const int page = t ? pg1 : pg0;
+                const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
+                const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
+                // a half with no valid token gets an empty range: loads return 0
+                const bool live = t == 0 || valid > kHalf;
+                krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
+                vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
+            }
+            for (int t = 0; t < 2; ++t)
+                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
+            u32x2_t vh[2][DC];
+            for (int t = 0; t < 2; ++t)
+                for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
+            for (int dc = 0; dc < DC; ++dc)
+                vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+        } else {
+            const int kpage = (BS == 16 && tk >= kHalf) ? pg1 : pg0;
+            const uint16_t* kb = kc + ((size_t)kpage * kv_heads + g) * tile_elems +
+                                 (size_t)(tk % BS) * 8 + (size_t)j * BS * 8;
+            const int vpage = (BS == 16 && tv >= kHalf) ? pg1 : pg0;
+            const uint16_t* vb = vc + ((size_t)vpage * kv_heads + g) * tile_elems + (tv % BS) +
+                                 (size_t)r * BS;
+            for (int t = 0; t < 2; ++t)
+                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = ld16(kb + 32 * t + (size_t)s * 4 * BS * 8);
+            for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
         }
 
         // ---- S = K . Q^T
@@ -149,42 +215,52 @@ void decode_mfma_kernel(DecodeParams p) {
                 st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[s], st[t], 0, 0, 0);
         }
 
-        // ---- online softmax; lane holds head hl at tau = tau_v0 + k
+        // ---- online softmax; slot 4 t + i of lane (hl, j) is token slot_token(t, i, j)
         float sc[8];
         for (int t = 0; t < 2; ++t)
             for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
         if (valid < kChunk) {
-            for (int k = 0; k < 8; ++k) sc[k] = (tau_v0 + k < valid) ? sc[k] : neg_inf();
+            for (int t = 0; t < 2; ++t)
+                for (int i = 0; i < 4; ++i)
+                    sc[4 * t + i] = (slot_token<SPLIT>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
         }
         float mx = sc[0];
         for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - mn);
-        m_run = mn;
+        // Lazy rescaling: the reference max moves only when a score exceeds it
+        // by more than kRescaleSlack (always on the first chunk, m_run = -inf).
+        // Between moves the weights are 2^(s - m_run) <= 2^kRescaleSlack; acc
+        // and l share the reference, so the result is the same.
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {       // wave-uniform branch
+            const float mn = grow ? mx : m_run;
+            const float alpha = fast_exp2(m_run - mn);      // 0 on the first chunk
+            for (int dc = 0; dc < DC; ++dc) acc[dc] = acc[dc] * alpha;
+            l_run *= alpha;
+            m_run = mn;
+        }
         bf16x8_t pf;
         float psum = 0.f;
         for (int k = 0; k < 8; ++k) {
-            const bf16_t pb = (bf16_t)fast_exp2(sc[k] - mn);
+            const bf16_t pb = (bf16_t)fast_exp2(sc[k] - m_run);
             pf[k] = pb;
             psum += (float)pb;           // normalise with the weights actually used
         }
-        l_run = l_run * alpha + psum;
+        l_run += psum;
 
         // ---- O^T += V^T . P^T
         if (valid < kChunk) {
-            // zero the value slots past the context (lane's k-slots tau_v0 + 0..7)
+            // zero the value slots past the context: dword q holds slots 2 q, 2 q + 1
             for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = (tau_v0 + 2 * q < valid) ? 0x0000ffffu : 0u;
-                const uint32_t hi = (tau_v0 + 2 * q + 1 < valid) ? 0xffff0000u : 0u;
-                for (int dc = 0; dc < DC; ++dc) vraw[dc][q] &= (lo | hi);
+                const int tok = slot_token<SPLIT>(q / 2, 2 * (q % 2), j);
+                const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
+                const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
+                for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
             }
         }
-        for (int dc = 0; dc < DC; ++dc) {
-            acc[dc] = acc[dc] * alpha;
-            acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vraw[dc]), pf, acc[dc], 0, 0, 0);
-        }
+        for (int dc = 0; dc < DC; ++dc)
+            acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf, acc[dc], 0, 0, 0);
     }
 
     // ---- merge the four waves; lane (hl, j) holds dims 16 dc + 4 j + i of head hl
@@ -228,21 +304,28 @@ void decode_mfma_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int BS>
+template <int D, int BS, bool SPLIT>
 hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
     const size_t smem = sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * p.group * D);
     const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * p.max_parts;
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS>), dim3((unsigned)nwg), dim3(kThreads), smem,
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, SPLIT>), dim3((unsigned)nwg), dim3(kThreads), smem,
                        stream, p);
     return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch_path(const DecodeParams& p, hipStream_t stream) {
+    if (p.head_dim == 64)
+        return p.block_size == 16 ? launch_shape<64, 16, SPLIT>(p, stream)
+                                  : launch_shape<64, 32, SPLIT>(p, stream);
+    return p.block_size == 16 ? launch_shape<128, 16, SPLIT>(p, stream)
+                              : launch_shape<128, 32, SPLIT>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-    if (p.head_dim == 64)
-        return p.block_size == 16 ? launch_shape<64, 16>(p, stream) : launch_shape<64, 32>(p, stream);
-    return p.block_size == 16 ? launch_shape<128, 16>(p, stream) : launch_shape<128, 32>(p, stream);
+    return p.stream_kv ? launch_path<true>(p, stream) : launch_path<false>(p, stream);
 }
 
 }  // namespace pa_impl

@@ -64,7 +64,7 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* out, size_t idx, f
     out[idx] = f32_to_bf16(v);
 }
 
-template <typename E, int D, int BS, int GMAX>
+template <typename E, int D, int BS, int GMAX, bool STREAM>
 __global__ __launch_bounds__(kThreads)
 void decode_valu_kernel(DecodeParams p) {
     constexpr int X = 16 / (int)sizeof(E);     // elements per 16-byte chunk
@@ -141,7 +141,7 @@ void decode_valu_kernel(DecodeParams p) {
         float ps[GMAX];
         for (int h = 0; h < GMAX; ++h) ps[h] = 0.f;
         u32x4_t kraw[CPL];
-        for (int cc = 0; cc < CPL; ++cc) kraw[cc] = ld16(kt + ((cc * NJ + j) * BS + o) * X);
+        for (int cc = 0; cc < CPL; ++cc) kraw[cc] = ld16_kv<STREAM>(kt + ((cc * NJ + j) * BS + o) * X);
         for (int cc = 0; cc < CPL; ++cc) {
             const int c = cc * NJ + j;
             float kf[X];
@@ -181,7 +181,7 @@ void decode_valu_kernel(DecodeParams p) {
             float vals[BS];
             for (int vv = 0; vv < VV; ++vv) {
                 float f[X];
-                unpack16<E, X>(ld16(vt + (size_t)d * BS + vv * X), f);
+                unpack16<E, X>(ld16_kv<STREAM>(vt + (size_t)d * BS + vv * X), f);
                 for (int x = 0; x < X; ++x) vals[vv * X + x] = f[x];
             }
             if (valid < BS)
@@ -237,32 +237,38 @@ void decode_valu_kernel(DecodeParams p) {
     }
 }
 
-template <typename E, int D, int BS, int GMAX>
+template <typename E, int D, int BS, int GMAX, bool STREAM>
 hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
     const size_t smem = sizeof(float) *
         (GMAX * D + kWaves * BS * GMAX + 2 * kWaves * GMAX + kWaves * GMAX * D);
     const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * p.max_parts;
-    hipLaunchKernelGGL((decode_valu_kernel<E, D, BS, GMAX>), dim3((unsigned)nwg), dim3(kThreads),
+    hipLaunchKernelGGL((decode_valu_kernel<E, D, BS, GMAX, STREAM>), dim3((unsigned)nwg), dim3(kThreads),
                        smem, stream, p);
     return hipGetLastError();
 }
 
-template <typename E, int D, int BS>
+template <typename E, int D, int BS, bool STREAM>
 hipError_t launch_group(const DecodeParams& p, hipStream_t stream) {
-    if (p.group <= 1) return launch_shape<E, D, BS, 1>(p, stream);
-    if (p.group <= 2) return launch_shape<E, D, BS, 2>(p, stream);
-    if (p.group <= 4) return launch_shape<E, D, BS, 4>(p, stream);
-    if (p.group <= 8) return launch_shape<E, D, BS, 8>(p, stream);
-    return launch_shape<E, D, BS, 16>(p, stream);
+    if (p.group <= 1) return launch_shape<E, D, BS, 1, STREAM>(p, stream);
+    if (p.group <= 2) return launch_shape<E, D, BS, 2, STREAM>(p, stream);
+    if (p.group <= 4) return launch_shape<E, D, BS, 4, STREAM>(p, stream);
+    if (p.group <= 8) return launch_shape<E, D, BS, 8, STREAM>(p, stream);
+    return launch_shape<E, D, BS, 16, STREAM>(p, stream);
+}
+
+template <typename E, int D, int BS>
+hipError_t launch_policy(const DecodeParams& p, hipStream_t stream) {
+    return p.stream_kv ? launch_group<E, D, BS, true>(p, stream)
+                       : launch_group<E, D, BS, false>(p, stream);
 }
 
 template <typename E>
 hipError_t launch_dtype(const DecodeParams& p, hipStream_t stream) {
     if (p.head_dim == 64)
-        return p.block_size == 16 ? launch_group<E, 64, 16>(p, stream)
-                                  : launch_group<E, 64, 32>(p, stream);
-    return p.block_size == 16 ? launch_group<E, 128, 16>(p, stream)
-                              : launch_group<E, 128, 32>(p, stream);
+        return p.block_size == 16 ? launch_policy<E, 64, 16>(p, stream)
+                                  : launch_policy<E, 64, 32>(p, stream);
+    return p.block_size == 16 ? launch_policy<E, 128, 16>(p, stream)
+                              : launch_policy<E, 128, 32>(p, stream);
 }
 
 }  // namespace

@@ -64,11 +64,13 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
                     int32_t block_size, int32_t num_kv_heads, float scale, void* out,
                     int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                     int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
-                    pa_dtype dtype, int32_t partition_size, pa_kernel kernel, void* workspace,
-                    size_t workspace_bytes, bool need_out, bool force_split, Plan* plan) {
+                    pa_dtype dtype, int32_t partition_size, pa_kernel kernel, pa_kv_reuse reuse,
+                    void* workspace, size_t workspace_bytes, bool need_out, bool force_split,
+                    Plan* plan) {
     if (!valid_dtype(dtype)) return PA_ERR_ARG;
     if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
         return PA_ERR_ARG;
+    if (reuse != PA_KV_AUTO && reuse != PA_KV_STREAM && reuse != PA_KV_SHARED) return PA_ERR_ARG;
     pa_status st = shape_status(num_kv_heads, head_dim, block_size);
     if (st != PA_OK) return st;
     if (num_heads <= 0 || num_heads % num_kv_heads != 0) return PA_ERR_ARG;
@@ -124,6 +126,7 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.max_blocks_per_seq = max_blocks_per_seq;
     p.max_context_len = max_context_len;
     p.num_blocks = num_blocks;
+    p.stream_kv = reuse != PA_KV_SHARED;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -176,7 +179,7 @@ const char* pa_status_string(pa_status status) {
     return "unknown status";
 }
 
-int32_t pa_version(void) { return 100; }
+int32_t pa_version(void) { return 200; }
 
 int32_t pa_decode_partition_size(int32_t max_context_len, int32_t partition_size) {
     return resolve_partition(max_context_len, partition_size);
@@ -234,12 +237,13 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                     int32_t max_blocks_per_seq, int32_t max_context_len,
                     int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
-                    pa_kernel kernel, void* workspace, size_t workspace_bytes) {
+                    pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
+                    size_t workspace_bytes) {
     Plan plan;
     pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
                              num_kv_heads, scale, out, num_seqs, num_heads, head_dim,
                              max_blocks_per_seq, max_context_len, num_blocks, dtype,
-                             partition_size, kernel, workspace, workspace_bytes,
+                             partition_size, kernel, reuse, workspace, workspace_bytes,
                              /*need_out=*/true, /*force_split=*/false, &plan);
     if (st != PA_OK || num_seqs == 0) return st;
     st = launch_plan(plan, stream);
@@ -254,13 +258,14 @@ pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_
                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                               int32_t max_blocks_per_seq, int32_t max_context_len,
                               int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
-                              pa_kernel kernel, void* workspace, size_t workspace_bytes) {
+                              pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
+                              size_t workspace_bytes) {
     if (partition_size <= 0) return PA_ERR_ARG;
     Plan plan;
     pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
                              num_kv_heads, scale, nullptr, num_seqs, num_heads, head_dim,
                              max_blocks_per_seq, max_context_len, num_blocks, dtype,
-                             partition_size, kernel, workspace, workspace_bytes,
+                             partition_size, kernel, reuse, workspace, workspace_bytes,
                              /*need_out=*/false, /*force_split=*/true, &plan);
     if (st != PA_OK || num_seqs == 0) return st;
     return launch_plan(plan, stream);

@@ -14,6 +14,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, one L2 each
 
+// Third word of a raw buffer resource on gfx9-family chips (32-bit data
+// format, no swizzle); the range check then compares byte offsets against
+// the record count and returns zeros past it.
+constexpr int kBufferFlags = 0x00020000;
+
+// Cache-policy bits of a vector memory instruction on gfx950 (sc0 = 1,
+// nt = 2, sc1 = 16).  K/V pages that no other workgroup reads again are
+// streamed with nt; pages shared between sequences keep the default policy
+// so that concurrent readers hit in L2.
+constexpr int kPolicyReuse = 0;
+constexpr int kPolicyStream = 2;
+
 // Reinterpret a 32-bit pattern as float.  Always goes through a scalar: a
 // bit cast applied directly to an element of a vector value (v[i]) has been
 // seen to read the wrong element with this compiler.
@@ -33,6 +45,15 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // 16-byte global load/store through a plain vector type.
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
+}
+// 16-byte K/V load: non-temporal when the pages are streamed (read by one
+// workgroup per call), ordinary when other workgroups read them too.
+template <bool STREAM>
+__device__ __forceinline__ u32x4_t ld16_kv(const void* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    else
+        return *reinterpret_cast<const u32x4_t*>(p);
 }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
     *reinterpret_cast<u32x4_t*>(p) = v;

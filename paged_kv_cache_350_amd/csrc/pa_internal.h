@@ -31,6 +31,7 @@ struct DecodeParams {
     int32_t partition;     // tokens per partition (single pass: covers max_context_len)
     int32_t max_parts;     // partitions per (seq, head) in the workspace (1 = single pass)
     int32_t split;         // 1: write partials to ws, 0: write out
+    int32_t stream_kv;     // 1: no page is shared between sequences (streaming loads)
 };
 
 struct ReduceParams {

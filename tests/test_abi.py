@@ -45,7 +45,7 @@ def test_status_strings(L):
         assert pa.status_string(code)
     assert pa.status_string(0) == "ok"
     assert pa.status_string(-99) == "unknown status"
-    assert L.pa_version() == 100
+    assert L.pa_version() == 200
 
 
 def test_partition_policy_and_workspace_size(L):
@@ -69,11 +69,11 @@ FAKE = 1 << 20          # 16-byte aligned, never dereferenced: validation fails 
 def _decode(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, bs=16, hkv=8, scale=0.1, out=FAKE,
              stream=None, B=4, hq=32, d=128, maxb=16, maxctx=256, nb=100, dtype=1, part=0,
-             kernel=0, ws=None, wsb=0)
+             kernel=0, reuse=0, ws=None, wsb=0)
     a.update(kw)
     return L.pa_decode(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bs"], a["hkv"], a["scale"],
                        a["out"], a["stream"], a["B"], a["hq"], a["d"], a["maxb"], a["maxctx"],
-                       a["nb"], a["dtype"], a["part"], a["kernel"], a["ws"], a["wsb"])
+                       a["nb"], a["dtype"], a["part"], a["kernel"], a["reuse"], a["ws"], a["wsb"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -87,6 +87,8 @@ def _decode(L, **kw):
     (dict(hkv=0), pa.PA_ERR_ARG),
     (dict(dtype=7), pa.PA_ERR_ARG),
     (dict(kernel=9), pa.PA_ERR_ARG),
+    (dict(reuse=3), pa.PA_ERR_ARG),
+    (dict(reuse=-1), pa.PA_ERR_ARG),
     (dict(dtype=0, kernel=2), pa.PA_ERR_UNSUPPORTED), # MFMA kernel is bf16 only
     (dict(maxctx=257), pa.PA_ERR_ARG),                # beyond max_blocks_per_seq * block_size
     (dict(maxctx=-1), pa.PA_ERR_ARG),
@@ -108,9 +110,10 @@ def test_zero_sequences_is_a_no_op(L):
 
 def test_stage_entry_points_validate(L):
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 0.1, None, 4, 32, 128, 16, 256, 100, 1]
-    assert L.pa_decode_partition(*args, 0, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG      # needs explicit P
-    assert L.pa_decode_partition(*args, -1, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG
-    assert L.pa_decode_partition(*args, 64, 0, None, 0) == pa.PA_ERR_WORKSPACE
+    assert L.pa_decode_partition(*args, 0, 0, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG   # needs explicit P
+    assert L.pa_decode_partition(*args, -1, 0, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG
+    assert L.pa_decode_partition(*args, 64, 0, 0, None, 0) == pa.PA_ERR_WORKSPACE
+    assert L.pa_decode_partition(*args, 64, 0, 5, FAKE, 1 << 30) == pa.PA_ERR_ARG  # bad reuse
     assert L.pa_decode_reduce(FAKE, 16, FAKE, FAKE, None, 4, 32, 128, 256, 64, 1) == pa.PA_ERR_WORKSPACE
     assert L.pa_decode_reduce(FAKE, 1 << 30, FAKE, FAKE, None, 4, 32, 128, 256, 0, 1) == pa.PA_ERR_ARG
     assert L.pa_decode_reduce(FAKE, 1 << 30, None, FAKE, None, 4, 32, 128, 256, 64, 1) == pa.PA_ERR_NULL

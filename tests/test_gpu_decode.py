@@ -39,10 +39,18 @@ def _kernels(dtype):
     return ["valu", "mfma"] if dtype == "bf16" else ["valu"]
 
 
-def run_decode(pa, w, t, kernel="auto", partition_size=None):
+REUSE = ["stream", "shared"]
+
+
+def run_decode(pa, w, t, kernel="auto", partition_size=None, reuse="auto"):
     ps = w.partition_size if partition_size is None else partition_size
     return pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                     w.scale, w.max_context_len, partition_size=ps, kernel=kernel)
+                     w.scale, w.max_context_len, partition_size=ps, kernel=kernel, reuse=reuse)
+
+
+def natural_reuse(w):
+    """The load path a caller would pick: shared when sequences share pages."""
+    return "shared" if w.extra.get("shared_pages") else "stream"
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
@@ -55,11 +63,12 @@ def test_decode_small_all_paths(shape):
     run_step_updates(pa, w, t)
     ref = oracle_decode(w, t, range(w.num_seqs))
     for kernel in _kernels(dtype):
-        for ps in PATHS:
-            say("  kernel", kernel, "partition", ps)
-            out = run_decode(pa, w, t, kernel, ps)
-            torch.cuda.synchronize()
-            check_close(out_f64(out), ref, dtype, f"{shape} {kernel} P={ps}")
+        for reuse in REUSE:
+            for ps in PATHS:
+                say("  kernel", kernel, "reuse", reuse, "partition", ps)
+                out = run_decode(pa, w, t, kernel, ps, reuse)
+                torch.cuda.synchronize()
+                check_close(out_f64(out), ref, dtype, f"{shape} {kernel} {reuse} P={ps}")
 
 
 @pytest.mark.parametrize("figure", [False, True])
@@ -72,10 +81,11 @@ def test_tiny_workload(figure):
     t = W.make_tensors(w, "cuda")
     run_step_updates(pa, w, t)
     ref = oracle_decode(w, t, range(w.num_seqs))
-    for ps in PATHS:
-        out = run_decode(pa, w, t, "auto", ps)
-        torch.cuda.synchronize()
-        check_close(out_f64(out), ref, "f32", f"tiny P={ps}")
+    for reuse in REUSE:
+        for ps in PATHS:
+            out = run_decode(pa, w, t, "auto", ps, reuse)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, "f32", f"tiny {reuse} P={ps}")
 
 
 def test_empty_context_gives_zeros():
@@ -90,20 +100,23 @@ def test_empty_context_gives_zeros():
     ref = oracle_decode(w, t, range(w.num_seqs))
     assert not ref[2].any()
     for kernel in ("valu", "mfma"):
-        for ps in PATHS:
-            out = run_decode(pa, w, t, kernel, ps)
-            torch.cuda.synchronize()
-            got = out_f64(out)
-            assert not got[2].any()
-            check_close(got, ref, "bf16", f"empty {kernel} P={ps}")
+        for reuse in REUSE:
+            for ps in PATHS:
+                out = run_decode(pa, w, t, kernel, ps, reuse)
+                torch.cuda.synchronize()
+                got = out_f64(out)
+                assert not got[2].any()
+                check_close(got, ref, "bf16", f"empty {kernel} {reuse} P={ps}")
     # every sequence empty, max_context_len 0
     t["context_lens"].zero_()
     for kernel in ("valu", "mfma"):
-        for ps in (-1, 0):
-            out = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                            w.scale, 0, partition_size=ps, kernel=kernel)
-            torch.cuda.synchronize()
-            assert not out_f64(out).any()
+        for reuse in REUSE:
+            for ps in (-1, 0):
+                out = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                t["context_lens"], w.scale, 0, partition_size=ps, kernel=kernel,
+                                reuse=reuse)
+                torch.cuda.synchronize()
+                assert not out_f64(out).any()
 
 
 def _sample(w, n, seed):
@@ -118,8 +131,10 @@ def _sample(w, n, seed):
 @pytest.mark.parametrize("name", ["tiny", "llama3_8b", "llama3_70b", "prefix_share", "beam_fork",
                                   "long_context"])
 def test_named_workload_full_size(name):
-    """Full-size workload, library-default launch (as benchmarked), sampled
-    sequences against the oracle; the vector-ALU kernel as a second check."""
+    """Full-size workload in the launch configuration the benchmark times
+    (library-default partitions, the load path a caller would pick), sampled
+    sequences against the oracle; the other load path and the vector-ALU
+    kernel as further checks."""
     pa = require_gpu()
     w = W.by_name(name)
     say("full", name, w.summary())
@@ -127,12 +142,14 @@ def test_named_workload_full_size(name):
     run_step_updates(pa, w, t)
     seqs = _sample(w, 8, 11)
     ref = oracle_decode(w, t, seqs)
-    for kernel in ["auto", "valu"]:
-        out = run_decode(pa, w, t, kernel)
+    nat = natural_reuse(w)
+    other = "shared" if nat == "stream" else "stream"
+    for kernel, reuse in [("auto", nat), ("auto", other), ("valu", nat)]:
+        out = run_decode(pa, w, t, kernel, reuse=reuse)
         torch.cuda.synchronize()
         got = out_f64(out)[seqs]
-        stats = check_close(got, ref, w.dtype, f"{name} {kernel}")
-        say("  ", kernel, stats)
+        stats = check_close(got, ref, w.dtype, f"{name} {kernel} {reuse}")
+        say("  ", kernel, reuse, stats)
         assert np.isfinite(out_f64(out)).all()
 
 
@@ -144,22 +161,25 @@ def test_single_pass_matches_split_at_full_size():
     run_step_updates(pa, w, t)
     seqs = _sample(w, 6, 12)
     ref = oracle_decode(w, t, seqs)
-    for ps in (-1, 256, 1024):
-        out = run_decode(pa, w, t, "mfma", ps)
-        torch.cuda.synchronize()
-        check_close(out_f64(out)[seqs], ref, "bf16", f"P={ps}")
+    for reuse in REUSE:
+        for ps in (-1, 256, 1024):
+            out = run_decode(pa, w, t, "mfma", ps, reuse)
+            torch.cuda.synchronize()
+            check_close(out_f64(out)[seqs], ref, "bf16", f"{reuse} P={ps}")
 
 
-@pytest.mark.parametrize("kernel,ps", [("mfma", 0), ("mfma", -1), ("valu", 64), ("valu", -1)])
-def test_page_permutation_is_bit_identical(kernel, ps):
+@pytest.mark.parametrize("kernel,ps,reuse", [("mfma", 0, "stream"), ("mfma", -1, "stream"),
+                                             ("mfma", 0, "shared"), ("mfma", -1, "shared"),
+                                             ("valu", 64, "stream"), ("valu", -1, "shared")])
+def test_page_permutation_is_bit_identical(kernel, ps, reuse):
     """Moving physical pages (with the matching table edit) changes no bit:
     the work order depends only on logical positions."""
     pa = require_gpu()
     w = W.llama3_8b(seed=21, num_seqs=12, len_range=(1, 1500))
-    say("permutation", kernel, ps)
+    say("permutation", kernel, ps, reuse)
     t = W.make_tensors(w, "cuda")
     run_step_updates(pa, w, t)
-    base = run_decode(pa, w, t, kernel, ps).clone()
+    base = run_decode(pa, w, t, kernel, ps, reuse).clone()
     perm = torch.from_numpy(np.random.default_rng(22).permutation(w.num_blocks)).cuda()
     kc2 = torch.empty_like(t["k_cache"])
     vc2 = torch.empty_like(t["v_cache"])
@@ -167,8 +187,8 @@ def test_page_permutation_is_bit_identical(kernel, ps):
     vc2[perm] = t["v_cache"]
     tables2 = perm[t["block_tables"].long()].to(torch.int32).contiguous()
     out2 = pa.decode(t["q"], kc2, vc2, tables2, t["context_lens"], w.scale, w.max_context_len,
-                     partition_size=ps, kernel=kernel)
-    again = run_decode(pa, w, t, kernel, ps)
+                     partition_size=ps, kernel=kernel, reuse=reuse)
+    again = run_decode(pa, w, t, kernel, ps, reuse)
     torch.cuda.synchronize()
     assert bits_equal(out2, base)
     assert bits_equal(again, base)
@@ -180,11 +200,11 @@ def test_stage_api_equals_one_call():
     say("stages", w.summary())
     t = W.make_tensors(w, "cuda")
     run_step_updates(pa, w, t)
-    for P in (64, 512):
-        one = run_decode(pa, w, t, "mfma", P)
+    for P, reuse in ((64, "stream"), (512, "shared")):
+        one = run_decode(pa, w, t, "mfma", P, reuse)
         ws = pa.make_workspace(t["q"], w.max_context_len, P)
         pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                            w.scale, w.max_context_len, P, ws, kernel="mfma")
+                            w.scale, w.max_context_len, P, ws, kernel="mfma", reuse=reuse)
         two = torch.empty_like(one)
         pa.decode_reduce(ws, t["context_lens"], two, w.max_context_len, P)
         torch.cuda.synchronize()
@@ -199,10 +219,11 @@ def test_group_of_sixteen_and_head_dim_64():
     run_step_updates(pa, w, t)
     ref = oracle_decode(w, t, range(w.num_seqs))
     for kernel in ("valu", "mfma"):
-        for ps in (-1, 0, 128):
-            out = run_decode(pa, w, t, kernel, ps)
-            torch.cuda.synchronize()
-            check_close(out_f64(out), ref, "bf16", f"g16 {kernel} P={ps}")
+        for reuse in REUSE:
+            for ps in (-1, 0, 128):
+                out = run_decode(pa, w, t, kernel, ps, reuse)
+                torch.cuda.synchronize()
+                check_close(out_f64(out), ref, "bf16", f"g16 {kernel} {reuse} P={ps}")
 
 
 def test_bad_table_entries_stay_in_bounds():
@@ -216,11 +237,13 @@ def test_bad_table_entries_stay_in_bounds():
     ref = oracle_decode(w, t, range(w.num_seqs))
     bt = t["block_tables"].clone()
     bt[0, 2:] = 2 ** 30          # entries past ceil(17 / 16) = 2: never read
-    out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
-                    w.max_context_len, partition_size=0, kernel="mfma")
-    torch.cuda.synchronize()
-    check_close(out_f64(out), ref, "bf16", "padding entries")
+    for reuse in REUSE:
+        out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
+                        w.max_context_len, partition_size=0, kernel="mfma", reuse=reuse)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"padding entries {reuse}")
     bt[1, 0] = -5                # a used entry out of range: guarded, no fault
-    out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
-                    w.max_context_len, partition_size=0, kernel="mfma")
-    torch.cuda.synchronize()
+    for reuse in REUSE:
+        out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
+                        w.max_context_len, partition_size=0, kernel="mfma", reuse=reuse)
+        torch.cuda.synchronize()
