@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     KERNELS, LIB_PATH, REUSE, PA_BF16, PA_ERR_ARG, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_UNSUPPORTED,
     PA_ERR_WORKSPACE, PA_F32, PA_OK, PaError, copy_blocks, decode, decode_partition,
     decode_partition_size, decode_reduce, decode_workspace_size, kv_append, lib,
-    make_workspace, status_string,
+    make_workspace, probe_stream_read, status_string,
 )

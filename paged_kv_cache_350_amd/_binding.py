@@ -54,6 +54,7 @@ _SIGNATURES = {
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
+    "pa_probe_stream_read": ([_vp, _c_size, _c_int, _c_int, _vp, _vp], _c_int),
 }
 
 
@@ -243,3 +244,14 @@ def decode_reduce(workspace: torch.Tensor, context_lens: torch.Tensor, out: torc
                                 int(partition_size), _elem_dtype(out))
     _check("pa_decode_reduce", st)
     return out
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = True,
+                      num_workgroups: int = 0) -> None:
+    """Read every byte of ``buf`` once (measurement helper, not the decode path)."""
+    _dev_tensor("buf", buf)
+    _dev_tensor("sink", sink, dtype=torch.int32)
+    st = lib().pa_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                    int(bool(nontemporal)), int(num_workgroups), sink.data_ptr(),
+                                    _stream(buf))
+    _check("pa_probe_stream_read", st)

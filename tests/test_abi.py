@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol include/pa.h declares, and
+"""The C-ABI library loads, exports every symbol include/*.h declares, and
 rejects bad arguments on the host (CPU only: no call here reaches the GPU)."""
 
 import ctypes
@@ -8,15 +8,19 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 pa = pytest.importorskip("paged_kv_cache_350_amd")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|int32_t|const char\*)\s+(pa_\w+)\s*\(",
-                                 text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = open(header).read()
+        names |= set(re.findall(r"^\s*(?:pa_status|size_t|int32_t|const char\*)\s+(pa_\w+)\s*\(",
+                                text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["pa_kv_append", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_size",
                  "pa_status_string", "pa_decode_partition", "pa_decode_reduce",
-                 "pa_decode_partition_size", "pa_version"]:
+                 "pa_decode_partition_size", "pa_version", "pa_probe_stream_read"]:
         assert want in names
 
 
@@ -142,3 +146,12 @@ def test_binding_refuses_cpu_tensors():
     vc = torch.zeros(4, 2, 128, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         pa.copy_blocks(kc, vc, torch.zeros(1, 2, dtype=torch.int64))
+
+
+def test_probe_validates(L):
+    # pa_probe_stream_read(buf, bytes, nontemporal, num_workgroups, sink, stream)
+    assert L.pa_probe_stream_read(FAKE, 100, 1, 0, FAKE, None) == pa.PA_ERR_ARG      # not 16-byte multiple
+    assert L.pa_probe_stream_read(FAKE, 1024, 2, 0, FAKE, None) == pa.PA_ERR_ARG
+    assert L.pa_probe_stream_read(None, 1024, 1, 0, FAKE, None) == pa.PA_ERR_NULL
+    assert L.pa_probe_stream_read(FAKE + 8, 1024, 1, 0, FAKE, None) == pa.PA_ERR_ARG
+    assert L.pa_probe_stream_read(None, 0, 1, 0, None, None) == pa.PA_OK
