@@ -176,18 +176,25 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
 /*
  * Partition size pa_decode uses for a request: > 0 = split path with that
  * many tokens per partition, 0 = single pass, < 0 = invalid request
- * (PA_ERR_ARG).  Pure host arithmetic.
+ * (PA_ERR_ARG).  Pure host arithmetic.  An explicit partition_size (a
+ * multiple of 32) is returned as is and -1 gives 0.  The library default
+ * (partition_size 0) is a single pass when max_context_len <= 512;
+ * otherwise the largest power of two P in [512, 2048] with
+ * 8 P <= max_context_len and num_seqs * num_kv_heads * ceil(max_context_len / P)
+ * >= 2048 workgroups (512 if none qualifies), lowered to 256 when that
+ * leaves fewer than 1024 workgroups.
  */
-int32_t pa_decode_partition_size(int32_t max_context_len, int32_t partition_size);
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                 int32_t partition_size);
 
 /*
  * Workspace bytes pa_decode needs (0 for the single pass):
  * num_seqs * num_heads * ceil(max_context_len / P) * (head_dim + 2) * 4,
- * P = pa_decode_partition_size(max_context_len, partition_size).
- * Returns 0 for invalid arguments as well.
+ * P = pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
+ * partition_size).  Returns 0 for invalid arguments as well.
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 /*
  * pa_decode_partition -- first stage of the split path on its own: every

@@ -4,12 +4,13 @@
 //     out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // (the common factor 2^-M cancels).
 //
-// One workgroup of 256 threads per (sequence, head).  Pass 1: threads load the
-// partition maxima and reduce M across the workgroup; each partition's weight
-// 2^(m_p - M) goes to LDS.  Pass 2: thread t owns 4 consecutive dims
-// (t % (D/4)) and every (256 / (D/4))-th partition, accumulating weighted
-// 16-byte rows; the partial sums meet in LDS and the first D/4 threads round
-// and store.  The output is rounded once to its dtype.
+// One wavefront per (sequence, head), four per workgroup.  Lane q holds the
+// max, sum and weight 2^(m_q - M) of partition q (blocks of 64 partitions);
+// M and the denominator are wave reductions.  Each lane then owns D / 64
+// consecutive dims and walks the partitions, taking partition k's weight from
+// lane k with a scalar read-lane and its accumulator slice with one 4- or
+// 8-byte load (the wave reads a whole row, coalesced), four partitions in
+// flight.  The output is rounded once to its dtype.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -17,41 +18,52 @@ namespace pa_impl {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxStaged = 1024;          // partition weights held in LDS per pass
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = kWavesPerBlock * kWave;
+constexpr int kUnroll = 4;
+
+template <int N>
+struct FloatN;
+template <>
+struct FloatN<1> { typedef float T; };
+template <>
+struct FloatN<2> { typedef __attribute__((__vector_size__(2 * sizeof(float)))) float T; };
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int s = 32; s >= 1; s /= 2) v = fmaxf(v, __shfl_xor(v, s));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int s = 32; s >= 1; s /= 2) v += __shfl_xor(v, s);
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int k) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k));
+}
 
 template <typename E>
-__device__ __forceinline__ void put4(E* out, size_t i, const float (&v)[4]);
+__device__ __forceinline__ void store_out(E* out, size_t i, float v);
 template <>
-__device__ __forceinline__ void put4<float>(float* out, size_t i, const float (&v)[4]) {
-    for (int k = 0; k < 4; ++k) out[i + k] = v[k];
-}
+__device__ __forceinline__ void store_out<float>(float* out, size_t i, float v) { out[i] = v; }
 template <>
-__device__ __forceinline__ void put4<uint16_t>(uint16_t* out, size_t i, const float (&v)[4]) {
-    for (int k = 0; k < 4; ++k) out[i + k] = f32_to_bf16(v[k]);
-}
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-    for (int s = 32; s >= 1; s /= 2) v = fmaxf(v, __shfl_xor(v, s));
-    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
-    __syncthreads();
-    float r = red[0];
-    for (int w = 1; w < kThreads / kWave; ++w) r = fmaxf(r, red[w]);
-    __syncthreads();
-    return r;
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* out, size_t i, float v) {
+    out[i] = f32_to_bf16(v);
 }
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads)
 void decode_reduce_kernel(ReduceParams p) {
-    constexpr int NQ = D / 4;                 // float4 groups per row
-    constexpr int NP = kThreads / NQ;         // partitions summed in parallel
-    __shared__ float s_w[kMaxStaged];         // 2^(m_p - M)
-    __shared__ float s_red[kThreads / kWave];
-    __shared__ float s_acc[NP][D];
-    __shared__ float s_den[NP];
+    constexpr int DPL = D / kWave;                 // dims per lane
+    typedef typename FloatN<DPL>::T vec_t;
+    static_assert(D % kWave == 0 && (DPL == 1 || DPL == 2), "head_dim");
 
-    const size_t bh = blockIdx.x;
+    const int lane = threadIdx.x % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const size_t bh = (size_t)blockIdx.x * kWavesPerBlock + w;
+    const size_t pairs = (size_t)p.num_seqs * p.num_heads;
+    if (bh >= pairs) return;
     const int b = (int)(bh / (size_t)p.num_heads);
     int L = p.context_lens[b];
     L = L < 0 ? 0 : (L > p.max_context_len ? p.max_context_len : L);
@@ -62,47 +74,55 @@ void decode_reduce_kernel(ReduceParams p) {
     const float* acc = p.ws + bh * p.max_parts * D;
     const float* wm = p.ws + rows * D + bh * p.max_parts;
     const float* wl = p.ws + rows * D + rows + bh * p.max_parts;
+    E* out = reinterpret_cast<E*>(p.out) + bh * D;
 
     float M = neg_inf();
-    for (int q = threadIdx.x; q < n; q += kThreads) M = fmaxf(M, wm[q]);
-    M = block_max(M, s_red);
+    for (int q = lane; q < n; q += kWave) M = fmaxf(M, wm[q]);
+    M = wave_max(M);
 
-    const int t = threadIdx.x;
-    const int dq = t % NQ;
-    const int pl = t / NQ;
-    float a4[4] = {0.f, 0.f, 0.f, 0.f};
+    float a[DPL];
+    for (int i = 0; i < DPL; ++i) a[i] = 0.f;
     float den = 0.f;
-    for (int base = 0; base < n; base += kMaxStaged) {
-        const int cnt = min(kMaxStaged, n - base);
-        for (int q = t; q < cnt; q += kThreads) s_w[q] = fast_exp2(wm[base + q] - M);
-        __syncthreads();
-        for (int q = pl; q < cnt; q += NP) {
-            const float w = s_w[q];
-            const u32x4_t raw = ld16(acc + (size_t)(base + q) * D + 4 * dq);
-            for (int k = 0; k < 4; ++k) a4[k] = fmaf(w, u32_as_f32(raw[k]), a4[k]);
-            if (dq == 0) den = fmaf(w, wl[base + q], den);
+    for (int base = 0; base < n; base += kWave) {
+        const int q = base + lane;
+        const float wq = q < n ? fast_exp2(wm[q] - M) : 0.f;
+        den = fmaf(wq, q < n ? wl[q] : 0.f, den);
+        const int cnt = min(kWave, n - base);
+        const float* row = acc + (size_t)base * D + DPL * lane;
+        int k = 0;
+        for (; k + kUnroll <= cnt; k += kUnroll) {
+            vec_t v[kUnroll];
+            for (int u = 0; u < kUnroll; ++u) v[u] = *reinterpret_cast<const vec_t*>(row + (size_t)(k + u) * D);
+            for (int u = 0; u < kUnroll; ++u) {
+                const float wk = lane_value(wq, k + u);
+                if constexpr (DPL == 1) {
+                    a[0] = fmaf(wk, v[u], a[0]);
+                } else {
+                    a[0] = fmaf(wk, v[u][0], a[0]);
+                    a[1] = fmaf(wk, v[u][1], a[1]);
+                }
+            }
         }
-        __syncthreads();
-    }
-    for (int k = 0; k < 4; ++k) s_acc[pl][4 * dq + k] = a4[k];
-    if (dq == 0) s_den[pl] = den;
-    __syncthreads();
-    if (t < NQ) {
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        float dsum = 0.f;
-        for (int q = 0; q < NP; ++q) {
-            dsum += s_den[q];
-            for (int k = 0; k < 4; ++k) o[k] += s_acc[q][4 * t + k];
+        for (; k < cnt; ++k) {
+            const vec_t v = *reinterpret_cast<const vec_t*>(row + (size_t)k * D);
+            const float wk = lane_value(wq, k);
+            if constexpr (DPL == 1) {
+                a[0] = fmaf(wk, v, a[0]);
+            } else {
+                a[0] = fmaf(wk, v[0], a[0]);
+                a[1] = fmaf(wk, v[1], a[1]);
+            }
         }
-        const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
-        for (int k = 0; k < 4; ++k) o[k] = dsum > 0.f ? o[k] * inv : 0.f;
-        put4<E>(reinterpret_cast<E*>(p.out), bh * D + 4 * t, o);
     }
+    den = wave_sum(den);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int i = 0; i < DPL; ++i) store_out<E>(out, (size_t)DPL * lane + i, den > 0.f ? a[i] * inv : 0.f);
 }
 
 template <typename E>
 hipError_t launch_dtype(const ReduceParams& p, hipStream_t stream) {
-    const dim3 grid((unsigned)((uint64_t)p.num_seqs * p.num_heads));
+    const uint64_t pairs = (uint64_t)p.num_seqs * p.num_heads;
+    const dim3 grid((unsigned)((pairs + kWavesPerBlock - 1) / kWavesPerBlock));
     if (p.head_dim == 64)
         hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(kThreads), 0, stream, p);
     else

@@ -12,7 +12,11 @@ using pa_impl::ReduceParams;
 
 namespace {
 
-constexpr int32_t kDefaultPartition = 512;   // tokens per partition on the split path
+constexpr int32_t kSplitAbove = 512;         // contexts up to this length run in one pass
+constexpr int32_t kMinPartition = 256;       // library-default partition sizes: powers of two
+constexpr int32_t kMaxPartition = 2048;      // in [kMinPartition, kMaxPartition]
+constexpr int64_t kFillUnits = 2048;         // workgroups that keep 256 CUs busy for several rounds
+constexpr int64_t kMinUnits = 1024;          // below this, fall back to the smallest partition
 constexpr int32_t kChunk = 32;               // partitions are whole 32-token chunks
 constexpr int32_t kMaxGroup = 16;            // query heads per kv head
 constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
@@ -30,16 +34,32 @@ pa_status shape_status(int32_t num_kv_heads, int32_t head_dim, int32_t block_siz
     return PA_OK;
 }
 
-int32_t resolve_partition(int32_t max_context_len, int32_t partition_size) {
-    if (max_context_len < 0) return -1;
-    if (partition_size == -1) return 0;
-    if (partition_size == 0) return max_context_len > kDefaultPartition ? kDefaultPartition : 0;
-    if (partition_size < kChunk || partition_size % kChunk != 0) return -1;
-    return partition_size;
-}
-
 int32_t parts_for(int32_t max_context_len, int32_t partition) {
     return (int32_t)(((int64_t)max_context_len + partition - 1) / partition);
+}
+
+// Library default: the longest partition that still leaves at least 8
+// partitions in the longest context and kFillUnits (sequence, kv head,
+// partition) workgroups; longer partitions mean fewer partials to write and
+// merge and less per-workgroup set-up, shorter ones better balance over
+// ragged lengths.  Tiny batches drop to kMinPartition for parallelism.
+int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+    if (max_context_len <= kSplitAbove) return 0;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+    auto units = [&](int32_t P) { return pairs * parts_for(max_context_len, P); };
+    int32_t P = kMaxPartition;
+    while (P > kSplitAbove && ((int64_t)P * 8 > max_context_len || units(P) < kFillUnits)) P /= 2;
+    if (units(P) < kMinUnits) P = kMinPartition;
+    return P;
+}
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                          int32_t partition_size) {
+    if (max_context_len < 0) return -1;
+    if (partition_size == -1) return 0;
+    if (partition_size == 0) return default_partition(num_seqs, num_kv_heads, max_context_len);
+    if (partition_size < kChunk || partition_size % kChunk != 0) return -1;
+    return partition_size;
 }
 
 size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -79,7 +99,7 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_ARG;
     if (num_blocks > (int64_t)INT32_MAX + 1) return PA_ERR_ARG;      // table entries are int32
     if (!isfinite(scale)) return PA_ERR_ARG;
-    int32_t partition = resolve_partition(max_context_len, partition_size);
+    int32_t partition = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
     if (partition < 0) return PA_ERR_ARG;
     if (force_split && partition <= 0) return PA_ERR_ARG;
     if (!force_split && partition > 0 && max_context_len == 0) partition = 0;   // nothing to split
@@ -179,16 +199,17 @@ const char* pa_status_string(pa_status status) {
     return "unknown status";
 }
 
-int32_t pa_version(void) { return 200; }
+int32_t pa_version(void) { return 300; }
 
-int32_t pa_decode_partition_size(int32_t max_context_len, int32_t partition_size) {
-    return resolve_partition(max_context_len, partition_size);
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                 int32_t partition_size) {
+    return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0) return 0;
-    const int32_t partition = resolve_partition(max_context_len, partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    const int32_t partition = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
     if (partition <= 0) return 0;
     return workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, partition);
 }
@@ -278,7 +299,7 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     if (!valid_dtype(dtype)) return PA_ERR_ARG;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size <= 0) return PA_ERR_ARG;
-    const int32_t partition = resolve_partition(max_context_len, partition_size);
+    const int32_t partition = resolve_partition(num_seqs, 1, max_context_len, partition_size);
     if (partition <= 0) return PA_ERR_ARG;
     if ((uint64_t)num_seqs * (uint64_t)num_heads >= kMaxGrid) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;

@@ -49,22 +49,34 @@ def test_status_strings(L):
         assert pa.status_string(code)
     assert pa.status_string(0) == "ok"
     assert pa.status_string(-99) == "unknown status"
-    assert L.pa_version() == 200
+    assert L.pa_version() == 300
 
 
 def test_partition_policy_and_workspace_size(L):
-    assert pa.decode_partition_size(4096, 0) == 512
-    assert pa.decode_partition_size(512, 0) == 0          # short: single pass
-    assert pa.decode_partition_size(4096, -1) == 0
-    assert pa.decode_partition_size(4096, 256) == 256
-    assert pa.decode_partition_size(4096, 100) < 0        # not a multiple of 32
-    assert pa.decode_partition_size(4096, 16) < 0
-    # long-context workload: 8 seqs x 32 heads x 64 partitions x (128 + 2) floats
-    assert pa.decode_workspace_size(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert pa.decode_workspace_size(64, 32, 128, 4096, 0) == 64 * 32 * 8 * 130 * 4
-    assert pa.decode_workspace_size(64, 32, 128, 500, 0) == 0
-    assert pa.decode_workspace_size(64, 32, 128, 4096, -1) == 0
-    assert pa.decode_workspace_size(3, 4, 64, 33, 32) == 3 * 4 * 2 * 66 * 4
+    # explicit sizes and single pass
+    assert pa.decode_partition_size(64, 8, 4096, -1) == 0
+    assert pa.decode_partition_size(64, 8, 4096, 256) == 256
+    assert pa.decode_partition_size(64, 8, 4096, 100) < 0        # not a multiple of 32
+    assert pa.decode_partition_size(64, 8, 4096, 16) < 0
+    assert pa.decode_partition_size(64, 8, -1, 0) < 0
+    # library default, worked through the rule in pa.h:
+    assert pa.decode_partition_size(64, 8, 512, 0) == 0          # short: single pass
+    assert pa.decode_partition_size(64, 8, 4027, 0) == 512       # 8B-shaped batch
+    assert pa.decode_partition_size(256, 8, 8192, 0) == 1024     # 70B-shaped batch
+    assert pa.decode_partition_size(8, 8, 32768, 0) == 1024      # long context: 2048 gives 1024 units
+    assert pa.decode_partition_size(100, 8, 10512, 0) == 1024    # prefix sharing
+    assert pa.decode_partition_size(8, 8, 32774, 0) == 1024      # beams
+    assert pa.decode_partition_size(512, 8, 32768, 0) == 2048    # plenty of work
+    assert pa.decode_partition_size(1, 8, 32768, 0) == 256       # one sequence: parallelism first
+    assert pa.decode_partition_size(2, 1, 600, 0) == 256
+    # workspace = seqs x heads x parts x (D + 2) floats
+    assert pa.decode_workspace_size(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 64 * 32 * 8 * 130 * 4
+    assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0) == 256 * 64 * 8 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 8, 128, 500, 0) == 0
+    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, -1) == 0
+    assert pa.decode_workspace_size(3, 4, 4, 64, 33, 32) == 3 * 4 * 2 * 66 * 4
+    assert pa.decode_workspace_size(3, 4, 0, 64, 33, 32) == 0
 
 
 FAKE = 1 << 20          # 16-byte aligned, never dereferenced: validation fails first

@@ -202,7 +202,7 @@ def test_stage_api_equals_one_call():
     run_step_updates(pa, w, t)
     for P, reuse in ((64, "stream"), (512, "shared")):
         one = run_decode(pa, w, t, "mfma", P, reuse)
-        ws = pa.make_workspace(t["q"], w.max_context_len, P)
+        ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P)
         pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                             w.scale, w.max_context_len, P, ws, kernel="mfma", reuse=reuse)
         two = torch.empty_like(one)
