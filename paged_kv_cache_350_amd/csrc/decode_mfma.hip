@@ -59,6 +59,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
 constexpr int kHalf = 16;             // tokens per row tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
+constexpr int kSegPages = 256;        // page ids staged in LDS at a time
 
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
@@ -109,21 +110,22 @@ void decode_mfma_kernel(DecodeParams p) {
                                          (uint32_t)(p.num_kv_heads * p.max_parts));
     const int b = wi.b;
     const int g = wi.q % p.num_kv_heads;
-    const int part = wi.q / p.num_kv_heads;
+    const int slot = wi.q / p.num_kv_heads;
     const int G = p.group;
 
     int L = p.context_lens[b];
     const int cap = min(p.max_context_len, p.max_blocks_per_seq * BS);
     L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int start = part * p.partition;
+    const int part = partition_of(slot, p.max_parts, L, p.partition, SPLIT);
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     const size_t head0 = (size_t)b * p.num_heads + (size_t)g * G;
-    if (start >= L) {
-        if (!p.split && part == 0) {
+    if (part < 0) {
+        if (!p.split && slot == 0) {          // single pass, empty context: zeros
             for (int e = tid; e < G * D; e += kThreads) out[head0 * D + e] = 0;
         }
         return;
     }
+    const int start = part * p.partition;
     const int end = min(start + p.partition, L);
 
     // Q^T as the B operand: lane (hl, j) holds head hl, dims 32 s + 8 j .. + 8.
@@ -159,108 +161,125 @@ void decode_mfma_kernel(DecodeParams p) {
     f32x4_t acc[DC];
     for (int dc = 0; dc < DC; ++dc) acc[dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // The partition's page ids are staged in LDS, up to kSegPages at a time:
+    // one coalesced load by the whole workgroup, then each chunk reads its
+    // ids from LDS (a short on-chip latency) instead of starting with a
+    // dependent global load.  Ids are clamped to the pool.
+    __shared__ int spage[kSegPages];
     const int nchunks = (end - start + kChunk - 1) / kChunk;
-    for (int ci = w; ci < nchunks; ci += kWaves) {
-        const int cstart = start + ci * kChunk;
-        const int valid = min(kChunk, end - cstart);
-
-        // ---- pages of the chunk (wave-uniform)
-        const int blk0 = cstart / BS;
-        int pg0 = row[blk0];
-        if ((uint32_t)pg0 >= (uint64_t)p.num_blocks) pg0 = 0;
-        int pg1 = pg0;
-        if (BS == 16 && valid > kHalf) {
-            pg1 = row[blk0 + 1];
-            if ((uint32_t)pg1 >= (uint64_t)p.num_blocks) pg1 = 0;
+    const int blk_first = start / BS;
+    const int blk_end = (end + BS - 1) / BS;                 // one past the last page used
+    constexpr int kSegChunks = kSegPages * BS / kChunk;
+    for (int seg = 0; seg < nchunks; seg += kSegChunks) {
+        const int seg_blk = blk_first + seg * (kChunk / BS);
+        const int seg_n = min(kSegPages, blk_end - seg_blk);
+        if (seg > 0) __syncthreads();                        // previous segment fully consumed
+        for (int i = tid; i < seg_n; i += kThreads) {
+            const int pg = row[seg_blk + i];
+            spage[i] = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
         }
+        __syncthreads();
+        const int seg_end = min(nchunks, seg + kSegChunks);
+        for (int ci = seg + w; ci < seg_end; ci += kWaves) {
+            const int cstart = start + ci * kChunk;
+            const int valid = min(kChunk, end - cstart);
 
-        // ---- loads: K of both row tiles, V of every 16-dim tile
-        u32x4_t kraw[2][KSTEPS];
-        u32x4_t vop[DC];                 // V^T operand, 8 bf16 per lane
-        if constexpr (SPLIT) {
-            __amdgpu_buffer_rsrc_t krs[2], vrs[2];
+            // ---- pages of the chunk (wave-uniform)
+            const int lb = (ci - seg) * (kChunk / BS);
+            const int pg0 = __builtin_amdgcn_readfirstlane(spage[lb]);
+            const int pg1 = (BS == 16 && valid > kHalf) ? __builtin_amdgcn_readfirstlane(spage[lb + 1]) : pg0;
+
+            // ---- loads: K of both row tiles, V of every 16-dim tile
+            u32x4_t kraw[2][KSTEPS];
+            u32x4_t vop[DC];                 // V^T operand, 8 bf16 per lane
+            if constexpr (SPLIT) {
+                __amdgpu_buffer_rsrc_t krs[2], vrs[2];
+                for (int t = 0; t < 2; ++t) {
+                    const int page = t ? pg1 : pg0;
+                    const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
+                    const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
+                    // a half with no valid token gets an empty range: loads return 0
+                    const bool live = t == 0 || valid > kHalf;
+                    krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
+                    vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
+                }
+                for (int t = 0; t < 2; ++t)
+                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
+                u32x2_t vh[2][DC];
+                for (int t = 0; t < 2; ++t)
+                    for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
+                // every load of the chunk is in flight before the first MFMA waits on one
+                __builtin_amdgcn_sched_barrier(0);
+                for (int dc = 0; dc < DC; ++dc)
+                    vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+            } else {
+                const int kpage = (BS == 16 && tk >= kHalf) ? pg1 : pg0;
+                const uint16_t* kb = kc + ((size_t)kpage * kv_heads + g) * tile_elems +
+                                     (size_t)(tk % BS) * 8 + (size_t)j * BS * 8;
+                const int vpage = (BS == 16 && tv >= kHalf) ? pg1 : pg0;
+                const uint16_t* vb = vc + ((size_t)vpage * kv_heads + g) * tile_elems + (tv % BS) +
+                                     (size_t)r * BS;
+                for (int t = 0; t < 2; ++t)
+                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = ld16(kb + 32 * t + (size_t)s * 4 * BS * 8);
+                for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- S = K . Q^T
+            f32x4_t st[2];
             for (int t = 0; t < 2; ++t) {
-                const int page = t ? pg1 : pg0;
-                const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
-                const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
-                // a half with no valid token gets an empty range: loads return 0
-                const bool live = t == 0 || valid > kHalf;
-                krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
-                vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
+                st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < KSTEPS; ++s)
+                    st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[s], st[t], 0, 0, 0);
             }
+
+            // ---- online softmax; slot 4 t + i of lane (hl, j) is token slot_token(t, i, j)
+            float sc[8];
             for (int t = 0; t < 2; ++t)
-                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
-            u32x2_t vh[2][DC];
-            for (int t = 0; t < 2; ++t)
-                for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
+                for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
+            if (valid < kChunk) {
+                for (int t = 0; t < 2; ++t)
+                    for (int i = 0; i < 4; ++i)
+                        sc[4 * t + i] = (slot_token<SPLIT>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
+            }
+            float mx = sc[0];
+            for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // Lazy rescaling: the reference max moves only when a score exceeds it
+            // by more than kRescaleSlack (always on the first chunk, m_run = -inf).
+            // Between moves the weights are 2^(s - m_run) <= 2^kRescaleSlack; acc
+            // and l share the reference, so the result is the same.
+            const bool grow = mx > m_run + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {       // wave-uniform branch
+                const float mn = grow ? mx : m_run;
+                const float alpha = fast_exp2(m_run - mn);      // 0 on the first chunk
+                for (int dc = 0; dc < DC; ++dc) acc[dc] = acc[dc] * alpha;
+                l_run *= alpha;
+                m_run = mn;
+            }
+            bf16x8_t pf;
+            float psum = 0.f;
+            for (int k = 0; k < 8; ++k) {
+                const bf16_t pb = (bf16_t)fast_exp2(sc[k] - m_run);
+                pf[k] = pb;
+                psum += (float)pb;           // normalise with the weights actually used
+            }
+            l_run += psum;
+
+            // ---- O^T += V^T . P^T
+            if (valid < kChunk) {
+                // zero the value slots past the context: dword q holds slots 2 q, 2 q + 1
+                for (int q = 0; q < 4; ++q) {
+                    const int tok = slot_token<SPLIT>(q / 2, 2 * (q % 2), j);
+                    const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
+                    const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
+                    for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
+                }
+            }
             for (int dc = 0; dc < DC; ++dc)
-                vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
-        } else {
-            const int kpage = (BS == 16 && tk >= kHalf) ? pg1 : pg0;
-            const uint16_t* kb = kc + ((size_t)kpage * kv_heads + g) * tile_elems +
-                                 (size_t)(tk % BS) * 8 + (size_t)j * BS * 8;
-            const int vpage = (BS == 16 && tv >= kHalf) ? pg1 : pg0;
-            const uint16_t* vb = vc + ((size_t)vpage * kv_heads + g) * tile_elems + (tv % BS) +
-                                 (size_t)r * BS;
-            for (int t = 0; t < 2; ++t)
-                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = ld16(kb + 32 * t + (size_t)s * 4 * BS * 8);
-            for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
+                acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf, acc[dc], 0, 0, 0);
         }
-
-        // ---- S = K . Q^T
-        f32x4_t st[2];
-        for (int t = 0; t < 2; ++t) {
-            st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < KSTEPS; ++s)
-                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[s], st[t], 0, 0, 0);
-        }
-
-        // ---- online softmax; slot 4 t + i of lane (hl, j) is token slot_token(t, i, j)
-        float sc[8];
-        for (int t = 0; t < 2; ++t)
-            for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
-        if (valid < kChunk) {
-            for (int t = 0; t < 2; ++t)
-                for (int i = 0; i < 4; ++i)
-                    sc[4 * t + i] = (slot_token<SPLIT>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
-        }
-        float mx = sc[0];
-        for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy rescaling: the reference max moves only when a score exceeds it
-        // by more than kRescaleSlack (always on the first chunk, m_run = -inf).
-        // Between moves the weights are 2^(s - m_run) <= 2^kRescaleSlack; acc
-        // and l share the reference, so the result is the same.
-        const bool grow = mx > m_run + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {       // wave-uniform branch
-            const float mn = grow ? mx : m_run;
-            const float alpha = fast_exp2(m_run - mn);      // 0 on the first chunk
-            for (int dc = 0; dc < DC; ++dc) acc[dc] = acc[dc] * alpha;
-            l_run *= alpha;
-            m_run = mn;
-        }
-        bf16x8_t pf;
-        float psum = 0.f;
-        for (int k = 0; k < 8; ++k) {
-            const bf16_t pb = (bf16_t)fast_exp2(sc[k] - m_run);
-            pf[k] = pb;
-            psum += (float)pb;           // normalise with the weights actually used
-        }
-        l_run += psum;
-
-        // ---- O^T += V^T . P^T
-        if (valid < kChunk) {
-            // zero the value slots past the context: dword q holds slots 2 q, 2 q + 1
-            for (int q = 0; q < 4; ++q) {
-                const int tok = slot_token<SPLIT>(q / 2, 2 * (q % 2), j);
-                const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
-                const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
-                for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
-            }
-        }
-        for (int dc = 0; dc < DC; ++dc)
-            acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf, acc[dc], 0, 0, 0);
     }
 
     // ---- merge the four waves; lane (hl, j) holds dims 16 dc + 4 j + i of head hl

@@ -90,21 +90,22 @@ void decode_valu_kernel(DecodeParams p) {
                                          (uint32_t)(p.num_kv_heads * p.max_parts));
     const int b = wi.b;
     const int g = wi.q % p.num_kv_heads;
-    const int part = wi.q / p.num_kv_heads;
+    const int slot = wi.q / p.num_kv_heads;
     const int G = p.group;
 
     int L = p.context_lens[b];
     const int cap = min(p.max_context_len, p.max_blocks_per_seq * BS);
     L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int start = part * p.partition;
+    const int part = partition_of(slot, p.max_parts, L, p.partition, STREAM);
     E* out = reinterpret_cast<E*>(p.out);
     const size_t head0 = (size_t)b * p.num_heads + (size_t)g * G;
-    if (start >= L) {
-        if (!p.split && part == 0) {                  // empty context: zeros
+    if (part < 0) {
+        if (!p.split && slot == 0) {                  // single pass, empty context: zeros
             for (int e = tid; e < G * D; e += kThreads) store_out<E>(out, head0 * D + e, 0.f);
         }
         return;
     }
+    const int start = part * p.partition;
     const int end = min(start + p.partition, L);
 
     const E* qb = reinterpret_cast<const E*>(p.q) + head0 * D;

@@ -86,4 +86,20 @@ __device__ __forceinline__ WorkItem decode_work_item(uint32_t hw_id, uint32_t nu
     return w;
 }
 
+// Partition handled by work-item slot `slot` (0 .. max_parts - 1, the order
+// in which slots are dispatched) of a sequence with L tokens and partitions
+// of P tokens; -1 when the sequence has no such partition.
+//   from_start: slot s is partition s.  Sequences that share a prompt prefix
+//     read the same pages in the same slot, at about the same time.
+//   from_end: slots count partitions back from each sequence's end, largest
+//     distance first, so the last partition of every sequence -- the only
+//     partial, shorter one -- is dispatched last and the grid drains on
+//     small work units instead of full ones.
+__device__ __forceinline__ int partition_of(int slot, int max_parts, int L, int P, bool from_end) {
+    if (!from_end) return slot * P < L ? slot : -1;
+    const int nparts = (L + P - 1) / P;
+    const int k = max_parts - 1 - slot;          // distance from the last partition
+    return k < nparts ? nparts - 1 - k : -1;
+}
+
 }  // namespace pa_impl
