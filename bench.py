@@ -1,8 +1,10 @@
 """Benchmark: one paged-decode step per iteration on one MI355X.
 
 A step is the whole data-parallel path over one synthetic batch: the KV
-append of every sequence's newest token, then paged decode attention over all
-cached tokens (split path: partition kernel + merge kernel).  Inputs are
+append of every sequence's newest token and paged decode attention over all
+cached tokens.  By default the append runs inside the decode kernel
+(pa_decode_append: partition kernel + merge kernel on the split path);
+--step separate times pa_kv_append followed by pa_decode instead.  Inputs are
 resident in HBM before timing starts.
 
 Default workload: the Llama-3-8B-shaped layer -- 64 sequences, 32 query / 8
@@ -44,6 +46,9 @@ def _args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--step", default="fused", choices=["fused", "separate"],
+                    help="fused: the append runs inside the decode kernel (pa_decode_append); "
+                         "separate: pa_kv_append, then pa_decode")
     ap.add_argument("--reuse", default="auto", choices=["auto", "stream", "shared"],
                     help="K/V load path (auto: shared when the workload's sequences share pages)")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -209,18 +214,29 @@ def main(argv=None) -> int:
     t = W.make_tensors(w, "cuda")
     if len(w.copy_pairs):
         pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
-    # Set-up: every token the workload appends (for the prefix workload that
-    # is each sequence's whole suffix, i.e. its prefill).  The timed decode
-    # step then appends only the newest token of each sequence, as a decode
-    # step does; rewriting a slot with the same row is idempotent.
-    pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    # Set-up: every token the workload appends except each sequence's newest
+    # (for the prefix workload that is the rest of each suffix, its prefill).
+    # The timed decode step appends the newest token of each sequence --
+    # rows [B, Hkv, D] plus its slot, -1 for a sequence that appends nothing --
+    # and decodes; rewriting a slot with the same row is idempotent.
     newest = {}
     for i, b in enumerate(w.append_seq.tolist()):
         newest[b] = i
-    idx = torch.tensor(sorted(newest.values()), dtype=torch.long, device="cuda")
-    step_k = t["k_new"].index_select(0, idx).contiguous()
-    step_v = t["v_new"].index_select(0, idx).contiguous()
-    step_slots = t["slot_mapping"].index_select(0, idx).contiguous()
+    older = [i for i in range(len(w.append_seq)) if i not in set(newest.values())]
+    if older:
+        oi = torch.tensor(older, dtype=torch.long, device="cuda")
+        pa.kv_append(t["k_new"].index_select(0, oi).contiguous(),
+                     t["v_new"].index_select(0, oi).contiguous(),
+                     t["slot_mapping"].index_select(0, oi).contiguous(), t["k_cache"], t["v_cache"])
+    step_k = torch.zeros(w.num_seqs, w.num_kv_heads, w.head_dim, dtype=t["k_new"].dtype, device="cuda")
+    step_v = torch.zeros_like(step_k)
+    slots = np.full(w.num_seqs, -1, dtype=np.int64)
+    for b, i in newest.items():
+        step_k[b] = t["k_new"][i]
+        step_v[b] = t["v_new"][i]
+        slots[b] = w.append_slots[i]
+    step_slots = torch.from_numpy(slots).cuda()
+    fused = a.step == "fused"
     torch.cuda.synchronize()
 
     # the load path a caller picks: its block manager knows whether pages are shared
@@ -236,20 +252,27 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pa.kv_append(step_k, step_v, step_slots, t["k_cache"], t["v_cache"])
+        if not fused:
+            pa.kv_append(step_k, step_v, step_slots, t["k_cache"], t["v_cache"])
         if ev is not None:
             ev[1].record(stream)
+        app = dict(k_new=step_k, v_new=step_v, slot_mapping=step_slots) if fused else {}
         if split:
             pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                 t["context_lens"], w.scale, w.max_context_len, P, ws, kernel=a.kernel,
-                                reuse=reuse)
+                                reuse=reuse, **app)
             if ev is not None:
                 ev[2].record(stream)
             pa.decode_reduce(ws, t["context_lens"], out, w.max_context_len, P)
         else:
-            pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                      w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel,
-                      reuse=reuse)
+            if fused:
+                pa.decode_append(step_k, step_v, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                 t["context_lens"], w.scale, w.max_context_len, slot_mapping=step_slots,
+                                 out=out, partition_size=-1, kernel=a.kernel, reuse=reuse)
+            else:
+                pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                          w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel,
+                          reuse=reuse)
             if ev is not None:
                 ev[2].record(stream)
         if ev is not None:
@@ -317,10 +340,11 @@ def main(argv=None) -> int:
             "block_size": w.block_size, "sum_context_tokens": int(w.context_lens.sum()),
             "max_context_len": w.max_context_len, "num_blocks": w.num_blocks,
             "partition_size": P, "kernel": kernel_name, "reuse": reuse, "seed": w.seed,
-            "kv_bytes_per_step": kv_bytes, "appended_tokens_per_step": int(idx.numel()),
+            "kv_bytes_per_step": kv_bytes, "appended_tokens_per_step": int((slots >= 0).sum()),
+            "step": a.step,
         },
         "kernels_avg_us": {
-            "kv_append": round(append_ms * 1e3, 2),
+            "kv_append": None if fused else round(append_ms * 1e3, 2),
             (kernel_name + ("_partition" if split else "_single")): round(main_ms * 1e3, 2),
             "decode_reduce": round(reduce_ms * 1e3, 2) if split else None,
             "decode_total": round(decode_ms * 1e3, 2),

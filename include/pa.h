@@ -174,6 +174,40 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     size_t workspace_bytes);
 
 /*
+ * pa_decode_append -- the usual decode step in one pass: every sequence
+ * appends its newest token and attends over all L = context_lens[b] tokens,
+ * the new one included.  Sequence b's new rows k_new[b], v_new[b] are written
+ * into the slot of position L - 1 (page block_tables[b][(L-1) / block_size],
+ * offset (L-1) % block_size) by the workgroup that reads that position,
+ * which uses the new rows directly.  The result -- cache contents and
+ * output -- is bit-identical to pa_kv_append with those slots followed by
+ * pa_decode with the same arguments, and saves one launch and the append's
+ * dependent memory round trips.  [Internals, "How PagedAttention Works"
+ * items 2 and 3]
+ *
+ *   k_new, v_new  device, [num_seqs][num_kv_heads][head_dim], read
+ *   slot_mapping  device, [num_seqs] int64, or NULL (every sequence with
+ *                 L > 0 appends).  A negative entry means sequence b appends
+ *                 nothing this step (it only attends); a non-negative entry
+ *                 must be the slot of position L - 1 -- the slot written is
+ *                 always the one the block table gives.
+ *   k_cache/v_cache device, read, and written at one slot per appending
+ *                 sequence
+ * Other arguments and return values as for pa_decode.  Sequences with
+ * L == 0 append nothing and get zeros.
+ */
+pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           const void* q, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t block_size, int32_t num_kv_heads, float scale,
+                           void* out, hipStream_t stream,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                           pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
+                           size_t workspace_bytes);
+
+/*
  * Partition size pa_decode uses for a request: > 0 = split path with that
  * many tokens per partition, 0 = single pass, < 0 = invalid request
  * (PA_ERR_ARG).  Pure host arithmetic.  An explicit partition_size (a
@@ -206,9 +240,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  * stages directly.  partition_size must be given explicitly here (a
  * multiple of 32, > 0); size the workspace with pa_decode_workspace_size()
  * for that same partition_size.  max_context_len == 0 launches nothing.
+ * k_new, v_new, slot_mapping: NULL for a plain decode; otherwise the fused
+ * append of pa_decode_append (then this stage plus pa_decode_reduce is
+ * exactly pa_decode_append, and k_cache / v_cache are written).
  * Arguments otherwise as for pa_decode.
  */
-pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_cache,
+pa_status pa_decode_partition(const void* q, void* k_cache, void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens,
                               int32_t block_size, int32_t num_kv_heads, float scale,
                               hipStream_t stream,
@@ -216,7 +253,8 @@ pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_
                               int32_t max_blocks_per_seq, int32_t max_context_len,
                               int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
                               pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
-                              size_t workspace_bytes);
+                              size_t workspace_bytes, const void* k_new, const void* v_new,
+                              const int64_t* slot_mapping);
 
 /*
  * pa_decode_reduce -- second stage: merge the partitions of every

@@ -8,7 +8,7 @@ benchmark call.  Build the library with
 
 from ._binding import (  # noqa: F401
     KERNELS, LIB_PATH, REUSE, PA_BF16, PA_ERR_ARG, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_UNSUPPORTED,
-    PA_ERR_WORKSPACE, PA_F32, PA_OK, PaError, copy_blocks, decode, decode_partition,
+    PA_ERR_WORKSPACE, PA_F32, PA_OK, PaError, copy_blocks, decode, decode_append, decode_partition,
     decode_partition_size, decode_reduce, decode_workspace_size, kv_append, lib,
     make_workspace, probe_stream_read, status_string,
 )

@@ -48,9 +48,12 @@ _SIGNATURES = {
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                    _c_int, _vp, _c_size], _c_int),
+    "pa_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
+                          _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                          _c_int, _vp, _c_size], _c_int),
     "pa_decode_partition": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp,
                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
-                             _c_int, _vp, _c_size], _c_int),
+                             _c_int, _vp, _c_size, _vp, _vp, _vp], _c_int),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -218,19 +221,72 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
+def decode_append(k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  scale: float, max_context_len: int, slot_mapping: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, partition_size: int = 0, kernel: str = "auto",
+                  workspace: Optional[torch.Tensor] = None, reuse: str = "auto") -> torch.Tensor:
+    """Append each sequence's newest K/V row [B, Hkv, D] at position L - 1 and
+    decode, in one pass; returns out [B, Hq, D].  ``slot_mapping`` [B] int64
+    (optional): negative entries mark sequences that append nothing."""
+    nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len)
+    _dev_tensor("k_new", k_new, dtype=q.dtype, ndim=3)
+    _dev_tensor("v_new", v_new, dtype=q.dtype, ndim=3)
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError("k_new / v_new must be [num_seqs, num_kv_heads, head_dim]")
+    sm_ptr = None
+    if slot_mapping is not None:
+        _dev_tensor("slot_mapping", slot_mapping, dtype=torch.int64, ndim=1)
+        if slot_mapping.shape[0] != B:
+            raise ValueError("slot_mapping must have one entry per sequence")
+        sm_ptr = slot_mapping.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dtype=q.dtype, ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if workspace is None:
+        workspace = make_workspace(q, hkv, max_context_len, partition_size)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().pa_decode_append(k_new.data_ptr(), v_new.data_ptr(), sm_ptr, q.data_ptr(),
+                                k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                                context_lens.data_ptr(), bs, hkv, float(scale), out.data_ptr(),
+                                _stream(q), B, hq, d, block_tables.shape[1], int(max_context_len), nb,
+                                _elem_dtype(q), int(partition_size), KERNELS[kernel], REUSE[reuse],
+                                ws_ptr, ws_bytes)
+    _check("pa_decode_append", st)
+    return out
+
+
 def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                      max_context_len: int, partition_size: int, workspace: torch.Tensor,
-                     kernel: str = "auto", reuse: str = "auto") -> None:
-    """First stage of the split path only (partials into ``workspace``)."""
+                     kernel: str = "auto", reuse: str = "auto", k_new=None, v_new=None,
+                     slot_mapping=None) -> None:
+    """First stage of the split path only (partials into ``workspace``); with
+    ``k_new``/``v_new`` [B, Hkv, D] it also does pa_decode_append's append."""
     nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len)
     _dev_tensor("workspace", workspace, dtype=torch.float32)
+    kn = vn = sm = None
+    if k_new is not None or v_new is not None:
+        _dev_tensor("k_new", k_new, dtype=q.dtype, ndim=3)
+        _dev_tensor("v_new", v_new, dtype=q.dtype, ndim=3)
+        if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+            raise ValueError("k_new / v_new must be [num_seqs, num_kv_heads, head_dim]")
+        kn, vn = k_new.data_ptr(), v_new.data_ptr()
+        if slot_mapping is not None:
+            _dev_tensor("slot_mapping", slot_mapping, dtype=torch.int64, ndim=1)
+            if slot_mapping.shape[0] != B:
+                raise ValueError("slot_mapping must have one entry per sequence")
+            sm = slot_mapping.data_ptr()
     st = lib().pa_decode_partition(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                    block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,
                                    float(scale), _stream(q), B, hq, d, block_tables.shape[1],
                                    int(max_context_len), nb, _elem_dtype(q), int(partition_size),
                                    KERNELS[kernel], REUSE[reuse], workspace.data_ptr(),
-                                   workspace.numel() * 4)
+                                   workspace.numel() * 4, kn, vn, sm)
     _check("pa_decode_partition", st)
 
 

@@ -161,6 +161,30 @@ void decode_mfma_kernel(DecodeParams p) {
     f32x4_t acc[DC];
     for (int dc = 0; dc < DC; ++dc) acc[dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // Fused append (pa_decode_append): the workgroup that reads position
+    // L - 1 first stores kv head g's new K and V rows into that slot.  The
+    // barrier after the page-id staging below makes the stores visible to
+    // every wave of the workgroup, which then reads the new token like any
+    // other.  No other workgroup reads that page: without sharing it belongs
+    // to this (sequence, kv head) alone, and a sequence only appends into a
+    // page it owns (copy-on-write happens before).
+    const bool appends = p.k_new != nullptr && end == L &&    // workgroup-uniform
+                         (p.append_mask == nullptr || p.append_mask[b] >= 0);
+    if (appends) {
+        const int pos = L - 1;
+        const int pg_raw = row[pos / BS];
+        const int pg = (uint32_t)pg_raw >= (uint64_t)p.num_blocks ? 0 : pg_raw;
+        const int off = pos % BS;
+        const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
+        const size_t src = ((size_t)b * kv_heads + g) * D;
+        const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + src;
+        const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + src;
+        uint16_t* kw = const_cast<uint16_t*>(kc) + tile;
+        uint16_t* vw = const_cast<uint16_t*>(vc) + tile;
+        for (int c = tid; c < D / 8; c += kThreads) st16(kw + ((size_t)c * BS + off) * 8, ld16(kn + 8 * c));
+        for (int d = tid; d < D; d += kThreads) vw[(size_t)d * BS + off] = vn[d];
+    }
+
     // The partition's page ids are staged in LDS, up to kSegPages at a time:
     // one coalesced load by the whole workgroup, then each chunk reads its
     // ids from LDS (a short on-chip latency) instead of starting with a

@@ -108,6 +108,30 @@ void decode_valu_kernel(DecodeParams p) {
     const int start = part * p.partition;
     const int end = min(start + p.partition, L);
 
+    // Fused append (pa_decode_append): the workgroup that reads position
+    // L - 1 first stores kv head g's new K and V rows into that slot; the
+    // barrier after the query staging below makes the stores visible to the
+    // whole workgroup, which then reads the new token like any other.  No
+    // other workgroup reads that page (see the matrix-core kernel).
+    const bool appends = p.k_new != nullptr && end == L &&    // workgroup-uniform
+                         (p.append_mask == nullptr || p.append_mask[b] >= 0);
+    if (appends) {
+        constexpr int NCH = D * (int)sizeof(E) / 16;        // 16-byte chunks per K row
+        const int* trow = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+        const int pos = L - 1;
+        const int pg_raw = trow[pos / BS];
+        const int pg = (uint32_t)pg_raw >= (uint64_t)p.num_blocks ? 0 : pg_raw;
+        const int off = pos % BS;
+        const size_t tile = ((size_t)pg * p.num_kv_heads + g) * (size_t)D * BS;
+        const size_t src = ((size_t)b * p.num_kv_heads + g) * D;
+        const E* kn = reinterpret_cast<const E*>(p.k_new) + src;
+        const E* vn = reinterpret_cast<const E*>(p.v_new) + src;
+        E* kw = const_cast<E*>(reinterpret_cast<const E*>(p.k_cache)) + tile;
+        E* vw = const_cast<E*>(reinterpret_cast<const E*>(p.v_cache)) + tile;
+        for (int c = tid; c < NCH; c += kThreads) st16(kw + ((size_t)c * BS + off) * X, ld16(kn + c * X));
+        for (int d = tid; d < D; d += kThreads) vw[(size_t)d * BS + off] = vn[d];
+    }
+
     const E* qb = reinterpret_cast<const E*>(p.q) + head0 * D;
     for (int e = tid; e < GMAX * D; e += kThreads) {
         sq[e] = (e / D) < G ? load_elem<E>(qb + e) : 0.f;

@@ -134,6 +134,9 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.v_cache = v_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
+    p.append_mask = nullptr;
     p.out = out;
     p.ws = static_cast<float*>(workspace);
     p.scale_log2 = scale * 1.4426950408889634f;     // log2(e): scores in log2 units
@@ -272,7 +275,34 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     return launch_reduce(plan, context_lens, out, stream);
 }
 
-pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_cache,
+pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           const void* q, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t block_size, int32_t num_kv_heads, float scale,
+                           void* out, hipStream_t stream,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                           pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
+                           size_t workspace_bytes) {
+    Plan plan;
+    pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                             num_kv_heads, scale, out, num_seqs, num_heads, head_dim,
+                             max_blocks_per_seq, max_context_len, num_blocks, dtype,
+                             partition_size, kernel, reuse, workspace, workspace_bytes,
+                             /*need_out=*/true, /*force_split=*/false, &plan);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!k_new || !v_new) return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_ARG;
+    plan.p.k_new = k_new;
+    plan.p.v_new = v_new;
+    plan.p.append_mask = slot_mapping;
+    st = launch_plan(plan, stream);
+    if (st != PA_OK || plan.partition == 0) return st;
+    return launch_reduce(plan, context_lens, out, stream);
+}
+
+pa_status pa_decode_partition(const void* q, void* k_cache, void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens,
                               int32_t block_size, int32_t num_kv_heads, float scale,
                               hipStream_t stream,
@@ -280,7 +310,8 @@ pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_
                               int32_t max_blocks_per_seq, int32_t max_context_len,
                               int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
                               pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
-                              size_t workspace_bytes) {
+                              size_t workspace_bytes, const void* k_new, const void* v_new,
+                              const int64_t* slot_mapping) {
     if (partition_size <= 0) return PA_ERR_ARG;
     Plan plan;
     pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
@@ -289,6 +320,11 @@ pa_status pa_decode_partition(const void* q, const void* k_cache, const void* v_
                              partition_size, kernel, reuse, workspace, workspace_bytes,
                              /*need_out=*/false, /*force_split=*/true, &plan);
     if (st != PA_OK || num_seqs == 0) return st;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
+    plan.p.k_new = k_new;
+    plan.p.v_new = v_new;
+    plan.p.append_mask = k_new ? slot_mapping : nullptr;
     return launch_plan(plan, stream);
 }
 

@@ -16,6 +16,9 @@ struct DecodeParams {
     const void* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    const void* k_new;     // fused append: new rows [num_seqs][num_kv_heads][head_dim], or null
+    const void* v_new;
+    const int64_t* append_mask;   // fused append: sequences with a negative entry append nothing (or null)
     void* out;             // final output (single pass)
     float* ws;             // partials (split): acc | m | l, see ws_* helpers
     float scale_log2;      // scale * log2(e): scores are kept in log2 units

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["pa_kv_append", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_size",
                  "pa_status_string", "pa_decode_partition", "pa_decode_reduce",
-                 "pa_decode_partition_size", "pa_version", "pa_probe_stream_read"]:
+                 "pa_decode_partition_size", "pa_version", "pa_probe_stream_read",
+                 "pa_decode_append"]:
         assert want in names
 
 
@@ -126,10 +127,14 @@ def test_zero_sequences_is_a_no_op(L):
 
 def test_stage_entry_points_validate(L):
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 0.1, None, 4, 32, 128, 16, 256, 100, 1]
-    assert L.pa_decode_partition(*args, 0, 0, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG   # needs explicit P
-    assert L.pa_decode_partition(*args, -1, 0, 0, FAKE, 1 << 30) == pa.PA_ERR_ARG
-    assert L.pa_decode_partition(*args, 64, 0, 0, None, 0) == pa.PA_ERR_WORKSPACE
-    assert L.pa_decode_partition(*args, 64, 0, 5, FAKE, 1 << 30) == pa.PA_ERR_ARG  # bad reuse
+    N = (None, None, None)                 # no fused append
+    assert L.pa_decode_partition(*args, 0, 0, 0, FAKE, 1 << 30, *N) == pa.PA_ERR_ARG   # needs explicit P
+    assert L.pa_decode_partition(*args, -1, 0, 0, FAKE, 1 << 30, *N) == pa.PA_ERR_ARG
+    assert L.pa_decode_partition(*args, 64, 0, 0, None, 0, *N) == pa.PA_ERR_WORKSPACE
+    assert L.pa_decode_partition(*args, 64, 0, 5, FAKE, 1 << 30, *N) == pa.PA_ERR_ARG  # bad reuse
+    # a fused append needs both rows, 16-byte aligned
+    assert L.pa_decode_partition(*args, 64, 0, 0, FAKE, 1 << 30, FAKE, None, None) == pa.PA_ERR_NULL
+    assert L.pa_decode_partition(*args, 64, 0, 0, FAKE, 1 << 30, FAKE, FAKE + 2, None) == pa.PA_ERR_ARG
     assert L.pa_decode_reduce(FAKE, 16, FAKE, FAKE, None, 4, 32, 128, 256, 64, 1) == pa.PA_ERR_WORKSPACE
     assert L.pa_decode_reduce(FAKE, 1 << 30, FAKE, FAKE, None, 4, 32, 128, 256, 0, 1) == pa.PA_ERR_ARG
     assert L.pa_decode_reduce(FAKE, 1 << 30, None, FAKE, None, 4, 32, 128, 256, 64, 1) == pa.PA_ERR_NULL
@@ -167,3 +172,22 @@ def test_probe_validates(L):
     assert L.pa_probe_stream_read(None, 1024, 1, 0, FAKE, None) == pa.PA_ERR_NULL
     assert L.pa_probe_stream_read(FAKE + 8, 1024, 1, 0, FAKE, None) == pa.PA_ERR_ARG
     assert L.pa_probe_stream_read(None, 0, 1, 0, None, None) == pa.PA_OK
+
+
+def test_decode_append_validates(L):
+    # pa_decode_append(k_new, v_new, slot_mapping, q, kc, vc, bt, cl, bs, hkv, scale, out, stream,
+    #                  B, hq, d, maxb, maxctx, nb, dtype, part, kernel, reuse, ws, wsb)
+    def call(**kw):
+        a = dict(kn=FAKE, vn=FAKE, sm=None, q=FAKE, B=4, bs=16, ws=None, wsb=0, part=-1, reuse=0)
+        a.update(kw)
+        return L.pa_decode_append(a["kn"], a["vn"], a["sm"], a["q"], FAKE, FAKE, FAKE, FAKE, a["bs"], 8,
+                                  0.1, FAKE, None, a["B"], 32, 128, 16, 256, 100, 1, a["part"], 0,
+                                  a["reuse"], a["ws"], a["wsb"])
+    assert call(kn=None) == pa.PA_ERR_NULL
+    assert call(vn=None) == pa.PA_ERR_NULL
+    assert call(kn=FAKE + 8) == pa.PA_ERR_ARG
+    assert call(q=None) == pa.PA_ERR_NULL
+    assert call(bs=8) == pa.PA_ERR_UNSUPPORTED
+    assert call(reuse=7) == pa.PA_ERR_ARG
+    assert call(part=256) == pa.PA_ERR_WORKSPACE
+    assert call(B=0, kn=None, vn=None, q=None) == pa.PA_OK
