@@ -9,8 +9,9 @@
 // M and the denominator are wave reductions.  Each lane then owns D / 64
 // consecutive dims and walks the partitions, taking partition k's weight from
 // lane k with a scalar read-lane and its accumulator slice with one 4- or
-// 8-byte load (the wave reads a whole row, coalesced), four partitions in
-// flight.  The output is rounded once to its dtype.
+// 8-byte load (the wave reads a whole row, coalesced).  The first eight rows
+// are loaded together with the maxima and sums, later ones four at a time.
+// The output is rounded once to its dtype.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -21,6 +22,7 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
 constexpr int kUnroll = 4;
+constexpr int kPre = 8;          // partitions whose rows are loaded up front
 
 template <int N>
 struct FloatN;
@@ -76,6 +78,16 @@ void decode_reduce_kernel(ReduceParams p) {
     const float* wl = p.ws + rows * D + rows + bh * p.max_parts;
     E* out = reinterpret_cast<E*>(p.out) + bh * D;
 
+    // The first kPre partitions' accumulator slices do not depend on the
+    // maxima: their loads go out together with those of m and l.
+    vec_t pre[kPre];
+    {
+        const float* row = acc + DPL * lane;
+        for (int u = 0; u < kPre; ++u) {
+            if (u < n) pre[u] = *reinterpret_cast<const vec_t*>(row + (size_t)u * D);
+            else pre[u] = vec_t{};
+        }
+    }
     float M = neg_inf();
     for (int q = lane; q < n; q += kWave) M = fmaxf(M, wm[q]);
     M = wave_max(M);
@@ -90,6 +102,20 @@ void decode_reduce_kernel(ReduceParams p) {
         const int cnt = min(kWave, n - base);
         const float* row = acc + (size_t)base * D + DPL * lane;
         int k = 0;
+        if (base == 0) {
+            for (int u = 0; u < kPre; ++u) {
+                if (u < cnt) {
+                    const float wk = lane_value(wq, u);
+                    if constexpr (DPL == 1) {
+                        a[0] = fmaf(wk, pre[u], a[0]);
+                    } else {
+                        a[0] = fmaf(wk, pre[u][0], a[0]);
+                        a[1] = fmaf(wk, pre[u][1], a[1]);
+                    }
+                }
+            }
+            k = min(kPre, cnt);
+        }
         for (; k + kUnroll <= cnt; k += kUnroll) {
             vec_t v[kUnroll];
             for (int u = 0; u < kUnroll; ++u) v[u] = *reinterpret_cast<const vec_t*>(row + (size_t)(k + u) * D);
