@@ -56,11 +56,15 @@ def _args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
-    ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe", "copy_calib"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe", "copy_calib",
+                                                         "blockmgr"],
                     help="copy_probe: time pa_copy_blocks on an eager fork of a 32,768-token "
                          "prompt to 7 beams (7,168 pages of 32 tokens, K and V); copy_calib: "
                          "the same number of page copies with 7,168 distinct sources (a plain "
-                         "copy of known size, used to scale rocprofv3 traffic counters)")
+                         "copy of known size, used to scale rocprofv3 traffic counters); "
+                         "blockmgr: host time of one decode step's page bookkeeping (append "
+                         "for every sequence + block tables), native manager vs the Python one "
+                         "(no GPU needed)")
     return ap.parse_args(argv)
 
 
@@ -189,6 +193,51 @@ def copy_probe(a, torch, pa, W) -> int:
     return 0
 
 
+def blockmgr_bench(a) -> int:
+    """Decode-step bookkeeping of the Llama-3-70B-shaped batch: every one of
+    the 256 sequences appends a token, then the int32 block tables and
+    context lengths the kernels take are built.  Native manager (libpa) vs
+    the host Python manager, same pool and page order."""
+    import paged_kv_cache_350_amd as pa
+    import workloads as W
+    w = W.llama3_70b()
+    steps = a.steps
+    seqs = list(range(w.num_seqs))
+    lens = (w.context_lens.astype(np.int64) - 1).tolist()
+    grow = w.num_seqs * (steps // w.block_size + 2)
+    nb = w.num_blocks + grow
+    order = np.random.default_rng(w.seed).permutation(nb)
+    maxb = -(-(int(max(lens)) + steps) // w.block_size)
+
+    def run(mgr, native):
+        for b, L in zip(seqs, lens):
+            mgr.allocate(b, L)
+        if native:
+            ids = np.asarray(seqs, dtype=np.int64)
+            tables, ctx = mgr.block_tables(ids, maxb, pad_page=0)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            if native:        # the tables are kept current in place
+                slots, copies = mgr.append(ids, tables, ctx)
+            else:
+                slots = np.array([mgr.append_token(b) for b in seqs], dtype=np.int64)
+                tables = np.zeros((len(seqs), maxb), dtype=np.int32)
+                for i, b in enumerate(seqs):
+                    pg = mgr.tables[b]
+                    tables[i, :len(pg)] = pg
+                ctx = np.array([mgr.lengths[b] for b in seqs], dtype=np.int32)
+        return (time.perf_counter() - t0) / steps * 1e6, tables, ctx, slots
+
+    nat_us, t_n, c_n, s_n = run(pa.NativeBlockManager(nb, w.block_size, free_order=order), True)
+    py_us, t_p, c_p, s_p = run(W.BlockManager(nb, w.block_size, free_order=order), False)
+    same = bool(np.array_equal(t_n, t_p) and np.array_equal(c_n, c_p) and np.array_equal(s_n, s_p))
+    print(json.dumps({"mode": "blockmgr", "workload": w.name, "num_seqs": w.num_seqs, "steps": steps,
+                      "native_us_per_step": round(nat_us, 2), "host_python_us_per_step": round(py_us, 2),
+                      "speedup": round(py_us / nat_us, 1), "identical_tables_slots": same,
+                      "pool_pages": nb, "max_blocks_per_seq": maxb}), flush=True)
+    return 0 if same else 1
+
+
 def main(argv=None) -> int:
     a = _args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -197,6 +246,9 @@ def main(argv=None) -> int:
                                    "part of this build (see the design notes on sharding)",
                           "n_gpus": a.gpus}), flush=True)
         return 2
+
+    if a.mode == "blockmgr":
+        return blockmgr_bench(a)
 
     import torch
     import paged_kv_cache_350_amd as pa

@@ -64,7 +64,10 @@ typedef enum pa_status {
     PA_ERR_ARG = -2,         /* a size or count is out of range or inconsistent */
     PA_ERR_UNSUPPORTED = -3, /* valid request outside the shapes listed above */
     PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
-    PA_ERR_HIP = -5          /* the HIP runtime refused a launch */
+    PA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
+    PA_ERR_OUT_OF_PAGES = -6, /* block manager: the page pool is exhausted */
+    PA_ERR_NOT_FOUND = -7,   /* block manager: no sequence with that id */
+    PA_ERR_HOST_MEMORY = -8  /* block manager: host allocation failed */
 } pa_status;
 
 typedef enum pa_dtype {

@@ -12,3 +12,4 @@ from ._binding import (  # noqa: F401
     decode_partition_size, decode_reduce, decode_workspace_size, kv_append, lib,
     make_workspace, probe_stream_read, status_string,
 )
+from .block_manager import NativeBlockManager, OutOfPages  # noqa: F401,E402

@@ -44,11 +44,12 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """HIP translation units (*.hip) and host-only C++ ones (*.cpp)."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str, verbose: bool, extra) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+    obj = os.path.join(OBJDIR, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

@@ -198,6 +198,9 @@ const char* pa_status_string(pa_status status) {
                                         "<= 16 query heads per kv head, bf16 for the MFMA kernel)";
         case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_size()";
         case PA_ERR_HIP: return "HIP runtime error while launching";
+        case PA_ERR_OUT_OF_PAGES: return "out of physical pages: the page pool is exhausted";
+        case PA_ERR_NOT_FOUND: return "no sequence with that id";
+        case PA_ERR_HOST_MEMORY: return "host memory allocation failed";
     }
     return "unknown status";
 }

@@ -1,0 +1,84 @@
+"""Decode steps driven end to end by the native page allocator, on the GPU.
+
+Six sequences fork one 40-token prompt (its last page is shared and partly
+filled, so their first appends copy-on-write) and four more run on their own.
+Every step the manager appends a token to each sequence and keeps the block
+tables current in place; its copy pairs go to pa_copy_blocks, the new rows to
+pa_decode_append (or pa_kv_append + pa_decode on alternate steps).  A host
+mirror of the caches is updated with the oracle's copy and append; each
+step's output is checked against the oracle decode and the caches bit for bit
+at the end."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import check_close, out_f64, require_gpu, say, storage_np
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_loop_driven_by_native_manager():
+    pa = require_gpu()
+    bs, hq, hkv, d, nb, maxb, steps = 16, 32, 8, 128, 300, 10, 14
+    rng = np.random.default_rng(31)
+    m = pa.NativeBlockManager(nb, bs, free_order=rng.permutation(nb))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(32)
+
+    def rows(n):
+        return (torch.randn(n, hkv, d, generator=g, device="cuda").to(torch.bfloat16),
+                torch.randn(n, hkv, d, generator=g, device="cuda").to(torch.bfloat16))
+
+    x = W.chunk_elems("bf16")
+    nan = float("nan")
+    kc = torch.full((nb, hkv, d // x, bs, x), nan, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((nb, hkv, d, bs), nan, dtype=torch.bfloat16, device="cuda")
+    hk, hv = storage_np(kc), storage_np(vc)                 # host mirror
+
+    def prefill(seq, n):
+        slots, copies = m.append(np.full(n, seq, dtype=np.int64))
+        assert len(copies) == 0
+        k, v = rows(n)
+        pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
+        return oracle.kv_append(storage_np(k), storage_np(v), slots, hk, hv, bs)
+
+    m.allocate(0, 0)
+    hk, hv = prefill(0, 40)
+    for child in range(1, 6):
+        m.fork(0, child)
+    for s in range(6, 10):
+        m.allocate(s, 0)
+        hk, hv = prefill(s, int(rng.integers(1, 100)))
+    ids = np.arange(10, dtype=np.int64)
+    tables, lens = m.block_tables(ids, maxb, pad_page=nb - 1)
+    tables, lens = tables.copy(), lens.copy()
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    copies_seen = 0
+    for step in range(steps):
+        slots, copies = m.append(ids, tables, lens)
+        copies_seen += len(copies)
+        say("step", step, "copies", copies.tolist())
+        if len(copies):
+            pa.copy_blocks(kc, vc, torch.from_numpy(np.ascontiguousarray(copies)).cuda())
+            hk, hv = oracle.copy_blocks(hk, hv, copies)
+        k, v = rows(len(ids))
+        q = torch.randn(len(ids), hq, d, generator=g, device="cuda").to(torch.bfloat16)
+        bt = torch.from_numpy(tables).cuda()
+        cl = torch.from_numpy(lens).cuda()
+        maxctx = int(lens.max())
+        if step % 2 == 0:
+            out = pa.decode_append(k, v, q, kc, vc, bt, cl, scale, maxctx,
+                                   slot_mapping=torch.from_numpy(slots).cuda(), reuse="shared")
+        else:
+            pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
+            out = pa.decode(q, kc, vc, bt, cl, scale, maxctx, reuse="shared")
+        torch.cuda.synchronize()
+        hk, hv = oracle.kv_append(storage_np(k), storage_np(v), slots, hk, hv, bs)
+        ref = oracle.decode(storage_np(q), hk, hv, tables, lens, scale, bs, "bf16")
+        check_close(out_f64(out), ref, "bf16", f"step {step}")
+    assert copies_seen == 5                                  # five children leave the shared page
+    assert np.array_equal(storage_np(kc).view(np.uint16), hk.view(np.uint16))
+    assert np.array_equal(storage_np(vc).view(np.uint16), hv.view(np.uint16))

@@ -42,6 +42,14 @@ import numpy as np
 
 from .blockmgr import BlockManager
 
+PROMPT_SEQ = -1      # sequence id of a shared prompt before it is forked
+
+
+def _manager(factory, num_blocks: int, block_size: int, free_order):
+    """Block manager for a workload: the host fixture, or any class with the
+    same interface passed as ``factory`` (e.g. the native one)."""
+    return (factory or BlockManager)(num_blocks, block_size, free_order=free_order)
+
 ELEM_BYTES = {"f32": 4, "bf16": 2}
 
 
@@ -167,7 +175,7 @@ def _plain(name: str, seed: int, dtype: str, lens: np.ndarray, num_heads: int,
            num_kv_heads: int, head_dim: int, block_size: int,
            rng: np.random.Generator, num_blocks: Optional[int] = None,
            partition_size: int = 0, description: str = "",
-           first_table: Optional[Sequence[int]] = None) -> Workload:
+           first_table: Optional[Sequence[int]] = None, manager=None) -> Workload:
     """Independent sequences; each appends its newest token (position L-1).
 
     Before the step every sequence holds L-1 tokens; the block manager gives
@@ -189,7 +197,7 @@ def _plain(name: str, seed: int, dtype: str, lens: np.ndarray, num_heads: int,
         first = [int(x) for x in first_table]
         rest = [int(x) for x in perm if int(x) not in first]
         perm = np.asarray(first + rest)
-    mgr = BlockManager(num_blocks, bs, free_order=perm)
+    mgr = _manager(manager, num_blocks, bs, perm)
     seqs = list(range(len(lens)))
     for b in seqs:
         mgr.allocate(b, int(lens[b]) - 1)
@@ -212,7 +220,7 @@ def _plain(name: str, seed: int, dtype: str, lens: np.ndarray, num_heads: int,
         partition_size=partition_size, description=description)
 
 
-def tiny(seed: int = 0, figure_table: bool = False) -> Workload:
+def tiny(seed: int = 0, figure_table: bool = False, manager=None) -> Workload:
     """2 sequences of 36 and 42 tokens, block 16, pool of 16 pages, 4 q = 4 kv
     heads, head_dim 64, fp32.  With ``figure_table`` sequence 0 sits on pages
     7, 14, 2 as in the page-table figure of "What is PagedAttention?"."""
@@ -220,12 +228,13 @@ def tiny(seed: int = 0, figure_table: bool = False) -> Workload:
     lens = np.array([36, 42])
     return _plain("tiny" + ("_figure" if figure_table else ""), seed, "f32", lens,
                   4, 4, 64, 16, rng, num_blocks=16,
-                  first_table=[7, 14, 2] if figure_table else None,
+                  first_table=[7, 14, 2] if figure_table else None, manager=manager,
                   description="2 seqs (36, 42 tokens), bs 16, pool 16, 4/4 heads, D 64, fp32")
 
 
 def llama3_8b(seed: int = 1, num_seqs: int = 64, len_range: Tuple[int, int] = (512, 4096),
-              dtype: str = "bf16", block_size: int = 16, partition_size: int = 0) -> Workload:
+              dtype: str = "bf16", block_size: int = 16, partition_size: int = 0,
+              manager=None) -> Workload:
     """Llama-3-8B-shaped layer: 32 q / 8 kv heads, head_dim 128, block 16,
     context lengths integer-uniform in ``len_range`` (inclusive), pool = pages
     needed + 10 %, ids randomly permuted."""
@@ -234,14 +243,14 @@ def llama3_8b(seed: int = 1, num_seqs: int = 64, len_range: Tuple[int, int] = (5
     return _plain("llama3_8b" if (num_seqs, len_range) == (64, (512, 4096)) else
                   f"llama3_8b_b{num_seqs}_l{len_range[0]}-{len_range[1]}",
                   seed, dtype, lens, 32, 8, 128, block_size, rng,
-                  partition_size=partition_size,
+                  partition_size=partition_size, manager=manager,
                   description=f"{num_seqs} seqs, L~U[{len_range[0]},{len_range[1]}], "
                               f"32/8 heads, D 128, bs {block_size}, {dtype}")
 
 
 def llama3_70b(seed: int = 2, num_seqs: int = 256, median: float = 1500.0,
                sigma: float = 1.0, clip: Tuple[int, int] = (64, 8192),
-               dtype: str = "bf16", partition_size: int = 0) -> Workload:
+               dtype: str = "bf16", partition_size: int = 0, manager=None) -> Workload:
     """Llama-3-70B-shaped layer: 64 q / 8 kv heads, head_dim 128, block 16,
     context lengths round(LogNormal(ln median, sigma)) clipped to ``clip``."""
     rng = np.random.default_rng(seed)
@@ -250,13 +259,13 @@ def llama3_70b(seed: int = 2, num_seqs: int = 256, median: float = 1500.0,
     return _plain("llama3_70b" if num_seqs == 256 and clip == (64, 8192) else
                   f"llama3_70b_b{num_seqs}_clip{clip[0]}-{clip[1]}",
                   seed, dtype, lens, 64, 8, 128, 16, rng,
-                  partition_size=partition_size,
+                  partition_size=partition_size, manager=manager,
                   description=f"{num_seqs} seqs, L=clip(round(LogNormal(ln {median:g}, {sigma:g})), "
                               f"{clip[0]}, {clip[1]}), 64/8 heads, D 128, bs 16, {dtype}")
 
 
 def long_context(seed: int = 4, num_seqs: int = 8, context: int = 32768,
-                 partition_size: int = 512) -> Workload:
+                 partition_size: int = 512, manager=None) -> Workload:
     """Long-context split path: ``num_seqs`` x ``context`` tokens, 32 q / 8 kv
     heads, head_dim 128, block 16, bf16, partitions of 512 tokens."""
     rng = np.random.default_rng(seed)
@@ -264,13 +273,13 @@ def long_context(seed: int = 4, num_seqs: int = 8, context: int = 32768,
     return _plain("long_context" if (num_seqs, context) == (8, 32768) else
                   f"long_context_b{num_seqs}_l{context}",
                   seed, "bf16", lens, 32, 8, 128, 16, rng,
-                  partition_size=partition_size,
+                  partition_size=partition_size, manager=manager,
                   description=f"{num_seqs} x {context} tokens, 32/8 heads, D 128, bs 16, bf16, "
                               f"partition {partition_size}")
 
 
 def prefix_share(seed: int = 3, num_seqs: int = 100, prefix: int = 10000,
-                 suffix_max: int = 512) -> Workload:
+                 suffix_max: int = 512, manager=None) -> Workload:
     """Shared system prompt: ``num_seqs`` sequences fork one ``prefix``-token
     prompt, then each appends its own suffix of U{0..suffix_max} tokens.
     Writing into the partly filled shared page triggers copy-on-write.
@@ -286,12 +295,12 @@ def prefix_share(seed: int = 3, num_seqs: int = 100, prefix: int = 10000,
     need = shared + private
     num_blocks = int(math.ceil(1.1 * need))
     perm = rng.permutation(num_blocks)
-    mgr = BlockManager(num_blocks, bs, free_order=perm)
-    mgr.allocate("prompt", prefix)
-    prompt_pages = list(mgr.tables["prompt"])
+    mgr = _manager(manager, num_blocks, bs, perm)
+    mgr.allocate(PROMPT_SEQ, prefix)
+    prompt_pages = list(mgr.tables[PROMPT_SEQ])
     for b in range(num_seqs):
-        mgr.fork("prompt", b)
-    mgr.free_sequence("prompt")
+        mgr.fork(PROMPT_SEQ, b)
+    mgr.free_sequence(PROMPT_SEQ)
     resident = _resident_mask(num_blocks, bs, [prompt_pages], [prefix])
     slots, owner = [], []
     for b in range(num_seqs):
@@ -316,7 +325,8 @@ def prefix_share(seed: int = 3, num_seqs: int = 100, prefix: int = 10000,
     return w
 
 
-def beam_fork(seed: int = 3, beams: int = 8, prompt: int = 32768, shared_gen: int = 5) -> Workload:
+def beam_fork(seed: int = 3, beams: int = 8, prompt: int = 32768, shared_gen: int = 5,
+              manager=None) -> Workload:
     """Beam search over one long prompt: the prompt plus ``shared_gen``
     generated tokens are shared by ``beams`` beams; each beam then appends its
     own token, so every beam but the last holder copies the shared tail page.
@@ -328,7 +338,7 @@ def beam_fork(seed: int = 3, beams: int = 8, prompt: int = 32768, shared_gen: in
     need = shared + (beams - 1)
     num_blocks = int(math.ceil(1.1 * need))
     perm = rng.permutation(num_blocks)
-    mgr = BlockManager(num_blocks, bs, free_order=perm)
+    mgr = _manager(manager, num_blocks, bs, perm)
     mgr.allocate(0, prompt)
     for _ in range(shared_gen):
         mgr.append_token(0)
@@ -367,12 +377,12 @@ def copy_probe(beams: int = 8, prompt: int = 32768) -> np.ndarray:
 
 def custom(name: str, seed: int, dtype: str, lens, num_heads: int, num_kv_heads: int,
            head_dim: int, block_size: int, num_blocks: Optional[int] = None,
-           partition_size: int = 0) -> Workload:
+           partition_size: int = 0, manager=None) -> Workload:
     """Independent sequences with explicit context lengths (each >= 1)."""
     rng = np.random.default_rng(seed)
     return _plain(name, seed, dtype, np.asarray(lens), num_heads, num_kv_heads, head_dim,
                   block_size, rng, num_blocks=num_blocks, partition_size=partition_size,
-                  description=f"{len(lens)} seqs, {num_heads}/{num_kv_heads} heads, D {head_dim}, "
+                  manager=manager, description=f"{len(lens)} seqs, {num_heads}/{num_kv_heads} heads, D {head_dim}, "
                               f"bs {block_size}, {dtype}")
 
 
@@ -387,8 +397,8 @@ NAMED = {
 }
 
 
-def by_name(name: str) -> Workload:
-    return NAMED[name]()
+def by_name(name: str, manager=None) -> Workload:
+    return NAMED[name](manager=manager)
 
 
 # ---------------------------------------------------------------------------
