@@ -57,14 +57,15 @@ def _args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe", "copy_calib",
-                                                         "blockmgr"],
+                                                         "blockmgr", "capacity"],
                     help="copy_probe: time pa_copy_blocks on an eager fork of a 32,768-token "
                          "prompt to 7 beams (7,168 pages of 32 tokens, K and V); copy_calib: "
                          "the same number of page copies with 7,168 distinct sources (a plain "
                          "copy of known size, used to scale rocprofv3 traffic counters); "
                          "blockmgr: host time of one decode step's page bookkeeping (append "
                          "for every sequence + block tables), native manager vs the Python one "
-                         "(no GPU needed)")
+                         "(no GPU needed); capacity: KV waste and concurrent capacity, paged vs "
+                         "contiguous pre-allocation, measured with the native allocator (no GPU)")
     return ap.parse_args(argv)
 
 
@@ -238,6 +239,47 @@ def blockmgr_bench(a) -> int:
     return 0 if same else 1
 
 
+def capacity_bench(a) -> int:
+    """KV waste of every named workload and concurrent capacity of a whole
+    Llama-3-shaped model's KV on one MI355X, paged (native allocator) vs a
+    contiguous runtime that reserves each request's maximum length."""
+    from paged_kv_cache_350_amd import capacity as C
+    import workloads as W
+    reserve = {"tiny": 64, "llama3_8b": 4096, "llama3_70b": 8192, "prefix_share": 10512,
+               "beam_fork": 32774, "long_context": 32768}
+    usage = {}
+    for name in W.NAMED:
+        w = W.by_name(name)
+        if name == "prefix_share":
+            u = C.measure_usage(w.context_lens, w.block_size, reserve[name], prompt=10000)
+            flat = C.measure_usage(w.context_lens, w.block_size, reserve[name])
+        elif name == "beam_fork":
+            u = C.measure_usage(w.context_lens, w.block_size, reserve[name], prompt=32768 + 5)
+            flat = C.measure_usage(w.context_lens, w.block_size, reserve[name])
+        else:
+            u = flat = C.measure_usage(w.context_lens, w.block_size, reserve[name])
+        d = u.as_dict()
+        d["reserve_tokens"] = reserve[name]
+        if u is not flat:
+            d["sharing_saving_vs_unshared_paged"] = round(1 - u.paged_tokens / flat.paged_tokens, 4)
+            d["sharing_saving_vs_contiguous"] = round(1 - u.paged_tokens / u.contiguous_tokens, 4)
+        usage[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+    kv_budget = 250e9           # bytes of HBM given to the KV cache on a 288 GB MI355X
+    models = {"llama3_8b": (32, 4096), "llama3_70b": (80, 8192)}
+    cap = {}
+    for name, (layers, res) in models.items():
+        per_tok = C.kv_bytes_per_token(layers, 8, 128, 2)
+        tokens = int(kv_budget // per_tok)
+        paged = C.paged_capacity(tokens, 16, C.sample_lengths(name, 4096, seed=5))
+        contig = C.contiguous_capacity(tokens, res)
+        cap[name] = {"layers": layers, "kv_bytes_per_token": per_tok, "budget_tokens": tokens,
+                     "reserve_tokens": res, "paged_sequences": paged, "contiguous_sequences": contig,
+                     "ratio": round(paged / contig, 2)}
+    print(json.dumps({"mode": "capacity", "kv_budget_bytes": kv_budget, "usage": usage,
+                      "capacity": cap}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     a = _args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -249,6 +291,8 @@ def main(argv=None) -> int:
 
     if a.mode == "blockmgr":
         return blockmgr_bench(a)
+    if a.mode == "capacity":
+        return capacity_bench(a)
 
     import torch
     import paged_kv_cache_350_amd as pa
