@@ -57,7 +57,7 @@ def _args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe", "copy_calib",
-                                                         "blockmgr", "capacity"],
+                                                         "blockmgr", "capacity", "prefix"],
                     help="copy_probe: time pa_copy_blocks on an eager fork of a 32,768-token "
                          "prompt to 7 beams (7,168 pages of 32 tokens, K and V); copy_calib: "
                          "the same number of page copies with 7,168 distinct sources (a plain "
@@ -65,7 +65,12 @@ def _args(argv=None):
                          "blockmgr: host time of one decode step's page bookkeeping (append "
                          "for every sequence + block tables), native manager vs the Python one "
                          "(no GPU needed); capacity: KV waste and concurrent capacity, paged vs "
-                         "contiguous pre-allocation, measured with the native allocator (no GPU)")
+                         "contiguous pre-allocation, measured with the native allocator (no GPU); "
+                         "prefix: prefix caching on a multi-tenant request stream, native manager "
+                         "vs the oracle (no GPU)")
+    ap.add_argument("--requests", type=int, default=2000, help="prefix mode: requests in the stream")
+    ap.add_argument("--oracle-requests", type=int, default=400,
+                    help="prefix mode: leading requests the oracle replays (CPU baseline sample)")
     return ap.parse_args(argv)
 
 
@@ -280,6 +285,75 @@ def capacity_bench(a) -> int:
     return 0
 
 
+def prefix_bench(a) -> int:
+    """Prefix caching on a multi-tenant request stream: share of prompt
+    tokens whose K/V was already cached, pages held with and without
+    caching, and the native manager's host cost per admission next to the
+    oracle's on a bounded sample (with identical decisions)."""
+    import paged_kv_cache_350_amd as pa
+    from paged_kv_cache_350_amd import capacity as C
+    import workloads.requests as R
+    from oracle.prefix_cache import PrefixCachingPool
+    bs, live_max = 16, 100
+    reqs = R.tenant_requests(num_tenants=8, num_requests=a.requests, seed=7)
+    arrays = [np.asarray(t, dtype=np.int32) for _, t in reqs]   # token ids as a serving loop holds them
+    per_tok = C.kv_bytes_per_token(32, 8, 128, 2)              # Llama-3-8B-shaped KV
+    nb = int(250e9 // per_tok) // bs                           # 250 GB of HBM for KV
+
+    def run(mgr, prompt_api, limit, native=True):
+        """Admissions are timed without reading the pages back (a serving
+        loop reads them through the block tables); the oracle's decisions
+        and the native manager's are compared on the leading sample."""
+        live, cached_sum, prompt_sum, peak, t_adm, t_free = [], 0, 0, 0, 0.0, 0.0
+        decisions = []
+        for i, (_, toks) in enumerate(reqs[:limit]):
+            if len(live) == live_max:                          # the oldest request finishes
+                t0 = time.perf_counter()
+                mgr.free_sequence(live.pop(0))
+                t_free += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            if not native:
+                cached = mgr.allocate_prompt(i, toks)[1]
+            elif prompt_api:
+                cached = mgr.allocate_prompt(i, arrays[i], return_pages=False)
+            else:
+                mgr.allocate(i, len(toks), return_pages=False)
+                cached = 0
+            t_adm += time.perf_counter() - t0
+            if i < sample:
+                decisions.append((list(mgr.pages[i] if not native else mgr.pages(i)), cached))
+            live.append(i)
+            cached_sum += cached
+            prompt_sum += len(toks)
+            held = nb - (mgr.num_free() if callable(getattr(mgr, "num_free", None)) else len(mgr.free))
+            peak = max(peak, held)
+        n = max(limit, 1)
+        return {"cached_tokens": cached_sum, "prompt_tokens": prompt_sum, "peak_pages": peak,
+                "us_per_admission": t_adm / n * 1e6, "us_per_free": t_free / n * 1e6}, decisions
+
+    sample = min(a.oracle_requests, len(reqs))
+    nat, nat_dec = run(pa.NativeBlockManager(nb, bs), True, len(reqs))
+    flat, _ = run(pa.NativeBlockManager(nb, bs), False, len(reqs))
+    t0 = time.perf_counter()
+    orc, orc_dec = run(PrefixCachingPool(nb, bs), True, sample, native=False)
+    oracle_s = time.perf_counter() - t0
+    same = orc_dec == nat_dec[:sample]
+    print(json.dumps({
+        "mode": "prefix", "requests": len(reqs), "tenants": 8, "block_size": bs, "live_max": live_max,
+        "pool_pages": nb, "cached_token_fraction": round(nat["cached_tokens"] / nat["prompt_tokens"], 4),
+        "peak_pages_cached": nat["peak_pages"], "peak_pages_uncached": flat["peak_pages"],
+        "memory_saving": round(1 - nat["peak_pages"] / flat["peak_pages"], 4),
+        "prefill_kv_bytes_skipped": nat["cached_tokens"] * per_tok,
+        "native_us_per_admission": round(nat["us_per_admission"], 2),
+        "native_us_per_free": round(nat["us_per_free"], 2),
+        "uncached_native_us_per_admission": round(flat["us_per_admission"], 2),
+        "identical_decisions_on_sample": same,
+        "cpu_baseline": {"value": round(orc["us_per_admission"], 2), "unit": "us/admission", "cores": 1,
+                         "kind": "oracle", "sample": f"first {sample} requests of the stream",
+                         "seconds": round(oracle_s, 2)}}), flush=True)
+    return 0 if same else 1
+
+
 def main(argv=None) -> int:
     a = _args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,6 +367,8 @@ def main(argv=None) -> int:
         return blockmgr_bench(a)
     if a.mode == "capacity":
         return capacity_bench(a)
+    if a.mode == "prefix":
+        return prefix_bench(a)
 
     import torch
     import paged_kv_cache_350_amd as pa

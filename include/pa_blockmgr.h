@@ -24,6 +24,14 @@
  *     for pa_copy_blocks (copy-on-write); the last holder writes in place;
  *   - running out of pages is an error status, never a partial result.
  *
+ * Prefix caching [Paged Attention (AI terminology), "Key Points" (sharing
+ * row) and "Common Usage Examples"; PagedAttention Internals, "Copy-on-Write and Prefix
+ * Sharing" and "Architectural Recommendations" item 2]: prompts allocated
+ * with pa_bm_allocate_prompt share every leading full page whose whole token
+ * prefix an earlier prompt already stored, so the caller writes K/V only for
+ * the tokens after the cached prefix.  Cached pages stay reusable after their
+ * last holder frees them, until the free list hands them out again.
+ *
  * Host memory only: the manager owns its state (allocated at create and as
  * sequences are added) and touches no device memory.  One manager must not
  * be used from two threads at once.  Sequence ids are caller-chosen int64.
@@ -84,6 +92,41 @@ int64_t pa_bm_free_list(const pa_block_manager* bm, int64_t cap, int32_t* pages)
  * pool has fewer free pages (nothing is taken).
  */
 pa_status pa_bm_allocate(pa_block_manager* bm, int64_t seq_id, int64_t num_tokens);
+
+/*
+ * New sequence seq_id for a prompt of num_tokens (>= 0) token ids (host
+ * int32 array `tokens`; NULL allowed when num_tokens is 0).
+ *
+ * Page k (k < num_tokens / block_size, i.e. a full page) is identified by
+ * tokens[0 .. (k + 1) * block_size): the K/V it holds depends on that whole
+ * prefix.  The leading run of full pages whose prefixes are cached is shared
+ * (reference counts raised; a cached page on the free list is taken back off
+ * it).  The remaining ceil(num_tokens / block_size) - hits pages come from
+ * the front of the free list, and each of them that is full is registered
+ * under its prefix (replacing an older page registered under the same
+ * prefix).  *num_cached_tokens receives hits * block_size: the tokens whose
+ * K/V is already in place; the caller writes tokens num_cached_tokens ..
+ * num_tokens - 1 (pa_kv_append) before any kernel reads them, and a prompt
+ * that hits pages registered by an earlier call in the same step reads them
+ * only after that call's writes.
+ *
+ * Identity is a 128-bit hash of the prefix: two different prefixes share a
+ * page only on a 128-bit collision.  A cached page is evicted (its entry
+ * dropped) when the free list hands it out for any allocation.
+ *
+ * PA_ERR_NULL (num_cached_tokens NULL, or tokens NULL with num_tokens > 0),
+ * PA_ERR_ARG (seq_id exists, num_tokens < 0), PA_ERR_OUT_OF_PAGES (fewer free
+ * pages than the fresh pages plus the cached free pages it takes back);
+ * every error changes no state.
+ */
+pa_status pa_bm_allocate_prompt(pa_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                                int64_t num_tokens, int64_t* num_cached_tokens);
+
+/* Pages registered in the prefix cache (held or free); -1 for a NULL manager. */
+int64_t pa_bm_num_cached(const pa_block_manager* bm);
+
+/* 1 if the page is registered in the prefix cache, 0 if not, -1 outside the pool. */
+int32_t pa_bm_page_cached(const pa_block_manager* bm, int64_t page);
 
 /*
  * New sequence child_id sharing every page of parent_id (reference counts

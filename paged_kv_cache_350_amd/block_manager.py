@@ -27,6 +27,9 @@ _SIGNATURES = {
     "pa_bm_ref_count": ([_vp, _i64], _i32),
     "pa_bm_free_list": ([_vp, _i64, _vp], _i64),
     "pa_bm_allocate": ([_vp, _i64, _i64], _i32),
+    "pa_bm_allocate_prompt": ([_vp, _i64, _vp, _i64, ctypes.POINTER(_i64)], _i32),
+    "pa_bm_num_cached": ([_vp], _i64),
+    "pa_bm_page_cached": ([_vp, _i64], _i32),
     "pa_bm_fork": ([_vp, _i64, _i64], _i32),
     "pa_bm_free": ([_vp, _i64], _i32),
     "pa_bm_append": ([_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp], _i32),
@@ -156,12 +159,36 @@ class NativeBlockManager:
         return out[:n].tolist()
 
     # -- updates ---------------------------------------------------------
-    def allocate(self, seq: int, num_tokens: int) -> List[int]:
+    def allocate(self, seq: int, num_tokens: int, return_pages: bool = True) -> Optional[List[int]]:
         st = _lib().pa_bm_allocate(self._h, int(seq), int(num_tokens))
         if st == -2:
             raise ValueError(f"sequence {seq} exists or num_tokens < 0")
         _check("pa_bm_allocate", st)
-        return self.pages(seq)
+        return self.pages(seq) if return_pages else None
+
+    def allocate_prompt(self, seq: int, tokens: Sequence[int], return_pages: bool = True):
+        """New sequence for a prompt of token ids, sharing every leading full
+        page an earlier prompt with the same prefix stored.  Returns (pages,
+        number of leading tokens whose K/V is already cached); with
+        return_pages=False only the count (the pages stay readable through
+        pages() and block_tables())."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        cached = _i64(0)
+        st = _lib().pa_bm_allocate_prompt(self._h, int(seq), _ptr(toks) if toks.size else None,
+                                          int(toks.size), ctypes.byref(cached))
+        if st == -2:
+            raise ValueError(f"sequence {seq} exists")
+        _check("pa_bm_allocate_prompt", st)
+        if not return_pages:
+            return int(cached.value)
+        return self.pages(seq), int(cached.value)
+
+    def num_cached(self) -> int:
+        """Pages registered in the prefix cache (held or free)."""
+        return int(_lib().pa_bm_num_cached(self._h))
+
+    def is_cached(self, page: int) -> bool:
+        return int(_lib().pa_bm_page_cached(self._h, int(page))) == 1
 
     def fork(self, parent: int, child: int) -> None:
         st = _lib().pa_bm_fork(self._h, int(parent), int(child))

@@ -6,15 +6,29 @@
 // PagedAttention Works" item 2, "Copy-on-Write and Prefix Sharing",
 // "Implementation: Custom Block Manager Simulation"]
 //
-// The free list is a ring buffer of capacity num_blocks (every page is
-// either in it or held by a sequence), so taking and returning pages never
-// allocates.  A batch append is first dry-run to count the pages it needs --
+// The free list is intrusive: doubly linked through two per-page arrays
+// (every page is either in it or held by a sequence), so taking a page from
+// the front, returning one to the back and pulling a cached page out of the
+// middle are O(1) and never allocate.  A batch append is first dry-run to count the pages it needs --
 // one per token that opens a block, one per copy-on-write -- so that running
 // out of pages leaves the state untouched; the dry run's scratch lives in the
 // sequences (tagged with a per-call epoch) and in per-page arrays kept
 // between calls, so a decode step costs one hash lookup per sequence.
+//
+// Prefix caching [Paged Attention (AI terminology), "Key Points" (sharing
+// row) and "Common Usage Examples" (prefix caching); PagedAttention Internals,
+// "Copy-on-Write and Prefix Sharing" and "Architectural Recommendations"
+// item 2]: a full page of a prompt is identified by the whole token prefix
+// up to its end, since a page's K/V depends on every earlier token.  The
+// identity is a 128-bit chained hash (per page, a position-salted sum of
+// mixed token pairs; chained across pages through two different 64-bit
+// finalizers); a lookup maps the low word to a page and checks the high
+// word.  A cached page stays cached while it is held and after it returns
+// to the free list; it is evicted when the free list hands it out again, so
+// the least recently released cached page goes first.
 #include <stdint.h>
 
+#include <memory>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -24,8 +38,9 @@
 struct pa_block_manager {
     int64_t num_blocks = 0;
     int32_t block_size = 0;
-    std::vector<int32_t> ring;     // free list: ring[(head + i) % num_blocks], i < nfree
-    int64_t head = 0;
+    // free list: head -> nxt -> ... -> tail, -1 terminated both ways
+    std::vector<int32_t> nxt, prv;
+    int32_t head = -1, tail = -1;
     int64_t nfree = 0;
     std::vector<int32_t> ref;      // reference count per page
     struct Seq {
@@ -43,24 +58,131 @@ struct pa_block_manager {
     std::vector<int32_t> dropped;          // per page: references the dry run dropped
     std::vector<int32_t> touched;          // pages with a non-zero `dropped` entry
     std::vector<Seq*> batch;               // sequence of each token of the batch
+    // prefix cache: per page its prefix key and whether it is registered
+    std::vector<uint64_t> key_lo, key_hi;
+    std::vector<uint8_t> cached;
+    // key_lo -> page: open addressing with linear probing, at most half
+    // full (one entry per cached page); built on first prompt use
+    struct Slot {
+        uint64_t lo;
+        int32_t page;                      // -1: empty
+    };
+    std::vector<Slot> table;
+    uint64_t mask = 0;
+    std::vector<int32_t> next_hint;        // per cached page: the page last found after it
+    int64_t num_cached = 0;
+    std::vector<int32_t> hits;             // allocate_prompt scratch
+
+    void unlink(int32_t page) {
+        const int32_t a = prv[(size_t)page], b = nxt[(size_t)page];
+        if (a >= 0) nxt[(size_t)a] = b; else head = b;
+        if (b >= 0) prv[(size_t)b] = a; else tail = a;
+        --nfree;
+    }
+
+    // Slot holding lo, or -1.
+    int64_t find_slot(uint64_t lo) const {
+        for (uint64_t i = lo & mask;; i = (i + 1) & mask) {
+            if (table[(size_t)i].page < 0) return -1;
+            if (table[(size_t)i].lo == lo) return (int64_t)i;
+        }
+    }
+
+    // Empty slot i and shift later entries of its probe run back into the
+    // hole, so no tombstones build up (deletion for linear probing, Knuth,
+    // TAOCP vol. 3, section 6.4, Algorithm R).
+    void erase_slot(uint64_t i) {
+        for (uint64_t j = i;;) {
+            j = (j + 1) & mask;
+            if (table[(size_t)j].page < 0) break;
+            const uint64_t home = table[(size_t)j].lo & mask;
+            // move j back into i unless its home lies cyclically in (i, j]
+            const bool stays = i <= j ? (i < home && home <= j) : (i < home || home <= j);
+            if (!stays) {
+                table[(size_t)i] = table[(size_t)j];
+                i = j;
+            }
+        }
+        table[(size_t)i].page = -1;
+    }
+
+    void uncache(int32_t page) {
+        if (!cached[(size_t)page]) return;
+        const int64_t at = find_slot(key_lo[(size_t)page]);
+        if (at >= 0 && table[(size_t)at].page == page) erase_slot((uint64_t)at);
+        cached[(size_t)page] = 0;
+        --num_cached;
+    }
 
     int32_t take() {               // caller checked nfree > 0
-        const int32_t page = ring[(size_t)head];
-        head = head + 1 == num_blocks ? 0 : head + 1;
-        --nfree;
+        const int32_t page = head;
+        unlink(page);
+        if (num_cached) uncache(page);   // handed out again: its old content goes
         ref[(size_t)page] = 1;
         return page;
     }
 
     void give_back(int32_t page) {
-        int64_t tail = head + nfree;
-        if (tail >= num_blocks) tail -= num_blocks;
-        ring[(size_t)tail] = page;
+        prv[(size_t)page] = tail;
+        nxt[(size_t)page] = -1;
+        if (tail >= 0) nxt[(size_t)tail] = page; else head = page;
+        tail = page;
         ++nfree;
     }
 
     void release(int32_t page) {
         if (--ref[(size_t)page] == 0) give_back(page);
+    }
+
+    // Page registered under (lo, hi), or -1.  `after` is the page holding
+    // the prefix one page shorter (-1 at the start): its hint is tried
+    // before the table, since a repeated prompt walks the same chain.
+    int32_t lookup(uint64_t lo, uint64_t hi, int32_t after) const {
+        if (after >= 0) {
+            const int32_t h = next_hint[(size_t)after];
+            if (h >= 0 && cached[(size_t)h] && key_lo[(size_t)h] == lo && key_hi[(size_t)h] == hi)
+                return h;
+        }
+        const int64_t at = find_slot(lo);
+        if (at < 0) return -1;
+        const int32_t page = table[(size_t)at].page;
+        return key_hi[(size_t)page] == hi ? page : -1;
+    }
+
+    // Register page under (lo, hi), replacing the page that held lo.  The
+    // table has a slot for every page, so this never allocates.
+    void enroll(int32_t page, uint64_t lo, uint64_t hi) {
+        uint64_t i = lo & mask;
+        while (table[(size_t)i].page >= 0 && table[(size_t)i].lo != lo) i = (i + 1) & mask;
+        Slot& e = table[(size_t)i];
+        if (e.page >= 0) {
+            cached[(size_t)e.page] = 0;
+            --num_cached;
+        }
+        e.lo = lo;
+        e.page = page;
+        key_lo[(size_t)page] = lo;
+        key_hi[(size_t)page] = hi;
+        cached[(size_t)page] = 1;
+        ++num_cached;
+    }
+
+    // Build the per-page prefix-cache arrays on first use (may throw
+    // bad_alloc; nothing else changes then).
+    void ensure_cache() {
+        if (!table.empty()) return;
+        uint64_t cap = 2;
+        while (cap < 2 * (uint64_t)num_blocks) cap <<= 1;
+        std::vector<Slot> t((size_t)cap, Slot{0, -1});
+        std::vector<uint64_t> lo((size_t)num_blocks, 0), hi((size_t)num_blocks, 0);
+        std::vector<uint8_t> c((size_t)num_blocks, 0);
+        std::vector<int32_t> nh((size_t)num_blocks, -1);
+        table.swap(t);
+        key_lo.swap(lo);
+        key_hi.swap(hi);
+        cached.swap(c);
+        next_hint.swap(nh);
+        mask = cap - 1;
     }
 };
 
@@ -79,6 +201,43 @@ pa_status guarded(F&& f) {
 
 int64_t blocks_for(int64_t tokens, int32_t bs) { return (tokens + bs - 1) / bs; }
 
+// splitmix64 output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014).
+inline uint64_t mix_a(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+// MurmurHash3's 64-bit finalizer (Appleby, MurmurHash3, fmix64).
+inline uint64_t mix_b(uint64_t z) {
+    z = (z ^ (z >> 33)) * 0xff51afd7ed558ccdull;
+    z = (z ^ (z >> 33)) * 0xc4ceb9fe1a85ec53ull;
+    return z ^ (z >> 33);
+}
+
+// Key of the prefix that ends with `page` (bs tokens), given the key of the
+// prefix before it.  Tokens are taken two at a time as one 64-bit word, and
+// word j is salted with its position, so the per-page sums are
+// order-sensitive; the chain makes the key depend on every earlier page.
+inline void chain_key(uint64_t& lo, uint64_t& hi, const int32_t* page, int32_t bs) {
+    uint64_t a = 0, b = 0;
+    int32_t i = 0;
+    uint64_t j = 1;
+    for (; i + 1 < bs; i += 2, ++j) {
+        const uint64_t w = (uint64_t)(uint32_t)page[i] | ((uint64_t)(uint32_t)page[i + 1] << 32);
+        a += mix_a(w + 0x9e3779b97f4a7c15ull * j);
+        b += mix_b(w ^ (0xd6e8feb86659fd93ull * j));
+    }
+    if (i < bs) {                                    // odd block size: last token alone
+        const uint64_t w = (uint64_t)(uint32_t)page[i] | (0xffffffffull << 32);
+        a += mix_a(w + 0x9e3779b97f4a7c15ull * j);
+        b += mix_b(w ^ (0xd6e8feb86659fd93ull * j));
+    }
+    lo = mix_a(lo ^ a);
+    hi = mix_b(hi + b);
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,25 +251,22 @@ pa_status pa_bm_create(int64_t num_blocks, int32_t block_size, const int64_t* fr
         pa_block_manager* bm = new pa_block_manager();
         bm->num_blocks = num_blocks;
         bm->block_size = block_size;
-        bm->ring.resize((size_t)num_blocks);
-        bm->ref.assign((size_t)num_blocks, 0);
-        bm->dropped.assign((size_t)num_blocks, 0);
-        if (free_order) {
-            std::vector<char> seen((size_t)num_blocks, 0);
-            for (int64_t i = 0; i < num_blocks; ++i) {
-                const int64_t p = free_order[i];
-                if (p < 0 || p >= num_blocks || seen[(size_t)p]) {
-                    delete bm;
-                    return PA_ERR_ARG;
-                }
+        std::unique_ptr<pa_block_manager> hold(bm);
+        const size_t nb = (size_t)num_blocks;
+        bm->nxt.assign(nb, -1);
+        bm->prv.assign(nb, -1);
+        bm->ref.assign(nb, 0);
+        bm->dropped.assign(nb, 0);
+        std::vector<char> seen(free_order ? nb : 0, 0);
+        for (int64_t i = 0; i < num_blocks; ++i) {
+            const int64_t p = free_order ? free_order[i] : i;
+            if (free_order) {
+                if (p < 0 || p >= num_blocks || seen[(size_t)p]) return PA_ERR_ARG;
                 seen[(size_t)p] = 1;
-                bm->ring[(size_t)i] = (int32_t)p;
             }
-        } else {
-            for (int64_t i = 0; i < num_blocks; ++i) bm->ring[(size_t)i] = (int32_t)i;
+            bm->give_back((int32_t)p);
         }
-        bm->nfree = num_blocks;
-        *out = bm;
+        *out = hold.release();
         return PA_OK;
     });
 }
@@ -145,11 +301,8 @@ int32_t pa_bm_ref_count(const pa_block_manager* bm, int64_t page) {
 int64_t pa_bm_free_list(const pa_block_manager* bm, int64_t cap, int32_t* pages) {
     if (!bm) return -1;
     if (pages) {
-        for (int64_t i = 0; i < bm->nfree && i < cap; ++i) {
-            int64_t at = bm->head + i;
-            if (at >= bm->num_blocks) at -= bm->num_blocks;
-            pages[i] = bm->ring[(size_t)at];
-        }
+        int32_t p = bm->head;
+        for (int64_t i = 0; p >= 0 && i < cap; ++i, p = bm->nxt[(size_t)p]) pages[i] = p;
     }
     return bm->nfree;
 }
@@ -169,6 +322,69 @@ pa_status pa_bm_allocate(pa_block_manager* bm, int64_t seq_id, int64_t num_token
         for (int64_t i = 0; i < need; ++i) pages.push_back(bm->take());
         return PA_OK;
     });
+}
+
+pa_status pa_bm_allocate_prompt(pa_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                                int64_t num_tokens, int64_t* num_cached_tokens) {
+    if (!bm) return PA_ERR_NULL;
+    if (num_cached_tokens) *num_cached_tokens = 0;
+    if (num_tokens < 0) return PA_ERR_ARG;
+    if (!num_cached_tokens || (num_tokens > 0 && !tokens)) return PA_ERR_NULL;
+    if (bm->seqs.count(seq_id)) return PA_ERR_ARG;
+    const int32_t bs = bm->block_size;
+    const int64_t total = blocks_for(num_tokens, bs);
+    const int64_t full = num_tokens / bs;
+    return guarded([&]() -> pa_status {
+        bm->ensure_cache();
+        // Walk the full pages while their prefixes are cached: those pages
+        // are shared (a free one is pulled back off the free list).
+        bm->hits.clear();
+        bm->hits.reserve((size_t)full);
+        uint64_t lo = 0x243f6a8885a308d3ull, hi = 0x13198a2e03707344ull;
+        int64_t revive = 0;
+        int64_t k = 0;
+        int32_t prev = -1;
+        for (; k < full; ++k) {
+            uint64_t nlo = lo, nhi = hi;
+            chain_key(nlo, nhi, tokens + k * bs, bs);
+            const int32_t page = bm->lookup(nlo, nhi, prev);
+            if (page < 0) break;
+            bm->hits.push_back(page);
+            prev = page;
+            revive += bm->ref[(size_t)page] == 0;
+            lo = nlo;
+            hi = nhi;
+        }
+        if (revive + (total - k) > bm->nfree) return PA_ERR_OUT_OF_PAGES;
+        pa_block_manager::Seq s;
+        s.pages.reserve((size_t)total);
+        s.len = num_tokens;
+        auto ins = bm->seqs.emplace(seq_id, std::move(s));     // may throw: nothing changed yet
+        std::vector<int32_t>& pages = ins.first->second.pages;
+        for (int32_t page : bm->hits) {
+            if (bm->ref[(size_t)page]++ == 0) bm->unlink(page);
+            pages.push_back(page);
+        }
+        for (int64_t j = k; j < total; ++j) {
+            const int32_t page = bm->take();
+            pages.push_back(page);
+            if (j < full) {                 // a full page: register its prefix
+                chain_key(lo, hi, tokens + j * bs, bs);
+                bm->enroll(page, lo, hi);
+            }
+        }
+        for (int64_t j = 1; j < full; ++j)  // hints along the chain just walked
+            bm->next_hint[(size_t)pages[(size_t)j - 1]] = pages[(size_t)j];
+        *num_cached_tokens = k * bs;
+        return PA_OK;
+    });
+}
+
+int64_t pa_bm_num_cached(const pa_block_manager* bm) { return bm ? bm->num_cached : -1; }
+
+int32_t pa_bm_page_cached(const pa_block_manager* bm, int64_t page) {
+    if (!bm || page < 0 || page >= bm->num_blocks) return -1;
+    return bm->cached.empty() ? 0 : bm->cached[(size_t)page];
 }
 
 pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id) {
