@@ -22,3 +22,4 @@ from .paged_attention import decode, gather_sequence, resolve_slot  # noqa: F401
 from .cache_ops import copy_blocks, kv_append  # noqa: F401
 from .streaming import online_decode_sequence, split_decode_sequence  # noqa: F401
 from .prefix_cache import PrefixCachingPool  # noqa: F401
+from .multi_query import decode_multi  # noqa: F401
