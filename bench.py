@@ -57,7 +57,7 @@ def _args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe", "copy_calib",
-                                                         "blockmgr", "capacity", "prefix"],
+                                                         "blockmgr", "capacity", "prefix", "multi"],
                     help="copy_probe: time pa_copy_blocks on an eager fork of a 32,768-token "
                          "prompt to 7 beams (7,168 pages of 32 tokens, K and V); copy_calib: "
                          "the same number of page copies with 7,168 distinct sources (a plain "
@@ -67,7 +67,8 @@ def _args(argv=None):
                          "(no GPU needed); capacity: KV waste and concurrent capacity, paged vs "
                          "contiguous pre-allocation, measured with the native allocator (no GPU); "
                          "prefix: prefix caching on a multi-tenant request stream, native manager "
-                         "vs the oracle (no GPU)")
+                         "vs the oracle (no GPU); multi: multi-query attention on the "
+                         "speculative-verification batch (5 queries per sequence)")
     ap.add_argument("--requests", type=int, default=2000, help="prefix mode: requests in the stream")
     ap.add_argument("--oracle-requests", type=int, default=400,
                     help="prefix mode: leading requests the oracle replays (CPU baseline sample)")
@@ -354,6 +355,98 @@ def prefix_bench(a) -> int:
     return 0 if same else 1
 
 
+def multi_bench(a, torch, pa, W) -> int:
+    """Multi-query step on the speculative-verification batch: append every
+    sequence's new tokens (pa_kv_append), then pa_decode_multi (partition and
+    merge kernels).  The roofline figure uses the whole pa_decode_multi call
+    (both kernels) as the launch; the rocprofv3 summary splits the two."""
+    import oracle
+    w = W.spec_verify()
+    t = W.make_tensors(w, "cuda")
+    reuse = a.reuse if a.reuse != "auto" else "stream"
+    ps_req = 0 if a.partition_size is None else a.partition_size
+    P = pa.decode_multi_partition_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.max_context_len,
+                                       w.max_query_len, ps_req)
+    T = int(w.query_lens.sum())
+    nws = pa.decode_multi_workspace_size(w.num_seqs, T, w.num_heads, w.num_kv_heads, w.head_dim,
+                                         w.max_context_len, w.max_query_len, P)
+    ws = torch.empty(max(nws // 4, 1), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(t["q"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+        if ev is not None:
+            ev[1].record(stream)
+        pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                        t["query_start"], w.scale, w.max_context_len, w.max_query_len, out=out,
+                        partition_size=P if P > 0 else -1, workspace=ws, reuse=reuse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done, timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nbd = min(a.steps, 100)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nbd)]
+    for k in range(nbd):
+        step(events[k])
+    torch.cuda.synchronize()
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    multi_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    kv_bytes = w.algorithmic_kv_bytes()       # every context token once per kv head (one column group)
+    ms_per_step = wall * 1e3 / a.steps
+    achieved = kv_bytes / (multi_ms * 1e-3) / 1e9
+    digest = _src_digest("decode_multi.hip", "decode_reduce.hip", "pa_device.h", "pa_internal.h")
+
+    # CPU baseline: the oracle on whole sequences, about cpu_seconds of work
+    kc0, vc0, q = _host(t["k_cache"]), _host(t["v_cache"]), _host(t["q"])
+    done = nbytes = 0
+    elapsed = 0.0
+    for b in range(w.num_seqs):
+        t1 = time.perf_counter()
+        oracle.decode_multi(q, kc0, vc0, w.block_tables, w.context_lens, w.query_start, w.scale,
+                            w.block_size, w.dtype, seqs=[b])
+        elapsed += time.perf_counter() - t1
+        done += 1
+        nbytes += int(w.context_lens[b]) * w.kv_bytes_per_token()
+        if elapsed >= a.cpu_seconds:
+            break
+    rec = {
+        "metric": "multi-query paged attention KV GB/s read (speculative verification)",
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "verified_tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "config": {"workload": w.name, "description": w.description, "num_seqs": w.num_seqs,
+                   "query_tokens": T, "max_query_len": w.max_query_len,
+                   "sum_context_tokens": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
+                   "partition_size": P, "reuse": reuse, "kv_bytes_per_step": kv_bytes},
+        "kernels_avg_us": {"kv_append": round(append_ms * 1e3, 2),
+                           "decode_multi_total": round(multi_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode_multi partition + merge", "avg_launch_us": round(multi_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": kv_bytes, "source_digest": digest},
+        "cpu_baseline": {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"{done} whole sequences of the {w.name} batch, float64 numpy oracle, "
+                                   f"{elapsed:.1f} s of CPU time"},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     a = _args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -381,6 +474,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     if a.mode in ("copy_probe", "copy_calib"):
         return copy_probe(a, torch, pa, W)
+    if a.mode == "multi":
+        return multi_bench(a, torch, pa, W)
     w = W.by_name(a.workload)
     ps_req = w.partition_size if a.partition_size is None else a.partition_size
     t = W.make_tensors(w, "cuda")

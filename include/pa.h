@@ -292,6 +292,57 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                          int32_t block_size, int64_t num_blocks, pa_dtype dtype,
                          hipStream_t stream);
 
+/*
+ * pa_decode_multi -- attention for several new tokens per sequence at once:
+ * the draft tokens speculative decoding verifies over paged memory
+ * [Internals, "The Mathematical Cause of KV Cache Fragmentation", closing
+ * link], or a chunk of a prompt, with the paging and attention of
+ * [Internals, "How PagedAttention Works" items 1-3].
+ *
+ * Sequence b has n_b = query_start[b + 1] - query_start[b] new tokens whose
+ * K and V rows are already in its pages (pa_kv_append, or pa_copy_blocks
+ * and pa_kv_append) at positions L_b - n_b .. L_b - 1, L_b = context_lens[b]
+ * counting them.  Row query_start[b] + j of q holds the queries of new token
+ * j (0 <= j < n_b); it attends, head by head as in pa_decode, over positions
+ * 0 .. L_b - n_b + j (causal among the new tokens), and the result goes to
+ * the same row of out.
+ *
+ *   q, out       device, [num_tokens][num_heads][head_dim] bf16, 16-byte aligned
+ *   query_start  device, [num_seqs + 1] int32, non-decreasing, query_start[0] = 0,
+ *                query_start[num_seqs] <= num_tokens; read
+ *   k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+ *   scale, num_heads, head_dim, max_blocks_per_seq, max_context_len,
+ *   num_blocks, partition_size, reuse, workspace  as for pa_decode
+ *   max_query_len  host bound on every n_b, 1 .. 1024
+ *   workspace      pa_decode_multi_workspace_size() bytes when the split
+ *                  path runs (else ignored); caller-owned
+ *
+ * Out-of-range device values are clamped (rows to [0, num_tokens), n_b to
+ * max_query_len and to L_b); rows no sequence covers are not part of the
+ * result (unspecified).  bf16 only: PA_ERR_UNSUPPORTED for fp32.  Returns
+ * PA_OK (num_seqs == 0 or num_tokens == 0 is a no-op), PA_ERR_NULL,
+ * PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE or PA_ERR_HIP.
+ */
+pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                          float scale, void* out, hipStream_t stream, int32_t num_seqs,
+                          int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
+                          int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                          pa_kv_reuse reuse, void* workspace, size_t workspace_bytes);
+
+/* Partition size pa_decode_multi uses for these sizes (0 = single pass,
+ * -1 = invalid request); partition_size as for pa_decode. */
+int32_t pa_decode_multi_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t max_query_len,
+                                       int32_t partition_size);
+
+/* Workspace bytes pa_decode_multi needs (0 when it runs in one pass). */
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                                      int32_t max_query_len, int32_t partition_size);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,12 @@ _SIGNATURES = {
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
     "pa_probe_stream_read": ([_vp, _c_size, _c_int, _c_int, _vp, _vp], _c_int),
+    "pa_decode_multi": ([_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_float, _vp, _vp,
+                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                         _c_int, _c_int, _vp, _c_size], _c_int),
+    "pa_decode_multi_partition_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_int),
+    "pa_decode_multi_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
+                                       _c_size),
 }
 
 
@@ -301,6 +307,58 @@ def decode_reduce(workspace: torch.Tensor, context_lens: torch.Tensor, out: torc
                                 out.data_ptr(), _stream(out), B, hq, d, int(max_context_len),
                                 int(partition_size), _elem_dtype(out))
     _check("pa_decode_reduce", st)
+    return out
+
+
+def decode_multi_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, max_context_len: int,
+                                max_query_len: int, partition_size: int = 0) -> int:
+    return lib().pa_decode_multi_partition_size(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                                max_query_len, partition_size)
+
+
+def decode_multi_workspace_size(num_seqs: int, num_tokens: int, num_heads: int, num_kv_heads: int,
+                                head_dim: int, max_context_len: int, max_query_len: int,
+                                partition_size: int = 0) -> int:
+    return lib().pa_decode_multi_workspace_size(num_seqs, num_tokens, num_heads, num_kv_heads, head_dim,
+                                                max_context_len, max_query_len, partition_size)
+
+
+def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+                 scale: float, max_context_len: int, max_query_len: int,
+                 out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                 workspace: Optional[torch.Tensor] = None, reuse: str = "auto") -> torch.Tensor:
+    """Attention for several new tokens per sequence (already appended):
+    q [T, Hq, D] packed by sequence, query_start [B + 1] int32; row
+    query_start[b] + j attends causally over positions 0 .. L_b - n_b + j.
+    Returns out [T, Hq, D]."""
+    nb, hkv, d, bs = _cache_dims(k_cache, v_cache)
+    _dev_tensor("q", q, dtype=k_cache.dtype, ndim=3)
+    _dev_tensor("block_tables", block_tables, dtype=torch.int32, ndim=2)
+    _dev_tensor("context_lens", context_lens, dtype=torch.int32, ndim=1)
+    _dev_tensor("query_start", query_start, dtype=torch.int32, ndim=1)
+    T, hq, dq = q.shape
+    B = context_lens.shape[0]
+    if dq != d:
+        raise ValueError(f"q head_dim {dq} != cache head_dim {d}")
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables / query_start disagree with context_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dtype=q.dtype, ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if workspace is None:
+        n = decode_multi_workspace_size(B, T, hq, hkv, d, max_context_len, max_query_len, partition_size)
+        workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device) if n else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().pa_decode_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
+                               bs, hkv, float(scale), out.data_ptr(), _stream(q), B, T, hq, d,
+                               block_tables.shape[1], int(max_context_len), int(max_query_len), nb,
+                               _elem_dtype(q), int(partition_size), REUSE[reuse], ws_ptr, ws_bytes)
+    _check("pa_decode_multi", st)
     return out
 
 

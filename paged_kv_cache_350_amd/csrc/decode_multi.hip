@@ -1,0 +1,327 @@
+// Multi-query paged attention on the MFMA matrix cores (bf16 caches, gfx950).
+//
+// Sequence b brings n new tokens whose K/V rows are already in its pages (at
+// positions L - n .. L - 1); the query of new token j attends over positions
+// 0 .. L - n + j through the block table.  This is what verifying draft
+// tokens of speculative decoding over paged memory needs [PagedAttention
+// Internals, "The Mathematical Cause of KV Cache Fragmentation", closing
+// link], with the paging and attention of "How PagedAttention Works" items
+// 1-3; a chunk of a prompt is the same computation.
+//
+// Same structure as the decode kernel, with the B operand of both products
+// widened from "the G query heads of a kv head" to (new token, head) pairs:
+// column c of a kv head's group is query token c / G, head c % G.  All
+// columns share every K and V row they see, so one K/V read serves up to
+// 16 * NT columns (NT = 1 or 2 tiles of 16): with G = 4, eight draft tokens
+// fill two tiles, where a decode step pads 4 heads to 16.  Column groups
+// beyond 16 * NT columns are separate workgroups.
+//
+// Work unit, loads, lazy rescaling and the wave merge are those of the
+// decode kernel's streaming path (split halves, raw buffer loads); only the
+// score mask differs: column c keeps token positions <= L - n + c / G, so
+// only the chunks that reach into the new tokens are masked per column.  A
+// column that has seen no visible position yet keeps a running max of -inf;
+// its weights are taken relative to 0 instead, which makes them 0, and its
+// rescale factor is 0 when a neighbouring column moves the tile's maxima.
+//
+// Partitions end at the last position any column of the group sees, so no
+// workgroup reads K/V that none of its queries attends to.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa_impl {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
+constexpr int kHalf = 16;             // tokens per row tile
+constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
+constexpr int kSegPages = 256;        // page ids staged in LDS at a time
+
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
+template <int POLICY>
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, POLICY);
+}
+
+// Chunk-relative token of score slot 4 t + i held by lane group j (row tile
+// t is the 16-token half t of the chunk).
+__device__ __forceinline__ int slot_token(int t, int i, int j) { return kHalf * t + 4 * j + i; }
+
+template <int D, int BS, int NT, int POLICY>
+__global__ __launch_bounds__(kThreads)
+void decode_multi_kernel(DecodeParams p) {
+    constexpr int KSTEPS = D / 32;   // Q.K^T k-steps
+    constexpr int DC = D / 16;       // 16-dim output tiles of P.V
+    constexpr int COLS = 16 * NT;    // (query token, head) columns per workgroup
+    constexpr uint32_t kTileBytes = (uint32_t)D * BS * 2;
+    static_assert(BS == 16 || BS == 32, "block size");
+
+    extern __shared__ float smem[];
+    float* sm_m = smem;                          // [kWaves][16]
+    float* sm_l = sm_m + kWaves * 16;            // [kWaves][16]
+    float* sacc = sm_l + kWaves * 16;            // [kWaves][16][D]
+    __shared__ int spage[kSegPages];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int hl = lane % 16;        // column of this lane inside a tile
+    const int j = lane / 16;         // lane group
+    const int r = lane % 16;         // A-operand row of this lane
+
+    const WorkItem wi = decode_work_item(blockIdx.x, (uint32_t)p.num_seqs,
+                                         (uint32_t)(p.num_kv_heads * p.col_groups * p.max_parts));
+    const int b = wi.b;
+    const int g = wi.q % p.num_kv_heads;
+    const int cg = (wi.q / p.num_kv_heads) % p.col_groups;
+    const int slot = wi.q / (p.num_kv_heads * p.col_groups);
+    const int G = p.group;
+
+    int L = p.context_lens[b];
+    const int cap = min(p.max_context_len, p.max_blocks_per_seq * BS);
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const QueryRows qr = query_rows(p.query_start, b, L, p.num_tokens, p.max_query_len);
+    const int n = qr.n;
+    const int col0 = cg * COLS;
+    if (col0 >= G * n) return;                               // no query in this column group
+    const int first_jq = col0 / G;
+    const int last_jq = min(n - 1, (col0 + COLS - 1) / G);
+    const int lo_lim = L - n + first_jq;                     // smallest last visible position
+    const int hi_lim = L - n + last_jq;                      // largest
+    const int part = partition_of(slot, p.max_parts, L, p.partition, p.stream_kv != 0);
+    if (part < 0) return;
+    const int start = part * p.partition;
+    if (start > hi_lim) return;                              // nothing here is visible to the group
+    const int end = min(start + p.partition, hi_lim + 1);
+
+    // Per tile: this lane's column, its query row and head, and the last
+    // position it sees (-1: a padding column past the sequence's queries).
+    int lim[NT];
+    bf16x8_t qf[NT][KSTEPS];
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = col0 + 16 * nt + hl;
+        const int jq = c / G;
+        const bool live = jq < n;
+        lim[nt] = live ? L - n + jq : -1;
+        const size_t qrow = ((size_t)(qr.row0 + (live ? jq : 0)) * p.num_heads + (size_t)g * G + c % G) * D;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qrow;
+        for (int s = 0; s < KSTEPS; ++s) {
+            u32x4_t raw = ld16(qp + 32 * s + 8 * j);
+            if (!live) raw = u32x4_t{0u, 0u, 0u, 0u};
+            qf[nt][s] = as_bf16x8(raw);
+        }
+    }
+
+    const uint32_t kofs = (uint32_t)((j * BS + r) * 16);
+    const uint32_t vofs = (uint32_t)((r * BS + 4 * j) * 2);
+    constexpr uint32_t kStepBytes = 4u * BS * 16;
+    constexpr uint32_t kTileStep = 16u * BS * 2;
+
+    const int* row = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+    const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache);
+    const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache);
+    const size_t tile_elems = (size_t)D * BS;
+    const size_t kv_heads = (size_t)p.num_kv_heads;
+
+    float m_run[NT], l_run[NT];
+    f32x4_t acc[NT][DC];
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = neg_inf();
+        l_run[nt] = 0.f;
+        for (int dc = 0; dc < DC; ++dc) acc[nt][dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int nchunks = (end - start + kChunk - 1) / kChunk;
+    const int blk_first = start / BS;
+    const int blk_end = (end + BS - 1) / BS;
+    constexpr int kSegChunks = kSegPages * BS / kChunk;
+    for (int seg = 0; seg < nchunks; seg += kSegChunks) {
+        const int seg_blk = blk_first + seg * (kChunk / BS);
+        const int seg_n = min(kSegPages, blk_end - seg_blk);
+        if (seg > 0) __syncthreads();
+        for (int i = tid; i < seg_n; i += kThreads) {
+            const int pg = row[seg_blk + i];
+            spage[i] = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
+        }
+        __syncthreads();
+        const int seg_end = min(nchunks, seg + kSegChunks);
+        for (int ci = seg + w; ci < seg_end; ci += kWaves) {
+            const int cstart = start + ci * kChunk;
+            const int valid = min(kChunk, end - cstart);
+
+            const int lb = (ci - seg) * (kChunk / BS);
+            const int pg0 = __builtin_amdgcn_readfirstlane(spage[lb]);
+            const int pg1 = (BS == 16 && valid > kHalf) ? __builtin_amdgcn_readfirstlane(spage[lb + 1]) : pg0;
+
+            u32x4_t kraw[2][KSTEPS];
+            u32x4_t vop[DC];
+            {
+                __amdgpu_buffer_rsrc_t krs[2], vrs[2];
+                for (int t = 0; t < 2; ++t) {
+                    const int page = t ? pg1 : pg0;
+                    const int toff = BS == 32 ? kHalf * t : 0;
+                    const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
+                    const bool half_live = t == 0 || valid > kHalf;
+                    krs[t] = make_rsrc(kc + tile + toff * 8, half_live ? kTileBytes - toff * 16 : 0);
+                    vrs[t] = make_rsrc(vc + tile + toff, half_live ? kTileBytes - toff * 2 : 0);
+                }
+                for (int t = 0; t < 2; ++t)
+                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16<POLICY>(krs[t], kofs, s * kStepBytes);
+                u32x2_t vh[2][DC];
+                for (int t = 0; t < 2; ++t)
+                    for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8<POLICY>(vrs[t], vofs, dc * kTileStep);
+                __builtin_amdgcn_sched_barrier(0);
+                for (int dc = 0; dc < DC; ++dc)
+                    vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+            }
+
+            // wave-uniform: does any score of this chunk need masking?
+            const bool masked = valid < kChunk || cstart + kChunk - 1 > lo_lim;
+            bf16x8_t pf[NT];
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4_t st[2];
+                for (int t = 0; t < 2; ++t) {
+                    st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    for (int s = 0; s < KSTEPS; ++s)
+                        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[nt][s], st[t], 0, 0, 0);
+                }
+                float sc[8];
+                for (int t = 0; t < 2; ++t)
+                    for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
+                if (masked) {
+                    // keep chunk tokens < cut: inside the partition and visible to this column
+                    const int cut = min(valid, lim[nt] - cstart + 1);
+                    for (int t = 0; t < 2; ++t)
+                        for (int i = 0; i < 4; ++i)
+                            sc[4 * t + i] = slot_token(t, i, j) < cut ? sc[4 * t + i] : neg_inf();
+                }
+                float mx = sc[0];
+                for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const bool grow = mx > m_run[nt] + kRescaleSlack;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    const float mn = grow ? mx : m_run[nt];
+                    // A column with nothing accumulated yet (running max -inf)
+                    // takes factor 0, not 2^(-inf - -inf) = NaN: another column
+                    // of the tile may be what took the branch.
+                    const float alpha = m_run[nt] == neg_inf() ? 0.f : fast_exp2(m_run[nt] - mn);
+                    for (int dc = 0; dc < DC; ++dc) acc[nt][dc] = acc[nt][dc] * alpha;
+                    l_run[nt] *= alpha;
+                    m_run[nt] = mn;
+                }
+                // -inf running max: nothing visible yet, every score here is -inf too
+                const float mref = m_run[nt] == neg_inf() ? 0.f : m_run[nt];
+                float psum = 0.f;
+                for (int k = 0; k < 8; ++k) {
+                    const bf16_t pb = (bf16_t)fast_exp2(sc[k] - mref);
+                    pf[nt][k] = pb;
+                    psum += (float)pb;
+                }
+                l_run[nt] += psum;
+            }
+
+            if (valid < kChunk) {
+                for (int q = 0; q < 4; ++q) {
+                    const int tok = slot_token(q / 2, 2 * (q % 2), j);
+                    const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
+                    const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
+                    for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
+                }
+            }
+            for (int nt = 0; nt < NT; ++nt)
+                for (int dc = 0; dc < DC; ++dc)
+                    acc[nt][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf[nt], acc[nt][dc], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the four waves, one tile at a time through the same LDS
+    const size_t rows = ws_rows(p.num_tokens, p.num_heads, p.max_parts);
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+    for (int nt = 0; nt < NT; ++nt) {
+        float l = l_run[nt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (nt > 0) __syncthreads();              // the previous tile's reads are done
+        if (lane < 16) {
+            sm_m[w * 16 + hl] = m_run[nt];
+            sm_l[w * 16 + hl] = l;
+        }
+        {
+            float* dst = sacc + (size_t)(w * 16 + hl) * D + 4 * j;
+            for (int dc = 0; dc < DC; ++dc)
+                for (int i = 0; i < 4; ++i) dst[16 * dc + i] = acc[nt][dc][i];
+        }
+        __syncthreads();
+        for (int e = tid; e < 16 * D; e += kThreads) {
+            const int h = e / D;
+            const int d = e % D;
+            const int c = col0 + 16 * nt + h;
+            const int jq = c / G;
+            if (jq >= n) continue;
+            float M = neg_inf();
+            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
+            float num = 0.f, den = 0.f;
+            if (M != neg_inf()) {
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const float f = fast_exp2(sm_m[ww * 16 + h] - M);
+                    num = fmaf(f, sacc[(size_t)(ww * 16 + h) * D + d], num);
+                    den = fmaf(f, sm_l[ww * 16 + h], den);
+                }
+            }
+            const size_t orow = (size_t)(qr.row0 + jq) * p.num_heads + (size_t)g * G + c % G;
+            if (p.split) {
+                const size_t rr = orow * p.max_parts + part;
+                p.ws[rr * D + d] = num;
+                if (d == 0) {
+                    p.ws[rows * D + rr] = M;
+                    p.ws[rows * D + rows + rr] = den;
+                }
+            } else {
+                out[orow * D + d] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+            }
+        }
+    }
+}
+
+template <int D, int BS, int NT, int POLICY>
+hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
+    const size_t smem = sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * 16 * D);
+    const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * p.col_groups * p.max_parts;
+    hipLaunchKernelGGL((decode_multi_kernel<D, BS, NT, POLICY>), dim3((unsigned)nwg), dim3(kThreads), smem,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <int NT, int POLICY>
+hipError_t launch_tiles(const DecodeParams& p, hipStream_t stream) {
+    if (p.head_dim == 64)
+        return p.block_size == 16 ? launch_shape<64, 16, NT, POLICY>(p, stream)
+                                  : launch_shape<64, 32, NT, POLICY>(p, stream);
+    return p.block_size == 16 ? launch_shape<128, 16, NT, POLICY>(p, stream)
+                              : launch_shape<128, 32, NT, POLICY>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_multi(const DecodeParams& p, int col_tiles, hipStream_t stream) {
+    if (p.stream_kv)
+        return col_tiles == 1 ? launch_tiles<1, kPolicyStream>(p, stream) : launch_tiles<2, kPolicyStream>(p, stream);
+    return col_tiles == 1 ? launch_tiles<1, kPolicyReuse>(p, stream) : launch_tiles<2, kPolicyReuse>(p, stream);
+}
+
+}  // namespace pa_impl

@@ -45,6 +45,27 @@ __device__ __forceinline__ float lane_value(float v, int k) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k));
 }
 
+__device__ __forceinline__ int clamp_len(int L, int max_context_len) {
+    return L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
+}
+
+// Multi-query merge: positions query token t sees (0 if no sequence covers
+// row t).  Its sequence is the last s with query_start[s] <= t (binary
+// search over the wave-uniform t, so scalar loads); the rows that sequence
+// covers come from query_rows, as in the partition kernel.
+__device__ __forceinline__ int token_context(const ReduceParams& p, int t) {
+    int lo = 0, hi = p.num_groups - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (p.query_start[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int L = clamp_len(p.context_lens[lo], p.max_context_len);
+    const QueryRows qr = query_rows(p.query_start, lo, L, p.num_seqs, p.max_query_len);
+    if (t < qr.row0 || t >= qr.row0 + qr.n) return 0;
+    return L - qr.n + (t - qr.row0) + 1;
+}
+
 template <typename E>
 __device__ __forceinline__ void store_out(E* out, size_t i, float v);
 template <>
@@ -67,8 +88,7 @@ void decode_reduce_kernel(ReduceParams p) {
     const size_t pairs = (size_t)p.num_seqs * p.num_heads;
     if (bh >= pairs) return;
     const int b = (int)(bh / (size_t)p.num_heads);
-    int L = p.context_lens[b];
-    L = L < 0 ? 0 : (L > p.max_context_len ? p.max_context_len : L);
+    const int L = p.query_start ? token_context(p, b) : clamp_len(p.context_lens[b], p.max_context_len);
     int n = (L + p.partition - 1) / p.partition;
     n = n > p.max_parts ? p.max_parts : n;
 

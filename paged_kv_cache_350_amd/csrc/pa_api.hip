@@ -20,6 +20,7 @@ constexpr int64_t kMinUnits = 1024;          // below this, fall back to the sma
 constexpr int32_t kChunk = 32;               // partitions are whole 32-token chunks
 constexpr int32_t kMaxGroup = 16;            // query heads per kv head
 constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
+constexpr int32_t kMaxQueryLen = 1024;       // multi-query: new tokens per sequence
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -150,6 +151,10 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.max_context_len = max_context_len;
     p.num_blocks = num_blocks;
     p.stream_kv = reuse != PA_KV_SHARED;
+    p.query_start = nullptr;
+    p.num_tokens = 0;
+    p.max_query_len = 0;
+    p.col_groups = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -173,6 +178,9 @@ pa_status launch_plan(const Plan& plan, hipStream_t stream) {
 
 pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out, hipStream_t stream) {
     ReduceParams r;
+    r.query_start = nullptr;
+    r.num_groups = 0;
+    r.max_query_len = 0;
     r.ws = plan.p.ws;
     r.context_lens = context_lens;
     r.out = out;
@@ -183,6 +191,26 @@ pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out
     r.partition = plan.p.partition;
     r.max_parts = plan.p.max_parts;
     return hip_status(pa_impl::launch_decode_reduce(r, plan.dtype, stream));
+}
+
+// Multi-query column tiling: (query token, head) pairs of one kv head, 16
+// per MFMA tile, one tile per workgroup when they fit, else two.
+int32_t multi_col_tiles(int32_t group, int32_t max_query_len) {
+    return (int64_t)group * max_query_len <= 16 ? 1 : 2;
+}
+
+int32_t multi_col_groups(int32_t group, int32_t max_query_len) {
+    const int64_t per = 16 * multi_col_tiles(group, max_query_len);
+    return (int32_t)(((int64_t)group * max_query_len + per - 1) / per);
+}
+
+int32_t resolve_multi_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t max_context_len, int32_t max_query_len, int32_t partition_size) {
+    if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0 || max_query_len < 1)
+        return -1;
+    const int64_t units = (int64_t)num_seqs * multi_col_groups(num_heads / num_kv_heads, max_query_len);
+    const int32_t seqs = units > INT32_MAX ? INT32_MAX : (int32_t)units;
+    return resolve_partition(seqs, num_kv_heads, max_context_len, partition_size);
 }
 
 }  // namespace
@@ -205,7 +233,7 @@ const char* pa_status_string(pa_status status) {
     return "unknown status";
 }
 
-int32_t pa_version(void) { return 300; }
+int32_t pa_version(void) { return 310; }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size) {
@@ -360,6 +388,122 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     plan.p.partition = partition;
     plan.p.max_parts = parts_for(max_context_len, partition);
     return launch_reduce(plan, context_lens, out, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int32_t pa_decode_multi_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t max_query_len,
+                                       int32_t partition_size) {
+    return resolve_multi_partition(num_seqs, num_heads, num_kv_heads, max_context_len, max_query_len,
+                                   partition_size);
+}
+
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                                      int32_t max_query_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_tokens < 0 || head_dim <= 0) return 0;
+    const int32_t partition = resolve_multi_partition(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                                      max_query_len, partition_size);
+    if (partition <= 0) return 0;
+    return workspace_bytes_for(num_tokens, num_heads, head_dim, max_context_len, partition);
+}
+
+pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                          float scale, void* out, hipStream_t stream, int32_t num_seqs,
+                          int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
+                          int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                          pa_kv_reuse reuse, void* workspace, size_t workspace_bytes) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    if (reuse != PA_KV_AUTO && reuse != PA_KV_STREAM && reuse != PA_KV_SHARED) return PA_ERR_ARG;
+    pa_status st = shape_status(num_kv_heads, head_dim, block_size);
+    if (st != PA_OK) return st;
+    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (num_heads <= 0 || num_heads % num_kv_heads != 0) return PA_ERR_ARG;
+    if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0) return PA_ERR_ARG;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_ARG;
+    if (num_blocks > (int64_t)INT32_MAX + 1) return PA_ERR_ARG;
+    if (!isfinite(scale)) return PA_ERR_ARG;
+    if (num_seqs < 0 || num_tokens < 0 || max_query_len < 1) return PA_ERR_ARG;
+    if (max_query_len > kMaxQueryLen) return PA_ERR_UNSUPPORTED;
+    int32_t partition = resolve_multi_partition(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                                 max_query_len, partition_size);
+    if (partition < 0) return PA_ERR_ARG;
+    if (partition > 0 && max_context_len == 0) partition = 0;
+    if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ARG;
+
+    const int32_t group = num_heads / num_kv_heads;
+    const int32_t tiles = multi_col_tiles(group, max_query_len);
+    const int32_t col_groups = multi_col_groups(group, max_query_len);
+    const int32_t parts = partition > 0 ? parts_for(max_context_len, partition) : 1;
+    if ((uint64_t)num_seqs * num_kv_heads * col_groups * parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
+    if ((uint64_t)num_tokens * num_heads >= kMaxGrid) return PA_ERR_UNSUPPORTED;
+    if (partition > 0) {
+        const size_t need = workspace_bytes_for(num_tokens, num_heads, head_dim, max_context_len, partition);
+        if (!workspace) return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PA_ERR_ARG;
+        if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    }
+
+    DecodeParams p{};
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.ws = static_cast<float*>(workspace);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = group;
+    p.head_dim = head_dim;
+    p.block_size = block_size;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.num_blocks = num_blocks;
+    p.stream_kv = reuse != PA_KV_SHARED;
+    p.query_start = query_start;
+    p.num_tokens = num_tokens;
+    p.max_query_len = max_query_len;
+    p.col_groups = col_groups;
+    if (partition > 0) {
+        p.partition = partition;
+        p.max_parts = parts;
+        p.split = 1;
+    } else {
+        const int32_t whole = max_context_len < 1 ? 1 : max_context_len;
+        p.partition = (int32_t)(((int64_t)whole + kChunk - 1) / kChunk * kChunk);
+        p.max_parts = 1;
+        p.split = 0;
+    }
+    st = hip_status(pa_impl::launch_decode_multi(p, tiles, stream));
+    if (st != PA_OK || partition == 0) return st;
+
+    ReduceParams r;
+    r.ws = p.ws;
+    r.context_lens = context_lens;
+    r.out = out;
+    r.num_seqs = num_tokens;              // merge rows are query tokens
+    r.num_heads = num_heads;
+    r.head_dim = head_dim;
+    r.max_context_len = max_context_len;
+    r.partition = partition;
+    r.max_parts = parts;
+    r.query_start = query_start;
+    r.num_groups = num_seqs;
+    r.max_query_len = max_query_len;
+    return hip_status(pa_impl::launch_decode_reduce(r, dtype, stream));
 }
 
 }  // extern "C"

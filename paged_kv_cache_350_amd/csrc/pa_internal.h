@@ -35,6 +35,11 @@ struct DecodeParams {
     int32_t max_parts;     // partitions per (seq, head) in the workspace (1 = single pass)
     int32_t split;         // 1: write partials to ws, 0: write out
     int32_t stream_kv;     // 1: no page is shared between sequences (streaming loads)
+    // multi-query launches only (null / 0 otherwise)
+    const int32_t* query_start;   // [num_seqs + 1]: query rows of each sequence
+    int32_t num_tokens;    // rows of q / out
+    int32_t max_query_len; // bound on query rows per sequence
+    int32_t col_groups;    // column groups of 16 * col_tiles (query token, head) pairs per kv head
 };
 
 struct ReduceParams {
@@ -47,6 +52,11 @@ struct ReduceParams {
     int32_t max_context_len;
     int32_t partition;
     int32_t max_parts;
+    // multi-query merge: rows are query tokens; a row's context is found
+    // through query_start [num_groups + 1] and the per-sequence context_lens
+    const int32_t* query_start;
+    int32_t num_groups;
+    int32_t max_query_len;
 };
 
 // Workspace layout for the split path (all fp32):
@@ -70,5 +80,6 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* block
 hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype dtype, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceParams& p, pa_dtype dtype, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeParams& p, int col_tiles, hipStream_t stream);
 
 }  // namespace pa_impl

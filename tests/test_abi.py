@@ -50,7 +50,7 @@ def test_status_strings(L):
         assert pa.status_string(code)
     assert pa.status_string(0) == "ok"
     assert pa.status_string(-99) == "unknown status"
-    assert L.pa_version() == 300
+    assert L.pa_version() == 310
 
 
 def test_partition_policy_and_workspace_size(L):
@@ -191,3 +191,46 @@ def test_decode_append_validates(L):
     assert call(reuse=7) == pa.PA_ERR_ARG
     assert call(part=256) == pa.PA_ERR_WORKSPACE
     assert call(B=0, kn=None, vn=None, q=None) == pa.PA_OK
+
+
+def test_decode_multi_validates(L):
+    """pa_decode_multi argument checks (all fail on the host, before any launch)."""
+    def call(**kw):
+        a = dict(q=FAKE, qs=FAKE, out=FAKE, B=4, T=20, hq=32, hkv=8, d=128, maxb=256, ctx=4096,
+                 maxq=5, dtype=1, part=0, reuse=0, ws=FAKE, wsb=1 << 30, bs=16, scale=0.1)
+        a.update(kw)
+        return L.pa_decode_multi(a["q"], FAKE, FAKE, FAKE, FAKE, a["qs"], a["bs"], a["hkv"], a["scale"],
+                                 a["out"], None, a["B"], a["T"], a["hq"], a["d"], a["maxb"], a["ctx"],
+                                 a["maxq"], 100000, a["dtype"], a["part"], a["reuse"], a["ws"], a["wsb"])
+    assert call(B=0) == pa.PA_OK and call(T=0) == pa.PA_OK          # nothing to do
+    assert call(dtype=0) == pa.PA_ERR_UNSUPPORTED                    # fp32: no multi-query kernel
+    assert call(dtype=7) == pa.PA_ERR_ARG
+    assert call(maxq=0) == pa.PA_ERR_ARG
+    assert call(maxq=1025) == pa.PA_ERR_UNSUPPORTED
+    assert call(qs=None) == pa.PA_ERR_NULL
+    assert call(out=None) == pa.PA_ERR_NULL
+    assert call(q=FAKE + 2) == pa.PA_ERR_ARG
+    assert call(ws=None) == pa.PA_ERR_WORKSPACE                      # 4096 tokens: split path
+    assert call(wsb=16) == pa.PA_ERR_WORKSPACE
+    assert call(hq=24, hkv=8, d=96) == pa.PA_ERR_UNSUPPORTED
+    assert call(hq=30) == pa.PA_ERR_ARG                              # not a multiple of kv heads
+    assert call(part=100) == pa.PA_ERR_ARG
+    assert call(reuse=9) == pa.PA_ERR_ARG
+    assert call(ctx=4097) == pa.PA_ERR_ARG                            # beyond the table width
+    assert call(scale=float("nan")) == pa.PA_ERR_ARG
+    assert call(B=-1) == pa.PA_ERR_ARG
+
+
+def test_decode_multi_partition_policy(L):
+    # columns: G = 4 query heads per kv head x up to 5 tokens = 20 -> one group of two tiles
+    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 5, -1) == 0
+    assert pa.decode_multi_partition_size(64, 32, 8, 512, 5, 0) == 0         # short: one pass
+    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 5, 0) == pa.decode_partition_size(64, 8, 4096, 0)
+    # 4 x 16 tokens = 64 columns -> two column groups count as twice the sequences
+    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 16, 0) == pa.decode_partition_size(128, 8, 4096, 0)
+    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 0, 0) < 0
+    # workspace rows are query tokens
+    P = pa.decode_multi_partition_size(64, 32, 8, 4096, 5, 0)
+    want = 320 * 32 * (-(-4096 // P)) * (128 + 2) * 4
+    assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 0) == want
+    assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, -1) == 0

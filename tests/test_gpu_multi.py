@@ -1,0 +1,149 @@
+"""pa_decode_multi (several new tokens per sequence, causal among them) on
+the GPU, through the C ABI.
+
+Every case appends the new tokens' K/V rows with pa_kv_append and then runs
+pa_decode_multi.  The oracle takes the caches as generated (before the
+append), applies its own append of the same rows and computes
+oracle.decode_multi in float64, so no oracle input comes from the device.
+Tolerances are the decode ones (bf16: max-abs 2e-2, relative L2 5e-3)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, storage_np
+
+pytestmark = pytest.mark.gpu
+
+# context lengths (new tokens included) around chunk and partition edges, and
+# the new tokens of each: 0, 1, all of the context, and more than fill a tile
+LENS = [1, 5, 16, 17, 31, 32, 33, 64, 100, 257, 513, 700]
+NEWS = [1, 5, 3, 0, 8, 1, 16, 7, 2, 12, 5, 9]
+
+SHAPES = [  # (block_size, num_heads, num_kv_heads, head_dim)
+    (16, 32, 8, 128),
+    (32, 32, 8, 128),
+    (16, 64, 8, 128),
+    (32, 8, 2, 64),
+    (16, 16, 16, 128),
+    (16, 16, 1, 64),
+]
+PARTS = [-1, 0, 64, 256]
+
+
+def run_gpu(pa, w, t, partition_size=0, reuse="auto"):
+    pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    return pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                           t["query_start"], w.scale, w.max_context_len, w.max_query_len,
+                           partition_size=partition_size, reuse=reuse)
+
+
+def oracle_multi(w, kc0, vc0, q, seqs=None):
+    """Oracle append of the step's rows into the generated caches, then the
+    multi-query oracle (rows of sequences outside ``seqs`` stay zero)."""
+    keep = np.ones(len(w.append_seq), dtype=bool) if seqs is None else np.isin(w.append_seq, list(seqs))
+    kc, vc = oracle.kv_append(w._k_new[keep], w._v_new[keep], w.append_slots[keep], kc0, vc0, w.block_size)
+    return oracle.decode_multi(q, kc, vc, w.block_tables, w.context_lens, w.query_start, w.scale,
+                               w.block_size, "bf16", seqs=seqs)
+
+
+def prepare(w):
+    t = W.make_tensors(w, "cuda")
+    w._k_new, w._v_new = storage_np(t["k_new"]), storage_np(t["v_new"])
+    return t, storage_np(t["k_cache"]), storage_np(t["v_cache"]), storage_np(t["q"])
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_multi_matches_oracle(shape):
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    w = W.multi_custom("ragged_multi", 41, LENS, NEWS, hq, hkv, d, bs)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    for P in PARTS:
+        t2 = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("multi", shape, "partition", P, w.summary())
+        out = run_gpu(pa, w, t2, partition_size=P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"{shape} P={P}")
+
+
+def test_one_new_token_is_bit_identical_to_decode():
+    """With n = 1 everywhere the multi-query kernel does the decode kernel's
+    arithmetic in the same order: outputs agree bit for bit with pa_decode's
+    streaming path, single pass and split."""
+    pa = require_gpu()
+    lens = [1, 17, 33, 300, 513, 1024, 2000, 4095]
+    w = W.multi_custom("one_new", 42, lens, [1] * len(lens), 32, 8, 128, 16)
+    for P in (-1, 0, 256):
+        t, _, _, _ = prepare(w)
+        say("n=1 vs decode, partition", P)
+        pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+        a = pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                            t["query_start"], w.scale, w.max_context_len, 1, partition_size=P)
+        b = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], w.scale,
+                      w.max_context_len, partition_size=P, kernel="mfma", reuse="stream")
+        torch.cuda.synchronize()
+        assert bits_equal(a, b), P
+
+
+def test_wide_queries_span_column_groups():
+    """16 query heads per kv head x 8 new tokens = 128 columns: four column
+    groups of two tiles, each reading the pages on its own."""
+    pa = require_gpu()
+    w = W.multi_custom("wide", 43, [8, 40, 129, 600], [8, 8, 3, 8], 64, 4, 128, 16)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    for P in (-1, 64):
+        t2 = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("wide, partition", P)
+        out = run_gpu(pa, w, t2, partition_size=P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"wide P={P}")
+
+
+def test_shared_and_stream_paths_agree():
+    pa = require_gpu()
+    w = W.multi_custom("paths", 44, LENS, NEWS, 32, 8, 128, 16)
+    outs = []
+    for reuse in ("stream", "shared"):
+        t, _, _, _ = prepare(w)
+        say("reuse", reuse)
+        outs.append(run_gpu(pa, w, t, partition_size=64, reuse=reuse))
+    torch.cuda.synchronize()
+    assert bits_equal(outs[0], outs[1])
+
+
+def test_rows_outside_the_sequences_are_untouched_in_one_pass():
+    """Query rows past query_start[num_seqs] are not written (single pass)."""
+    pa = require_gpu()
+    w = W.multi_custom("tail_rows", 45, [40, 70], [3, 2], 32, 8, 128, 16)
+    t, kc0, vc0, q = prepare(w)
+    pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    q_big = torch.cat([t["q"], t["q"][:2]]).contiguous()
+    out = torch.full_like(q_big, 7.0)
+    pa.decode_multi(q_big, t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], t["query_start"],
+                    w.scale, w.max_context_len, w.max_query_len, out=out, partition_size=-1)
+    torch.cuda.synchronize()
+    ref = oracle_multi(w, kc0, vc0, q)
+    check_close(out_f64(out[:5]), ref, "bf16", "covered rows")
+    assert bool((out[5:] == 7.0).all())
+
+
+def test_spec_verify_full_size_sampled():
+    """The speculative-verification batch at full size (64 sequences, 5
+    queries each, contexts up to 4,096) in the benchmark's launch
+    configuration; 12 sampled sequences checked against the oracle."""
+    pa = require_gpu()
+    w = W.spec_verify()
+    t, kc0, vc0, q = prepare(w)
+    say("spec_verify full size", w.summary())
+    out = run_gpu(pa, w, t)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    seqs = sorted(rng.choice(w.num_seqs, size=12, replace=False).tolist())
+    ref = oracle_multi(w, kc0, vc0, q, seqs=seqs)
+    rows = np.concatenate([np.arange(w.query_start[b], w.query_start[b + 1]) for b in seqs])
+    check_close(out_f64(out)[rows], ref[rows], "bf16", "spec_verify sampled")

@@ -78,6 +78,7 @@ class Workload:
     partition_size: int = 0           # 0 = library default
     description: str = ""
     extra: Dict[str, object] = field(default_factory=dict)
+    query_lens: Optional[np.ndarray] = None   # int32 [B]: new tokens per sequence (multi-query); None = 1 query each
 
     @property
     def num_seqs(self) -> int:
@@ -94,6 +95,17 @@ class Workload:
     @property
     def max_blocks_per_seq(self) -> int:
         return int(self.block_tables.shape[1])
+
+    @property
+    def query_start(self) -> Optional[np.ndarray]:
+        """int32 [B + 1] offsets of each sequence's query rows (multi-query only)."""
+        if self.query_lens is None:
+            return None
+        return np.concatenate([[0], np.cumsum(self.query_lens)]).astype(np.int32)
+
+    @property
+    def max_query_len(self) -> int:
+        return 1 if self.query_lens is None else max(int(self.query_lens.max()), 1)
 
     @property
     def scale(self) -> float:
@@ -365,6 +377,67 @@ def beam_fork(seed: int = 3, beams: int = 8, prompt: int = 32768, shared_gen: in
     return w
 
 
+def _multi(name: str, seed: int, lens, news, num_heads: int, num_kv_heads: int, head_dim: int,
+           block_size: int, rng: np.random.Generator, description: str, manager=None) -> Workload:
+    """Independent sequences that each bring n_b new tokens at once: before
+    the step sequence b holds L_b - n_b tokens, the step appends n_b (slots
+    in position order, pages opened as blocks fill), then n_b queries attend
+    (multi-query).  Pool = pages needed + 10 %, ids randomly permuted, bf16."""
+    lens = np.asarray(lens, dtype=np.int64)
+    news = np.asarray(news, dtype=np.int64)
+    if (news < 0).any() or (news > lens).any():
+        raise ValueError("0 <= new tokens <= context length")
+    bs = block_size
+    need = int(sum(-(-int(L) // bs) for L in lens))
+    num_blocks = max(int(math.ceil(1.1 * need)), need + 1)
+    perm = rng.permutation(num_blocks)
+    mgr = _manager(manager, num_blocks, bs, perm)
+    seqs = list(range(len(lens)))
+    for b in seqs:
+        mgr.allocate(b, int(lens[b] - news[b]))
+    pre_tables = [list(mgr.tables[b]) for b in seqs]
+    slots, owner = [], []
+    for b in seqs:
+        for _ in range(int(news[b])):
+            slots.append(mgr.append_token(b))
+            owner.append(b)
+    pad_page = int(mgr.free[-1])
+    return Workload(
+        name=name, seed=seed, dtype="bf16", num_heads=num_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, block_size=bs, num_blocks=num_blocks,
+        context_lens=lens.astype(np.int32), block_tables=_tables_from(mgr, seqs, pad_page),
+        pad_page=pad_page, resident=_resident_mask(num_blocks, bs, pre_tables, lens - news),
+        copy_pairs=np.zeros((0, 2), dtype=np.int64), append_slots=np.asarray(slots, dtype=np.int64),
+        append_seq=np.asarray(owner, dtype=np.int32), description=description,
+        query_lens=news.astype(np.int32))
+
+
+def spec_verify(seed: int = 5, num_seqs: int = 64, len_range: Tuple[int, int] = (512, 4096),
+                drafts: int = 4, manager=None) -> Workload:
+    """Speculative-decoding verification on the Llama-3-8B-shaped batch:
+    every sequence scores its last accepted token plus ``drafts`` draft
+    tokens (n = drafts + 1 queries), context lengths (new tokens included)
+    integer-uniform in ``len_range``; 32 q / 8 kv heads, head_dim 128,
+    block 16, bf16."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(len_range[0], len_range[1], size=num_seqs, endpoint=True)
+    news = np.full(num_seqs, drafts + 1)
+    return _multi("spec_verify" if (num_seqs, len_range, drafts) == (64, (512, 4096), 4) else
+                  f"spec_verify_b{num_seqs}_l{len_range[0]}-{len_range[1]}_k{drafts}",
+                  seed, lens, news, 32, 8, 128, 16, rng, manager=manager,
+                  description=f"{num_seqs} seqs, L~U[{len_range[0]},{len_range[1]}], {drafts + 1} queries "
+                              f"each (verify {drafts} drafts), 32/8 heads, D 128, bs 16, bf16")
+
+
+def multi_custom(name: str, seed: int, lens, news, num_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, manager=None) -> Workload:
+    """Multi-query sequences with explicit context lengths and new-token counts."""
+    rng = np.random.default_rng(seed)
+    return _multi(name, seed, lens, news, num_heads, num_kv_heads, head_dim, block_size, rng,
+                  manager=manager, description=f"{len(lens)} seqs, {num_heads}/{num_kv_heads} heads, "
+                                               f"D {head_dim}, bs {block_size}, bf16, multi-query")
+
+
 def copy_probe(beams: int = 8, prompt: int = 32768) -> np.ndarray:
     """Eager fork of a ``prompt``-token prompt (block 32) to ``beams-1`` beams:
     the page copies copy-on-write avoids.  Returns (src, dst) pairs over a pool
@@ -424,7 +497,8 @@ def make_tensors(w: Workload, device, value_seed: Optional[int] = None) -> Dict[
 
     B, Hq, Hkv, D = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim
     T = int(w.append_slots.shape[0])
-    q = randn(B, Hq, D)
+    rows = B if w.query_lens is None else int(w.query_lens.sum())
+    q = randn(rows, Hq, D)
     k_new = randn(T, Hkv, D)
     v_new = randn(T, Hkv, D)
     k_cache = randn(*w.k_cache_shape())
@@ -441,4 +515,5 @@ def make_tensors(w: Workload, device, value_seed: Optional[int] = None) -> Dict[
         "context_lens": torch.from_numpy(w.context_lens).to(dev),
         "slot_mapping": torch.from_numpy(w.append_slots).to(dev),
         "copy_pairs": torch.from_numpy(w.copy_pairs).to(dev),
+        "query_start": None if w.query_lens is None else torch.from_numpy(w.query_start).to(dev),
     }
