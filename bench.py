@@ -409,18 +409,24 @@ def multi_bench(a, torch, pa, W) -> int:
     digest = _src_digest("decode_multi.hip", "decode_reduce.hip", "pa_device.h", "pa_internal.h")
 
     # CPU baseline: the oracle on whole sequences, about cpu_seconds of work
-    kc0, vc0, q = _host(t["k_cache"]), _host(t["v_cache"]), _host(t["q"])
-    done = nbytes = 0
-    elapsed = 0.0
-    for b in range(w.num_seqs):
-        t1 = time.perf_counter()
-        oracle.decode_multi(q, kc0, vc0, w.block_tables, w.context_lens, w.query_start, w.scale,
-                            w.block_size, w.dtype, seqs=[b])
-        elapsed += time.perf_counter() - t1
-        done += 1
-        nbytes += int(w.context_lens[b]) * w.kv_bytes_per_token()
-        if elapsed >= a.cpu_seconds:
-            break
+    cpu = None
+    if not a.no_cpu_baseline:
+        kc0, vc0, q = _host(t["k_cache"]), _host(t["v_cache"]), _host(t["q"])
+        done = nbytes = 0
+        elapsed = 0.0
+        for b in range(w.num_seqs):
+            t1 = time.perf_counter()
+            oracle.decode_multi(q, kc0, vc0, w.block_tables, w.context_lens, w.query_start, w.scale,
+                                w.block_size, w.dtype, seqs=[b])
+            elapsed += time.perf_counter() - t1
+            done += 1
+            nbytes += int(w.context_lens[b]) * w.kv_bytes_per_token()
+            if elapsed >= a.cpu_seconds:
+                break
+        cpu = {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} whole sequences of the {w.name} batch, float64 numpy oracle, "
+                         f"{elapsed:.1f} s of CPU time"}
+    kname = "decode_multi" + ("_single" if P <= 0 else " partition + merge")
     rec = {
         "metric": "multi-query paged attention KV GB/s read (speculative verification)",
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
@@ -433,15 +439,13 @@ def multi_bench(a, torch, pa, W) -> int:
                    "sum_context_tokens": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
                    "partition_size": P, "reuse": reuse, "kv_bytes_per_step": kv_bytes},
         "kernels_avg_us": {"kv_append": round(append_ms * 1e3, 2),
-                           "decode_multi_total": round(multi_ms * 1e3, 2)},
+                           kname: round(multi_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_multi partition + merge", "avg_launch_us": round(multi_ms * 1e3, 2),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": _traffic("decode_multi", w.name, digest) if P <= 0 else None,
+                     "kernel": kname, "avg_launch_us": round(multi_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes, "source_digest": digest},
-        "cpu_baseline": {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-                         "kind": "oracle",
-                         "sample": f"{done} whole sequences of the {w.name} batch, float64 numpy oracle, "
-                                   f"{elapsed:.1f} s of CPU time"},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
     return 0

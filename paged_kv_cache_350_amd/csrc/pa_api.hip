@@ -21,6 +21,8 @@ constexpr int32_t kChunk = 32;               // partitions are whole 32-token ch
 constexpr int32_t kMaxGroup = 16;            // query heads per kv head
 constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
 constexpr int32_t kMaxQueryLen = 1024;       // multi-query: new tokens per sequence
+constexpr int64_t kMultiFill = 256;          // multi-query: workgroups that keep every CU busy
+constexpr int32_t kMultiMaxPartition = 8192;
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -204,13 +206,32 @@ int32_t multi_col_groups(int32_t group, int32_t max_query_len) {
     return (int32_t)(((int64_t)group * max_query_len + per - 1) / per);
 }
 
+// Multi-query default: the fewest partitions that still give kMultiFill
+// workgroups.  A multi-query workgroup writes a partial row per (query
+// token, head) column, so partials and the merge cost several times what
+// they cost a decode step, and long partitions win as soon as the chip is
+// full: one pass when (sequence, column group, kv head) units alone fill it,
+// else the longest power-of-two partition in [kMinPartition,
+// kMultiMaxPartition] that does (kMinPartition when none does).
+int32_t default_multi_partition(int64_t units, int32_t max_context_len) {
+    if (max_context_len <= kSplitAbove || units >= kMultiFill) return 0;
+    for (int32_t P = kMultiMaxPartition; P >= kMinPartition; P /= 2) {
+        if (P >= max_context_len) continue;         // one partition: a single pass does it without the merge
+        if (units * parts_for(max_context_len, P) >= kMultiFill) return P;
+    }
+    return kMinPartition;
+}
+
 int32_t resolve_multi_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t max_context_len, int32_t max_query_len, int32_t partition_size) {
     if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0 || max_query_len < 1)
         return -1;
-    const int64_t units = (int64_t)num_seqs * multi_col_groups(num_heads / num_kv_heads, max_query_len);
-    const int32_t seqs = units > INT32_MAX ? INT32_MAX : (int32_t)units;
-    return resolve_partition(seqs, num_kv_heads, max_context_len, partition_size);
+    if (partition_size != 0)
+        return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+    if (max_context_len < 0) return -1;
+    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) *
+                          multi_col_groups(num_heads / num_kv_heads, max_query_len) * num_kv_heads;
+    return default_multi_partition(units, max_context_len);
 }
 
 }  // namespace

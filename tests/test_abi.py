@@ -210,8 +210,8 @@ def test_decode_multi_validates(L):
     assert call(qs=None) == pa.PA_ERR_NULL
     assert call(out=None) == pa.PA_ERR_NULL
     assert call(q=FAKE + 2) == pa.PA_ERR_ARG
-    assert call(ws=None) == pa.PA_ERR_WORKSPACE                      # 4096 tokens: split path
-    assert call(wsb=16) == pa.PA_ERR_WORKSPACE
+    assert call(ws=None, part=256) == pa.PA_ERR_WORKSPACE            # split path needs a workspace
+    assert call(wsb=16, part=256) == pa.PA_ERR_WORKSPACE
     assert call(hq=24, hkv=8, d=96) == pa.PA_ERR_UNSUPPORTED
     assert call(hq=30) == pa.PA_ERR_ARG                              # not a multiple of kv heads
     assert call(part=100) == pa.PA_ERR_ARG
@@ -222,15 +222,19 @@ def test_decode_multi_validates(L):
 
 
 def test_decode_multi_partition_policy(L):
-    # columns: G = 4 query heads per kv head x up to 5 tokens = 20 -> one group of two tiles
-    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 5, -1) == 0
-    assert pa.decode_multi_partition_size(64, 32, 8, 512, 5, 0) == 0         # short: one pass
-    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 5, 0) == pa.decode_partition_size(64, 8, 4096, 0)
-    # 4 x 16 tokens = 64 columns -> two column groups count as twice the sequences
-    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 16, 0) == pa.decode_partition_size(128, 8, 4096, 0)
-    assert pa.decode_multi_partition_size(64, 32, 8, 4096, 0, 0) < 0
+    f = pa.decode_multi_partition_size
+    # explicit sizes behave as for pa_decode
+    assert f(64, 32, 8, 4096, 5, -1) == 0 and f(64, 32, 8, 4096, 5, 256) == 256
+    assert f(64, 32, 8, 4096, 5, 100) < 0 and f(64, 32, 8, 4096, 0, 0) < 0
+    # default: one pass once (sequence, column group, kv head) units fill the chip (>= 256)
+    assert f(64, 32, 8, 4096, 5, 0) == 0          # 64 x 1 x 8 = 512 units
+    assert f(64, 32, 8, 512, 5, 0) == 0           # short contexts: one pass
+    assert f(16, 32, 8, 4094, 5, 0) == 2048       # 128 units: two partitions each
+    assert f(4, 32, 8, 8192, 8, 0) == 1024        # 32 units x 8 partitions
+    assert f(8, 32, 8, 32768, 5, 0) == 8192       # long contexts: 64 units x 4
+    assert f(2, 32, 8, 600, 5, 0) == 256          # nothing fills the chip: the shortest partition
+    assert f(16, 32, 8, 4094, 16, 0) == 0         # 4 x 16 = 64 columns: two column groups, 256 units
     # workspace rows are query tokens
-    P = pa.decode_multi_partition_size(64, 32, 8, 4096, 5, 0)
-    want = 320 * 32 * (-(-4096 // P)) * (128 + 2) * 4
-    assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 0) == want
-    assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, -1) == 0
+    want = 320 * 32 * (-(-4096 // 256)) * (128 + 2) * 4
+    assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 256) == want
+    assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 0) == 0
