@@ -216,9 +216,9 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
  * (PA_ERR_ARG).  Pure host arithmetic.  An explicit partition_size (a
  * multiple of 32) is returned as is and -1 gives 0.  The library default
  * (partition_size 0) is a single pass when max_context_len <= 512;
- * otherwise the largest power of two P in [512, 2048] with
- * 8 P <= max_context_len and num_seqs * num_kv_heads * ceil(max_context_len / P)
- * >= 2048 workgroups (512 if none qualifies), lowered to 256 when that
+ * otherwise the largest power of two P in [512, 4096] with
+ * 4 P <= max_context_len and num_seqs * num_kv_heads * ceil(max_context_len / P)
+ * >= 1024 workgroups (512 if none qualifies), lowered to 256 when that
  * leaves fewer than 1024 workgroups.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

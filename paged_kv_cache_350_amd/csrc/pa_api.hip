@@ -14,8 +14,8 @@ namespace {
 
 constexpr int32_t kSplitAbove = 512;         // contexts up to this length run in one pass
 constexpr int32_t kMinPartition = 256;       // library-default partition sizes: powers of two
-constexpr int32_t kMaxPartition = 2048;      // in [kMinPartition, kMaxPartition]
-constexpr int64_t kFillUnits = 2048;         // workgroups that keep 256 CUs busy for several rounds
+constexpr int32_t kMaxPartition = 4096;      // in [kMinPartition, kMaxPartition]
+constexpr int64_t kFillUnits = 1024;         // workgroups that keep 256 CUs busy (4 resident each)
 constexpr int64_t kMinUnits = 1024;          // below this, fall back to the smallest partition
 constexpr int32_t kChunk = 32;               // partitions are whole 32-token chunks
 constexpr int32_t kMaxGroup = 16;            // query heads per kv head
@@ -41,7 +41,7 @@ int32_t parts_for(int32_t max_context_len, int32_t partition) {
     return (int32_t)(((int64_t)max_context_len + partition - 1) / partition);
 }
 
-// Library default: the longest partition that still leaves at least 8
+// Library default: the longest partition that still leaves at least 4
 // partitions in the longest context and kFillUnits (sequence, kv head,
 // partition) workgroups; longer partitions mean fewer partials to write and
 // merge and less per-workgroup set-up, shorter ones better balance over
@@ -51,7 +51,7 @@ int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_co
     const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
     auto units = [&](int32_t P) { return pairs * parts_for(max_context_len, P); };
     int32_t P = kMaxPartition;
-    while (P > kSplitAbove && ((int64_t)P * 8 > max_context_len || units(P) < kFillUnits)) P /= 2;
+    while (P > kSplitAbove && ((int64_t)P * 4 > max_context_len || units(P) < kFillUnits)) P /= 2;
     if (units(P) < kMinUnits) P = kMinPartition;
     return P;
 }

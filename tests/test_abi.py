@@ -62,18 +62,18 @@ def test_partition_policy_and_workspace_size(L):
     assert pa.decode_partition_size(64, 8, -1, 0) < 0
     # library default, worked through the rule in pa.h:
     assert pa.decode_partition_size(64, 8, 512, 0) == 0          # short: single pass
-    assert pa.decode_partition_size(64, 8, 4027, 0) == 512       # 8B-shaped batch
-    assert pa.decode_partition_size(256, 8, 8192, 0) == 1024     # 70B-shaped batch
-    assert pa.decode_partition_size(8, 8, 32768, 0) == 1024      # long context: 2048 gives 1024 units
-    assert pa.decode_partition_size(100, 8, 10512, 0) == 1024    # prefix sharing
-    assert pa.decode_partition_size(8, 8, 32774, 0) == 1024      # beams
-    assert pa.decode_partition_size(512, 8, 32768, 0) == 2048    # plenty of work
+    assert pa.decode_partition_size(64, 8, 4027, 0) == 512       # 8B-shaped batch: 4 partitions per long context
+    assert pa.decode_partition_size(256, 8, 8192, 0) == 2048     # 70B-shaped batch
+    assert pa.decode_partition_size(8, 8, 32768, 0) == 2048      # long context: 4096 gives only 512 units
+    assert pa.decode_partition_size(100, 8, 10512, 0) == 2048    # prefix sharing
+    assert pa.decode_partition_size(8, 8, 32774, 0) == 2048      # beams
+    assert pa.decode_partition_size(512, 8, 32768, 0) == 4096    # plenty of work
     assert pa.decode_partition_size(1, 8, 32768, 0) == 256       # one sequence: parallelism first
     assert pa.decode_partition_size(2, 1, 600, 0) == 256
     # workspace = seqs x heads x parts x (D + 2) floats
     assert pa.decode_workspace_size(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 64 * 32 * 8 * 130 * 4
-    assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0) == 256 * 64 * 8 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 64 * 32 * 4 * 130 * 4   # P = 1024 at 4,096
+    assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0) == 256 * 64 * 4 * 130 * 4
     assert pa.decode_workspace_size(64, 32, 8, 128, 500, 0) == 0
     assert pa.decode_workspace_size(64, 32, 8, 128, 4096, -1) == 0
     assert pa.decode_workspace_size(3, 4, 4, 64, 33, 32) == 3 * 4 * 2 * 66 * 4
