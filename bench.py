@@ -219,6 +219,8 @@ def blockmgr_bench(a) -> int:
     def run(mgr, native):
         for b, L in zip(seqs, lens):
             mgr.allocate(b, L)
+        page_lists = mgr.tables if hasattr(mgr, "lengths") else getattr(mgr, "pages", None)
+        lengths = mgr.lengths if hasattr(mgr, "lengths") else getattr(mgr, "length", None)
         if native:
             ids = np.asarray(seqs, dtype=np.int64)
             tables, ctx = mgr.block_tables(ids, maxb, pad_page=0)
@@ -230,18 +232,24 @@ def blockmgr_bench(a) -> int:
                 slots = np.array([mgr.append_token(b) for b in seqs], dtype=np.int64)
                 tables = np.zeros((len(seqs), maxb), dtype=np.int32)
                 for i, b in enumerate(seqs):
-                    pg = mgr.tables[b]
+                    pg = page_lists[b]
                     tables[i, :len(pg)] = pg
-                ctx = np.array([mgr.lengths[b] for b in seqs], dtype=np.int32)
+                ctx = np.array([lengths[b] for b in seqs], dtype=np.int32)
         return (time.perf_counter() - t0) / steps * 1e6, tables, ctx, slots
 
+    from oracle.prefix_cache import PrefixCachingPool
     nat_us, t_n, c_n, s_n = run(pa.NativeBlockManager(nb, w.block_size, free_order=order), True)
     py_us, t_p, c_p, s_p = run(W.BlockManager(nb, w.block_size, free_order=order), False)
-    same = bool(np.array_equal(t_n, t_p) and np.array_equal(c_n, c_p) and np.array_equal(s_n, s_p))
+    or_us, t_o, c_o, s_o = run(PrefixCachingPool(nb, w.block_size, free_order=order.tolist()), False)
+    same = bool(np.array_equal(t_n, t_p) and np.array_equal(c_n, c_p) and np.array_equal(s_n, s_p) and
+                np.array_equal(t_n, t_o) and np.array_equal(c_n, c_o) and np.array_equal(s_n, s_o))
     print(json.dumps({"mode": "blockmgr", "workload": w.name, "num_seqs": w.num_seqs, "steps": steps,
                       "native_us_per_step": round(nat_us, 2), "host_python_us_per_step": round(py_us, 2),
                       "speedup": round(py_us / nat_us, 1), "identical_tables_slots": same,
-                      "pool_pages": nb, "max_blocks_per_seq": maxb}), flush=True)
+                      "pool_pages": nb, "max_blocks_per_seq": maxb,
+                      "cpu_baseline": {"value": round(or_us, 2), "unit": "us/step", "cores": 1, "kind": "oracle",
+                                       "sample": f"{steps} steps of the same bookkeeping by the oracle's "
+                                                 f"plain page pool (oracle/prefix_cache.py)"}}), flush=True)
     return 0 if same else 1
 
 
