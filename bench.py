@@ -364,10 +364,12 @@ def prefix_bench(a) -> int:
 
 
 def multi_bench(a, torch, pa, W) -> int:
-    """Multi-query step on the speculative-verification batch: append every
-    sequence's new tokens (pa_kv_append), then pa_decode_multi (partition and
-    merge kernels).  The roofline figure uses the whole pa_decode_multi call
-    (both kernels) as the launch; the rocprofv3 summary splits the two."""
+    """Multi-query step on the speculative-verification batch: every
+    sequence's new tokens appended and attended to -- in one launch
+    (pa_decode_multi_append, --step fused, the default) or as pa_kv_append
+    then pa_decode_multi (--step separate).  The roofline figure uses the
+    whole pa_decode_multi call as the launch (one kernel in one pass; with a
+    split the merge kernel too, which the rocprofv3 summary separates)."""
     import oracle
     w = W.spec_verify()
     t = W.make_tensors(w, "cuda")
@@ -382,15 +384,19 @@ def multi_bench(a, torch, pa, W) -> int:
     out = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream()
 
+    fused = a.step == "fused"
+    app = dict(k_new=t["k_new"], v_new=t["v_new"]) if fused else {}
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+        if not fused:
+            pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
         if ev is not None:
             ev[1].record(stream)
         pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                         t["query_start"], w.scale, w.max_context_len, w.max_query_len, out=out,
-                        partition_size=P if P > 0 else -1, workspace=ws, reuse=reuse)
+                        partition_size=P if P > 0 else -1, workspace=ws, reuse=reuse, **app)
         if ev is not None:
             ev[2].record(stream)
 
@@ -445,8 +451,8 @@ def multi_bench(a, torch, pa, W) -> int:
         "config": {"workload": w.name, "description": w.description, "num_seqs": w.num_seqs,
                    "query_tokens": T, "max_query_len": w.max_query_len,
                    "sum_context_tokens": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
-                   "partition_size": P, "reuse": reuse, "kv_bytes_per_step": kv_bytes},
-        "kernels_avg_us": {"kv_append": round(append_ms * 1e3, 2),
+                   "partition_size": P, "reuse": reuse, "kv_bytes_per_step": kv_bytes, "step": a.step},
+        "kernels_avg_us": {"kv_append": None if fused else round(append_ms * 1e3, 2),
                            kname: round(multi_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -332,6 +332,28 @@ pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cach
                           int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
                           pa_kv_reuse reuse, void* workspace, size_t workspace_bytes);
 
+/*
+ * pa_decode_multi_append -- the step's append and pa_decode_multi in one
+ * launch (no separate pa_kv_append).  k_new, v_new (device,
+ * [num_tokens][num_kv_heads][head_dim] bf16, 16-byte aligned, read) are the
+ * new tokens' K and V rows, row for row aligned with q: row
+ * query_start[b] + j goes to position L_b - n_b + j of sequence b, i.e. to
+ * page block_tables[b][pos / block_size] at offset pos % block_size, which
+ * must already be the sequence's own page (allocated, copied on write).  A
+ * page id outside [0, num_blocks) writes nothing there.  Every other
+ * argument, the result and the status codes are those of pa_decode_multi
+ * (PA_ERR_NULL also for a missing k_new / v_new); outputs and caches equal
+ * pa_kv_append of the same rows followed by pa_decode_multi, bit for bit.
+ */
+pa_status pa_decode_multi_append(const void* k_new, const void* v_new, const void* q, void* k_cache,
+                                 void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                                 float scale, void* out, hipStream_t stream, int32_t num_seqs,
+                                 int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
+                                 int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                                 pa_kv_reuse reuse, void* workspace, size_t workspace_bytes);
+
 /* Partition size pa_decode_multi uses for these sizes (0 = single pass,
  * -1 = invalid request); partition_size as for pa_decode. */
 int32_t pa_decode_multi_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -61,6 +61,9 @@ _SIGNATURES = {
     "pa_decode_multi": ([_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_float, _vp, _vp,
                          _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
                          _c_int, _c_int, _vp, _c_size], _c_int),
+    "pa_decode_multi_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_float, _vp,
+                                _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                                _c_int, _c_int, _vp, _c_size], _c_int),
     "pa_decode_multi_partition_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_int),
     "pa_decode_multi_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                                        _c_size),
@@ -327,10 +330,13 @@ def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
                  scale: float, max_context_len: int, max_query_len: int,
                  out: Optional[torch.Tensor] = None, partition_size: int = 0,
-                 workspace: Optional[torch.Tensor] = None, reuse: str = "auto") -> torch.Tensor:
-    """Attention for several new tokens per sequence (already appended):
-    q [T, Hq, D] packed by sequence, query_start [B + 1] int32; row
-    query_start[b] + j attends causally over positions 0 .. L_b - n_b + j.
+                 workspace: Optional[torch.Tensor] = None, reuse: str = "auto",
+                 k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention for several new tokens per sequence: q [T, Hq, D] packed by
+    sequence, query_start [B + 1] int32; row query_start[b] + j attends
+    causally over positions 0 .. L_b - n_b + j.  Without k_new / v_new the
+    new tokens' rows must already be in the caches; with them ([T, Hkv, D],
+    aligned with q) the same launch appends them (pa_decode_multi_append).
     Returns out [T, Hq, D]."""
     nb, hkv, d, bs = _cache_dims(k_cache, v_cache)
     _dev_tensor("q", q, dtype=k_cache.dtype, ndim=3)
@@ -353,12 +359,18 @@ def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device) if n else None
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().pa_decode_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                               block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
-                               bs, hkv, float(scale), out.data_ptr(), _stream(q), B, T, hq, d,
-                               block_tables.shape[1], int(max_context_len), int(max_query_len), nb,
-                               _elem_dtype(q), int(partition_size), REUSE[reuse], ws_ptr, ws_bytes)
-    _check("pa_decode_multi", st)
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            context_lens.data_ptr(), query_start.data_ptr(), bs, hkv, float(scale), out.data_ptr(), _stream(q),
+            B, T, hq, d, block_tables.shape[1], int(max_context_len), int(max_query_len), nb, _elem_dtype(q),
+            int(partition_size), REUSE[reuse], ws_ptr, ws_bytes)
+    if k_new is None and v_new is None:
+        _check("pa_decode_multi", lib().pa_decode_multi(*args))
+        return out
+    _dev_tensor("k_new", k_new, dtype=q.dtype, ndim=3)
+    _dev_tensor("v_new", v_new, dtype=q.dtype, ndim=3)
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError("k_new / v_new must be [num_tokens, num_kv_heads, head_dim], aligned with q")
+    _check("pa_decode_multi_append", lib().pa_decode_multi_append(k_new.data_ptr(), v_new.data_ptr(), *args))
     return out
 
 

@@ -167,13 +167,14 @@ void decode_mfma_kernel(DecodeParams p) {
     // every wave of the workgroup, which then reads the new token like any
     // other.  No other workgroup reads that page: without sharing it belongs
     // to this (sequence, kv head) alone, and a sequence only appends into a
-    // page it owns (copy-on-write happens before).
+    // page it owns (copy-on-write happens before).  A page id outside the
+    // pool writes nothing, as pa_kv_append skips an out-of-range slot.
     const bool appends = p.k_new != nullptr && end == L &&    // workgroup-uniform
-                         (p.append_mask == nullptr || p.append_mask[b] >= 0);
+                         (p.append_mask == nullptr || p.append_mask[b] >= 0) &&
+                         (uint32_t)row[(L - 1) / BS] < (uint64_t)p.num_blocks;
     if (appends) {
         const int pos = L - 1;
-        const int pg_raw = row[pos / BS];
-        const int pg = (uint32_t)pg_raw >= (uint64_t)p.num_blocks ? 0 : pg_raw;
+        const int pg = row[pos / BS];
         const int off = pos % BS;
         const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
         const size_t src = ((size_t)b * kv_heads + g) * D;

@@ -145,6 +145,41 @@ void decode_multi_kernel(DecodeParams p) {
         for (int dc = 0; dc < DC; ++dc) acc[nt][dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Fused append (pa_decode_multi_append): new token j's K and V rows (row
+    // row0 + j of k_new / v_new, aligned with q) belong at position
+    // L - n + j.  Every workgroup stores the new rows that fall inside the
+    // positions it reads, before the first barrier below, which makes them
+    // visible to all its waves; so whoever reads a new row has written it
+    // itself.  Column groups of one (sequence, kv head) store the same bytes,
+    // which cannot change what either reads.  A page id outside the pool
+    // writes nothing.
+    if (p.k_new != nullptr) {
+        const int first_new = max(start, L - n);
+        const int count = end - first_new;                   // may be <= 0
+        const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new);
+        const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new);
+        uint16_t* kw = const_cast<uint16_t*>(kc);
+        uint16_t* vw = const_cast<uint16_t*>(vc);
+        for (int e = tid; e < count * (D / 8); e += kThreads) {          // K: 16-byte chunks
+            const int pos = first_new + e / (D / 8);
+            const int c = e % (D / 8);
+            const int pg = row[pos / BS];
+            if ((uint32_t)pg >= (uint64_t)p.num_blocks) continue;
+            const size_t src = ((size_t)(qr.row0 + pos - (L - n)) * kv_heads + g) * D;
+            const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
+            st16(kw + tile + ((size_t)c * BS + pos % BS) * 8, ld16(kn + src + 8 * c));
+        }
+        for (int e = tid; e < count * D; e += kThreads) {                // V: one element per dim
+            const int pos = first_new + e / D;
+            const int d = e % D;
+            const int pg = row[pos / BS];
+            if ((uint32_t)pg >= (uint64_t)p.num_blocks) continue;
+            const size_t src = ((size_t)(qr.row0 + pos - (L - n)) * kv_heads + g) * D;
+            const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
+            vw[tile + (size_t)d * BS + pos % BS] = vn[src + d];
+        }
+    }
+
     const int nchunks = (end - start + kChunk - 1) / kChunk;
     const int blk_first = start / BS;
     const int blk_end = (end + BS - 1) / BS;

@@ -112,15 +112,16 @@ void decode_valu_kernel(DecodeParams p) {
     // L - 1 first stores kv head g's new K and V rows into that slot; the
     // barrier after the query staging below makes the stores visible to the
     // whole workgroup, which then reads the new token like any other.  No
-    // other workgroup reads that page (see the matrix-core kernel).
+    // other workgroup reads that page (see the matrix-core kernel).  A page
+    // id outside the pool writes nothing.
+    const int* trow = p.block_tables + (size_t)b * p.max_blocks_per_seq;
     const bool appends = p.k_new != nullptr && end == L &&    // workgroup-uniform
-                         (p.append_mask == nullptr || p.append_mask[b] >= 0);
+                         (p.append_mask == nullptr || p.append_mask[b] >= 0) &&
+                         (uint32_t)trow[(L - 1) / BS] < (uint64_t)p.num_blocks;
     if (appends) {
         constexpr int NCH = D * (int)sizeof(E) / 16;        // 16-byte chunks per K row
-        const int* trow = p.block_tables + (size_t)b * p.max_blocks_per_seq;
         const int pos = L - 1;
-        const int pg_raw = trow[pos / BS];
-        const int pg = (uint32_t)pg_raw >= (uint64_t)p.num_blocks ? 0 : pg_raw;
+        const int pg = trow[pos / BS];
         const int off = pos % BS;
         const size_t tile = ((size_t)pg * p.num_kv_heads + g) * (size_t)D * BS;
         const size_t src = ((size_t)b * p.num_kv_heads + g) * D;

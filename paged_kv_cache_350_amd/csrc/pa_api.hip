@@ -432,14 +432,18 @@ size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_tokens, int3
     return workspace_bytes_for(num_tokens, num_heads, head_dim, max_context_len, partition);
 }
 
-pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_tables, const int32_t* context_lens,
-                          const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
-                          float scale, void* out, hipStream_t stream, int32_t num_seqs,
-                          int32_t num_tokens, int32_t num_heads, int32_t head_dim,
-                          int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
-                          int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
-                          pa_kv_reuse reuse, void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                            float scale, void* out, hipStream_t stream, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
+                            int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                            pa_kv_reuse reuse, void* workspace, size_t workspace_bytes) {
     if (!valid_dtype(dtype)) return PA_ERR_ARG;
     if (reuse != PA_KV_AUTO && reuse != PA_KV_STREAM && reuse != PA_KV_SHARED) return PA_ERR_ARG;
     pa_status st = shape_status(num_kv_heads, head_dim, block_size);
@@ -461,6 +465,8 @@ pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cach
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
         return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ARG;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
 
     const int32_t group = num_heads / num_kv_heads;
     const int32_t tiles = multi_col_tiles(group, max_query_len);
@@ -498,6 +504,8 @@ pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cach
     p.num_tokens = num_tokens;
     p.max_query_len = max_query_len;
     p.col_groups = col_groups;
+    p.k_new = k_new;
+    p.v_new = v_new;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -525,6 +533,39 @@ pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cach
     r.num_groups = num_seqs;
     r.max_query_len = max_query_len;
     return hip_status(pa_impl::launch_decode_reduce(r, dtype, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                          float scale, void* out, hipStream_t stream, int32_t num_seqs,
+                          int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
+                          int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                          pa_kv_reuse reuse, void* workspace, size_t workspace_bytes) {
+    return decode_multi_impl(nullptr, nullptr, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                             block_size, num_kv_heads, scale, out, stream, num_seqs, num_tokens, num_heads,
+                             head_dim, max_blocks_per_seq, max_context_len, max_query_len, num_blocks, dtype,
+                             partition_size, reuse, workspace, workspace_bytes);
+}
+
+pa_status pa_decode_multi_append(const void* k_new, const void* v_new, const void* q, void* k_cache,
+                                 void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                                 float scale, void* out, hipStream_t stream, int32_t num_seqs,
+                                 int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len, int32_t max_query_len,
+                                 int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                                 pa_kv_reuse reuse, void* workspace, size_t workspace_bytes) {
+    if (num_seqs > 0 && num_tokens > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
+    return decode_multi_impl(k_new, v_new, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                             block_size, num_kv_heads, scale, out, stream, num_seqs, num_tokens, num_heads,
+                             head_dim, max_blocks_per_seq, max_context_len, max_query_len, num_blocks, dtype,
+                             partition_size, reuse, workspace, workspace_bytes);
 }
 
 }  // extern "C"

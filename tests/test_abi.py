@@ -238,3 +238,17 @@ def test_decode_multi_partition_policy(L):
     want = 320 * 32 * (-(-4096 // 256)) * (128 + 2) * 4
     assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 256) == want
     assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 0) == 0
+
+
+def test_decode_multi_append_validates(L):
+    def call(kn=FAKE, vn=FAKE, **kw):
+        a = dict(q=FAKE, B=4, T=20, maxq=5, part=0)
+        a.update(kw)
+        return L.pa_decode_multi_append(kn, vn, a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 0.1, FAKE, None,
+                                        a["B"], a["T"], 32, 128, 256, 4096, a["maxq"], 100000, 1, a["part"], 0,
+                                        FAKE, 1 << 30)
+    assert call(kn=None) == pa.PA_ERR_NULL
+    assert call(vn=None) == pa.PA_ERR_NULL
+    assert call(kn=FAKE + 2) == pa.PA_ERR_ARG
+    assert call(kn=None, vn=None, B=0) == pa.PA_OK          # nothing to do
+    assert call(maxq=0) == pa.PA_ERR_ARG

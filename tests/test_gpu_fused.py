@@ -179,3 +179,26 @@ def test_fused_named_workload_full_size(name):
     ref = oracle_decode(w, t, seqs)
     stats = check_close(out_f64(out)[seqs], ref, w.dtype, f"fused {name}")
     say("  ", stats)
+
+
+def test_fused_append_skips_a_page_outside_the_pool():
+    """pa_decode_append with a block-table entry outside the pool at a
+    sequence's newest position writes nothing for that sequence (the clamped
+    page 0 stays as it was); every other newest row lands as the oracle puts
+    it."""
+    pa = require_gpu()
+    w = W.custom("bad_page", 18, "bf16", [40, 70, 20, 33], 32, 8, 128, 16)
+    t = W.make_tensors(w, "cuda")
+    k_new, v_new, mask, older = newest_rows(w, t)
+    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
+    tables = w.block_tables.copy()
+    bad = 1
+    tables[bad, (int(w.context_lens[bad]) - 1) // 16] = w.num_blocks + 7
+    say("decode_append, page outside the pool")
+    pa.decode_append(k_new, v_new, t["q"], t["k_cache"], t["v_cache"], torch.from_numpy(tables).cuda(),
+                     t["context_lens"], w.scale, w.max_context_len, partition_size=-1)
+    torch.cuda.synchronize()
+    keep = np.arange(w.num_seqs) != bad
+    rk, rv = oracle.kv_append(storage_np(k_new)[keep], storage_np(v_new)[keep], mask[keep], kc0, vc0, 16)
+    assert np.array_equal(storage_np(t["k_cache"]).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(storage_np(t["v_cache"]).view(np.uint16), rv.view(np.uint16))

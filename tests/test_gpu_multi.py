@@ -148,3 +148,51 @@ def test_spec_verify_full_size_sampled():
     ref = oracle_multi(w, kc0, vc0, q, seqs=seqs)
     rows = np.concatenate([np.arange(w.query_start[b], w.query_start[b + 1]) for b in seqs])
     check_close(out_f64(out)[rows], ref[rows], "bf16", "spec_verify sampled")
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 8, 128), (32, 8, 2, 64), (16, 16, 1, 64)],
+                         ids=lambda s: "-".join(map(str, s)))
+def test_fused_append_equals_append_then_multi(shape):
+    """pa_decode_multi_append = pa_kv_append + pa_decode_multi, bit for bit
+    (outputs and whole caches, NaN poison included), and within tolerance of
+    the oracle; new tokens straddle pages, partitions and column groups."""
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    w = W.multi_custom("fused_multi", 46, LENS, NEWS, hq, hkv, d, bs)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    for P in (-1, 0, 64):
+        a = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        b = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("fused multi append", shape, "partition", P)
+        out_a = run_gpu(pa, w, a, partition_size=P)
+        out_b = pa.decode_multi(b["q"], b["k_cache"], b["v_cache"], b["block_tables"], b["context_lens"],
+                                b["query_start"], w.scale, w.max_context_len, w.max_query_len, partition_size=P,
+                                k_new=b["k_new"], v_new=b["v_new"])
+        torch.cuda.synchronize()
+        assert bits_equal(out_a, out_b), P
+        assert bits_equal(a["k_cache"], b["k_cache"]) and bits_equal(a["v_cache"], b["v_cache"]), P
+        check_close(out_f64(out_b), ref, "bf16", f"fused {shape} P={P}")
+
+
+def test_fused_append_skips_pages_outside_the_pool():
+    """A block-table entry outside the pool at a new token's position: that
+    row is not written anywhere (as pa_kv_append skips an out-of-range slot);
+    every other new row lands where the oracle puts it."""
+    pa = require_gpu()
+    w = W.multi_custom("bad_page", 47, [40, 70, 20], [5, 3, 4], 32, 8, 128, 16)
+    t, kc0, vc0, q = prepare(w)
+    bad_seq, bad_pos = 1, 69                       # the last new token of sequence 1
+    tables = w.block_tables.copy()
+    tables[bad_seq, bad_pos // 16] = w.num_blocks + 3
+    bt = torch.from_numpy(tables).cuda()
+    say("fused multi append, page outside the pool")
+    pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], t["query_start"], w.scale,
+                    w.max_context_len, w.max_query_len, partition_size=-1, k_new=t["k_new"], v_new=t["v_new"])
+    torch.cuda.synchronize()
+    slots = w.append_slots.copy()
+    page_of_bad = w.block_tables[bad_seq, bad_pos // 16]
+    keep = (slots // 16) != page_of_bad           # every row of the page the bad entry stood for
+    kc, vc = oracle.kv_append(w._k_new[keep], w._v_new[keep], slots[keep], kc0, vc0, 16)
+    assert np.array_equal(storage_np(t["k_cache"]).view(np.uint16), kc.view(np.uint16))
+    assert np.array_equal(storage_np(t["v_cache"]).view(np.uint16), vc.view(np.uint16))
