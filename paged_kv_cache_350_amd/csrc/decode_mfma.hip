@@ -269,8 +269,8 @@ void decode_mfma_kernel(DecodeParams p) {
             }
             float mx = sc[0];
             for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_xor16(mx);
+            mx = max_xor32(mx);
             // Lazy rescaling: the reference max moves only when a score exceeds it
             // by more than kRescaleSlack (always on the first chunk, m_run = -inf).
             // Between moves the weights are 2^(s - m_run) <= 2^kRescaleSlack; acc
@@ -308,8 +308,8 @@ void decode_mfma_kernel(DecodeParams p) {
     }
 
     // ---- merge the four waves; lane (hl, j) holds dims 16 dc + 4 j + i of head hl
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_xor16(l_run);
+    l_run = sum_xor32(l_run);
     if (lane < 16) {
         sm_m[w * 16 + hl] = m_run;
         sm_l[w * 16 + hl] = l_run;

@@ -246,8 +246,8 @@ void decode_multi_kernel(DecodeParams p) {
                 }
                 float mx = sc[0];
                 for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = max_xor16(mx);
+                mx = max_xor32(mx);
                 const bool grow = mx > m_run[nt] + kRescaleSlack;
                 if (__builtin_amdgcn_ballot_w64(grow) != 0) {
                     const float mn = grow ? mx : m_run[nt];
@@ -289,8 +289,8 @@ void decode_multi_kernel(DecodeParams p) {
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     for (int nt = 0; nt < NT; ++nt) {
         float l = l_run[nt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        l = sum_xor16(l);
+        l = sum_xor32(l);
         if (nt > 0) __syncthreads();              // the previous tile's reads are done
         if (lane < 16) {
             sm_m[w * 16 + hl] = m_run[nt];

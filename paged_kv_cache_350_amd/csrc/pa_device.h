@@ -42,6 +42,32 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Cross-lane reductions over lane pairs (l, l ^ 16) and (l, l ^ 32) of a
+// wave without LDS: v_permlane16_swap / v_permlane32_swap (gfx950) leave each
+// lane holding {x[l], x[l ^ k]} in its two results (order depending on the
+// lane), so a commutative operation on the two is exactly the reduction a
+// __shfl_xor would give, with no LDS round trip.
+__device__ __forceinline__ float max_xor16(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(u32_as_f32(r[0]), u32_as_f32(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(u32_as_f32(r[0]), u32_as_f32(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return u32_as_f32(r[0]) + u32_as_f32(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return u32_as_f32(r[0]) + u32_as_f32(r[1]);
+}
+
 // 16-byte global load/store through a plain vector type.
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
