@@ -20,7 +20,9 @@ def test_append_matches_elementwise_writes_and_keeps_bits():
     kc[3, :, :, 7, :] = np.float32(np.nan)       # a NaN payload elsewhere must survive
     kn = rng.standard_normal((4, hkv, d)).astype(np.float32)
     vn = rng.standard_normal((4, hkv, d)).astype(np.float32)
-    slots = np.array([2 * bs + 5, -1, 0, nb * bs - 1], np.int64)
+    # the padding slot -1 would wrap to the pool's very last slot: keep that
+    # slot unwritten, so a write through a negative slot shows
+    slots = np.array([2 * bs + 5, -1, 0, nb * bs - 2], np.int64)
     k2, v2 = oracle.kv_append(kn, vn, slots, kc, vc, bs)
     want_k, want_v = kc.copy(), vc.copy()
     for i, s in enumerate(slots):
