@@ -202,4 +202,35 @@ def pin_page_permutation(oracle):
     assert np.array_equal(base, far)
 
 
-ALL_PINS = [pin_brute_force, pin_library_sdpa, pin_closed_forms, pin_page_permutation]
+def pin_batch_rows(oracle):
+    """Several sequences of different lengths in one pool and one call: row b
+    is the brute force over sequence b's own contiguous tensor (so each row
+    reads its own table row and length)."""
+    rng = np.random.default_rng(15)
+    lens, hq, hkv, d, bs, x = [23, 5, 40, 17], 4, 2, 8, 16, 4
+    npg = [-(-L // bs) for L in lens]
+    nb = sum(npg) + 1
+    perm = [int(p) for p in rng.permutation(nb)]
+    kc = np.full((nb, hkv, d // x, bs, x), np.nan, dtype=np.float32)
+    vc = np.full((nb, hkv, d, bs), np.nan, dtype=np.float32)
+    tables = np.full((len(lens), max(npg)), perm[-1], dtype=np.int32)
+    seqs, at = [], 0
+    for b, L in enumerate(lens):
+        K, V = _f32(rng, L, hkv, d), _f32(rng, L, hkv, d)
+        pages = perm[at:at + npg[b]]
+        at += npg[b]
+        tables[b, :npg[b]] = pages
+        k1, v1 = contiguous_to_paged(K, V, pages, bs, nb, x)
+        for p in pages:
+            kc[p], vc[p] = k1[p], v1[p]
+        seqs.append((K, V))
+    q = _f32(rng, len(lens), hq, d)
+    scale = float(np.float32(0.3))
+    got = oracle.decode(q, kc, vc, tables, np.array(lens, np.int32), scale, bs, "f32")
+    for b, (K, V) in enumerate(seqs):
+        want = np.array(brute_attention(q[b].astype(np.float64).tolist(), K.astype(np.float64).tolist(),
+                                        V.astype(np.float64).tolist(), scale, hq // hkv))
+        assert np.allclose(got[b], want, rtol=0, atol=1e-12), b
+
+
+ALL_PINS = [pin_brute_force, pin_library_sdpa, pin_closed_forms, pin_page_permutation, pin_batch_rows]

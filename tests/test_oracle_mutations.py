@@ -71,7 +71,33 @@ def _gather_factory(kind):
     return gather
 
 
+def _attend_default_scale(qvec, K, V, scale):
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1])
+    s = (K @ qvec) / math.sqrt(K.shape[1])           # the given scale ignored
+    p = np.exp(s - s.max())
+    return (p @ V) / p.sum()
+
+
+_real_gather = pa.gather_sequence
+
+
+def _gather_drops_newest(k_cache, v_cache, table_row, context_len, block_size, dtype):
+    return _real_gather(k_cache, v_cache, table_row, max(int(context_len) - 1, 0), block_size, dtype)
+
+
+_real_decode = pa.decode
+
+
+def _decode_wrong_row(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, dtype, seqs=None):
+    tables = np.roll(np.asarray(block_tables), 1, axis=0)        # sequence b reads b - 1's table
+    return _real_decode(q, k_cache, v_cache, tables, context_lens, scale, block_size, dtype, seqs)
+
+
 MUTANTS = {
+    "given_scale_ignored": ("attend", _attend_default_scale),
+    "newest_token_dropped": ("gather_sequence", _gather_drops_newest),
+    "neighbouring_table_row": ("decode", _decode_wrong_row),
     "scale_dropped": ("attend", _attend_no_scale),
     "softmax_sign": ("attend", _attend_wrong_sign),
     "no_normalisation": ("attend", _attend_no_normalise),
@@ -90,6 +116,8 @@ MUTANTS = {
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(pa, attr, fn)
+    if hasattr(oracle, attr):                 # the pins call the package-level name
+        monkeypatch.setattr(oracle, attr, fn)
     caught = []
     for pin in ALL_PINS:
         try:
