@@ -89,6 +89,56 @@ def sub_pool(w, t, seqs, k_cache=None, v_cache=None):
 
 
 def oracle_decode(w, t, seqs, k_cache=None, v_cache=None):
+    """Oracle decode of ``seqs`` over caches taken as they stand: only for
+    caches the library has not written (as generated, or uploaded from the
+    host)."""
     kc, vc, tables, lens = sub_pool(w, t, seqs, k_cache, v_cache)
     q = storage_np(t["q"])[list(seqs)]
     return oracle.decode(q, kc, vc, tables, lens, w.scale, w.block_size, w.dtype)
+
+
+def run_step_updates(pa, w, t):
+    """Apply the step's copy-on-write copies and appends on the GPU."""
+    if len(w.copy_pairs):
+        pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
+    if len(w.append_slots):
+        pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+
+
+def reference_after_step(w, t, seqs):
+    """The float64 oracle decode of ``seqs`` after the step's copy-on-write
+    copies and appends, computed on the host before the device runs them.
+    The pages those sequences read (plus the sources copied into them) are
+    taken as generated; the oracle applies its own copy_blocks and kv_append
+    of the same pairs and rows, renumbered into that sub-pool, so nothing
+    the library writes reaches the oracle."""
+    seqs = list(seqs)
+    bs = w.block_size
+    read = set()
+    for b in seqs:
+        n = -(-int(w.context_lens[b]) // bs)
+        read.update(int(p) for p in w.block_tables[b, :n])
+    pairs = [(int(s), int(d)) for s, d in w.copy_pairs.reshape(-1, 2) if int(d) in read]
+    pages = sorted(read | {s for s, _ in pairs}) or [0]
+    where = {p: i for i, p in enumerate(pages)}
+    idx = torch.tensor(pages, dtype=torch.long, device=t["k_cache"].device)
+    kc = storage_np(t["k_cache"].index_select(0, idx))
+    vc = storage_np(t["v_cache"].index_select(0, idx))
+    kc, vc = oracle.copy_blocks(kc, vc, np.array([[where[s], where[d]] for s, d in pairs], np.int64).reshape(-1, 2))
+    slots = np.asarray(w.append_slots, dtype=np.int64)
+    keep = np.array([s >= 0 and int(s) // bs in read for s in slots], dtype=bool)
+    sub = np.array([where[int(s) // bs] * bs + int(s) % bs for s in slots[keep]], dtype=np.int64)
+    kc, vc = oracle.kv_append(storage_np(t["k_new"])[keep], storage_np(t["v_new"])[keep], sub, kc, vc, bs)
+    tables = np.zeros((len(seqs), w.block_tables.shape[1]), dtype=np.int32)
+    for i, b in enumerate(seqs):
+        n = -(-int(w.context_lens[b]) // bs)
+        tables[i, :n] = [where[int(p)] for p in w.block_tables[b, :n]]
+    q = storage_np(t["q"])[seqs]
+    return oracle.decode(q, kc, vc, tables, w.context_lens[seqs], w.scale, bs, w.dtype)
+
+
+def step_and_reference(pa, w, t, seqs):
+    """reference_after_step, then the step's copies and appends on the GPU."""
+    ref = reference_after_step(w, t, seqs)
+    run_step_updates(pa, w, t)
+    return ref

@@ -4,10 +4,13 @@ Six sequences fork one 40-token prompt (its last page is shared and partly
 filled, so their first appends copy-on-write) and four more run on their own.
 Every step the manager appends a token to each sequence and keeps the block
 tables current in place; its copy pairs go to pa_copy_blocks, the new rows to
-pa_decode_append (or pa_kv_append + pa_decode on alternate steps).  A host
-mirror of the caches is updated with the oracle's copy and append; each
-step's output is checked against the oracle decode and the caches bit for bit
-at the end."""
+pa_decode_append (or pa_kv_append + pa_decode on alternate steps).
+
+The oracle's page pool runs the same calls in lockstep: the manager's slots
+and copy pairs must equal the pool's, and the oracle decode takes the pool's
+own block tables and lengths.  A host mirror of the caches is updated with
+the oracle's copy and append; each step's output is checked against the
+oracle decode and the caches bit for bit at the end."""
 
 import numpy as np
 import pytest
@@ -24,7 +27,9 @@ def test_decode_loop_driven_by_native_manager():
     pa = require_gpu()
     bs, hq, hkv, d, nb, maxb, steps = 16, 32, 8, 128, 300, 10, 14
     rng = np.random.default_rng(31)
-    m = pa.NativeBlockManager(nb, bs, free_order=rng.permutation(nb))
+    order = rng.permutation(nb)
+    m = pa.NativeBlockManager(nb, bs, free_order=order)
+    pool = oracle.PrefixCachingPool(nb, bs, free_order=order.tolist())
     g = torch.Generator(device="cuda")
     g.manual_seed(32)
 
@@ -38,19 +43,30 @@ def test_decode_loop_driven_by_native_manager():
     vc = torch.full((nb, hkv, d, bs), nan, dtype=torch.bfloat16, device="cuda")
     hk, hv = storage_np(kc), storage_np(vc)                 # host mirror
 
+    def pool_tables(ids):
+        t = np.full((len(ids), maxb), nb - 1, dtype=np.int32)
+        for i, b in enumerate(ids):
+            t[i, :len(pool.pages[b])] = pool.pages[b]
+        return t, np.array([pool.length[b] for b in ids], dtype=np.int32)
+
     def prefill(seq, n):
         slots, copies = m.append(np.full(n, seq, dtype=np.int64))
         assert len(copies) == 0
+        pslots = [pool.append_token(seq) for _ in range(n)]
+        assert slots.tolist() == pslots
         k, v = rows(n)
         pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
-        return oracle.kv_append(storage_np(k), storage_np(v), slots, hk, hv, bs)
+        return oracle.kv_append(storage_np(k), storage_np(v), pslots, hk, hv, bs)
 
     m.allocate(0, 0)
+    pool.allocate(0, 0)
     hk, hv = prefill(0, 40)
     for child in range(1, 6):
         m.fork(0, child)
+        pool.fork(0, child)
     for s in range(6, 10):
         m.allocate(s, 0)
+        pool.allocate(s, 0)
         hk, hv = prefill(s, int(rng.integers(1, 100)))
     ids = np.arange(10, dtype=np.int64)
     tables, lens = m.block_tables(ids, maxb, pad_page=nb - 1)
@@ -60,10 +76,16 @@ def test_decode_loop_driven_by_native_manager():
     for step in range(steps):
         slots, copies = m.append(ids, tables, lens)
         copies_seen += len(copies)
+        before = len(pool.copies)
+        pslots = [pool.append_token(int(b)) for b in ids]
+        assert slots.tolist() == pslots
+        assert [tuple(c) for c in np.asarray(copies).reshape(-1, 2).tolist()] == pool.copies[before:]
+        ptables, plens = pool_tables(ids.tolist())
+        assert np.array_equal(ptables, tables) and np.array_equal(plens, lens)
         say("step", step, "copies", copies.tolist())
         if len(copies):
             pa.copy_blocks(kc, vc, torch.from_numpy(np.ascontiguousarray(copies)).cuda())
-            hk, hv = oracle.copy_blocks(hk, hv, copies)
+            hk, hv = oracle.copy_blocks(hk, hv, np.array(pool.copies[before:], dtype=np.int64))
         k, v = rows(len(ids))
         q = torch.randn(len(ids), hq, d, generator=g, device="cuda").to(torch.bfloat16)
         bt = torch.from_numpy(tables).cuda()
@@ -76,8 +98,8 @@ def test_decode_loop_driven_by_native_manager():
             pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
             out = pa.decode(q, kc, vc, bt, cl, scale, maxctx, reuse="shared")
         torch.cuda.synchronize()
-        hk, hv = oracle.kv_append(storage_np(k), storage_np(v), slots, hk, hv, bs)
-        ref = oracle.decode(storage_np(q), hk, hv, tables, lens, scale, bs, "bf16")
+        hk, hv = oracle.kv_append(storage_np(k), storage_np(v), pslots, hk, hv, bs)
+        ref = oracle.decode(storage_np(q), hk, hv, ptables, plens, scale, bs, "bf16")
         check_close(out_f64(out), ref, "bf16", f"step {step}")
     assert copies_seen == 5                                  # five children leave the shared page
     assert np.array_equal(storage_np(kc).view(np.uint16), hk.view(np.uint16))

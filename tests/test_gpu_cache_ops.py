@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import bits_equal, require_gpu, say, storage_np
+from gpu_util import bits_equal, require_gpu, run_step_updates, say, storage_np
 
 pytestmark = pytest.mark.gpu
 
@@ -85,14 +85,6 @@ def test_empty_calls_are_no_ops():
     pa.copy_blocks(kc, vc, torch.empty(0, 2, dtype=torch.int64, device="cuda"))
     torch.cuda.synchronize()
     assert bits_equal(kc, k0) and bits_equal(vc, v0)
-
-
-def run_step_updates(pa, w, t):
-    """Apply the step's copy-on-write copies and appends on the GPU."""
-    if len(w.copy_pairs):
-        pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
-    if len(w.append_slots):
-        pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
 
 
 def check_step_updates(pa, w, t):

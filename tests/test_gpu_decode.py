@@ -12,10 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import workloads as W
-from gpu_util import bits_equal, check_close, oracle_decode, out_f64, require_gpu, say, storage_np
-from test_gpu_cache_ops import run_step_updates
+from gpu_util import bits_equal, check_close, out_f64, require_gpu, run_step_updates, say, step_and_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -60,8 +58,7 @@ def test_decode_small_all_paths(shape):
     w = W.custom("ragged", 7, dtype, RAGGED, hq, hkv, d, bs)
     say("small", shape, w.summary())
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
-    ref = oracle_decode(w, t, range(w.num_seqs))
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
     for kernel in _kernels(dtype):
         for reuse in REUSE:
             for ps in PATHS:
@@ -79,8 +76,7 @@ def test_tiny_workload(figure):
     w = W.tiny(figure_table=figure)
     say("tiny", figure, w.block_tables.tolist())
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
-    ref = oracle_decode(w, t, range(w.num_seqs))
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
     for reuse in REUSE:
         for ps in PATHS:
             out = run_decode(pa, w, t, "auto", ps, reuse)
@@ -93,11 +89,10 @@ def test_empty_context_gives_zeros():
     w = W.custom("with_empty", 8, "bf16", [40, 1, 77, 600], 32, 8, 128, 16)
     say("empty context")
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
     t["context_lens"][2] = 0                 # sequence 2 has nothing to attend to
     w.context_lens = w.context_lens.copy()
     w.context_lens[2] = 0
-    ref = oracle_decode(w, t, range(w.num_seqs))
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
     assert not ref[2].any()
     for kernel in ("valu", "mfma"):
         for reuse in REUSE:
@@ -139,9 +134,8 @@ def test_named_workload_full_size(name):
     w = W.by_name(name)
     say("full", name, w.summary())
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
     seqs = _sample(w, 8, 11)
-    ref = oracle_decode(w, t, seqs)
+    ref = step_and_reference(pa, w, t, seqs)
     nat = natural_reuse(w)
     other = "shared" if nat == "stream" else "stream"
     for kernel, reuse in [("auto", nat), ("auto", other), ("valu", nat)]:
@@ -158,9 +152,8 @@ def test_single_pass_matches_split_at_full_size():
     w = W.llama3_8b()
     say("single vs split", w.summary())
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
     seqs = _sample(w, 6, 12)
-    ref = oracle_decode(w, t, seqs)
+    ref = step_and_reference(pa, w, t, seqs)
     for reuse in REUSE:
         for ps in (-1, 256, 1024):
             out = run_decode(pa, w, t, "mfma", ps, reuse)
@@ -216,8 +209,7 @@ def test_group_of_sixteen_and_head_dim_64():
     w = W.custom("g16", 9, "bf16", [5, 300, 1025, 2048], 32, 2, 64, 32)
     say("g16", w.summary())
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
-    ref = oracle_decode(w, t, range(w.num_seqs))
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
     for kernel in ("valu", "mfma"):
         for reuse in REUSE:
             for ps in (-1, 0, 128):
@@ -233,8 +225,7 @@ def test_bad_table_entries_stay_in_bounds():
     w = W.custom("pad", 10, "bf16", [17, 40], 32, 8, 128, 16)
     say("bad table entries")
     t = W.make_tensors(w, "cuda")
-    run_step_updates(pa, w, t)
-    ref = oracle_decode(w, t, range(w.num_seqs))
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
     bt = t["block_tables"].clone()
     bt[0, 2:] = 2 ** 30          # entries past ceil(17 / 16) = 2: never read
     for reuse in REUSE:
@@ -247,3 +238,32 @@ def test_bad_table_entries_stay_in_bounds():
         out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale,
                         w.max_context_len, partition_size=0, kernel="mfma", reuse=reuse)
         torch.cuda.synchronize()
+
+
+def test_loose_max_context_len_changes_nothing():
+    """max_context_len is only an upper bound.  A loose one (four times the
+    table width, so about 16 times the longest sequence) sizes a larger grid
+    whose extra partitions hold no tokens: for a given partition size every
+    output bit stays the same, and the library default for the loose bound
+    stays within tolerance of the oracle."""
+    pa = require_gpu()
+    w = W.custom("loose", 12, "bf16", [5, 300, 1025, 2000], 32, 8, 128, 16)
+    say("loose max_context_len", w.summary())
+    t = W.make_tensors(w, "cuda")
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    nbt = w.block_tables.shape[1]
+    bt = torch.zeros((w.num_seqs, 4 * nbt), dtype=torch.int32, device="cuda")
+    bt[:, :nbt] = t["block_tables"]
+    loose = 4 * nbt * w.block_size
+    for kernel in ("valu", "mfma"):
+        for ps in (-1, 64, 512):
+            say("  ", kernel, "partition", ps, "max_context_len", w.max_context_len, "vs", loose)
+            tight = run_decode(pa, w, t, kernel, ps, "stream")
+            wide = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale, loose,
+                             partition_size=ps, kernel=kernel, reuse="stream")
+            torch.cuda.synchronize()
+            assert bits_equal(tight, wide), (kernel, ps)
+        out = pa.decode(t["q"], t["k_cache"], t["v_cache"], bt, t["context_lens"], w.scale, loose,
+                        partition_size=0, kernel=kernel)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"loose default {kernel}")

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import bits_equal, check_close, oracle_decode, out_f64, require_gpu, say, storage_np
+from gpu_util import bits_equal, check_close, out_f64, reference_after_step, require_gpu, say, storage_np
 
 pytestmark = pytest.mark.gpu
 
@@ -111,9 +111,10 @@ def test_fused_mask_and_empty_contexts():
     k_new, v_new, mask, _ = newest_rows(w, t)
     skip = [1, 3]
     # sequences 1 and 3 got their newest token before; hand in other rows now
+    kc0, vc0 = oracle.kv_append(storage_np(k_new[skip]), storage_np(v_new[skip]), mask[skip],
+                                storage_np(t["k_cache"]), storage_np(t["v_cache"]), 16)
     pa.kv_append(k_new[skip].contiguous(), v_new[skip].contiguous(),
                  torch.from_numpy(mask[skip]).cuda(), t["k_cache"], t["v_cache"])
-    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
     appending = mask.copy()
     appending[skip] = -1
     k_in, v_in = k_new.clone(), v_new.clone()
@@ -153,6 +154,11 @@ def test_fused_named_workload_full_size(name):
     w = W.by_name(name)
     say("fused full", name, w.summary())
     t = W.make_tensors(w, "cuda")
+    rng = np.random.default_rng(19)
+    order = np.argsort(w.context_lens)
+    seqs = sorted({int(order[0]), int(order[-1])} |
+                  set(int(s) for s in rng.choice(w.num_seqs, size=min(6, w.num_seqs), replace=False)))
+    ref = reference_after_step(w, t, seqs)         # every row of the step appended, by the oracle
     if len(w.copy_pairs):
         pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
     k_new, v_new, mask, older = newest_rows(w, t)
@@ -172,11 +178,6 @@ def test_fused_named_workload_full_size(name):
         got_v = vc[page, :, :, off]
         assert bits_equal(got_k.contiguous(), k_new[b].contiguous())
         assert bits_equal(got_v.contiguous(), v_new[b].contiguous())
-    rng = np.random.default_rng(19)
-    order = np.argsort(w.context_lens)
-    seqs = sorted({int(order[0]), int(order[-1])} |
-                  set(int(s) for s in rng.choice(w.num_seqs, size=min(6, w.num_seqs), replace=False)))
-    ref = oracle_decode(w, t, seqs)
     stats = check_close(out_f64(out)[seqs], ref, w.dtype, f"fused {name}")
     say("  ", stats)
 

@@ -196,3 +196,31 @@ def test_fused_append_skips_pages_outside_the_pool():
     kc, vc = oracle.kv_append(w._k_new[keep], w._v_new[keep], slots[keep], kc0, vc0, 16)
     assert np.array_equal(storage_np(t["k_cache"]).view(np.uint16), kc.view(np.uint16))
     assert np.array_equal(storage_np(t["v_cache"]).view(np.uint16), vc.view(np.uint16))
+
+
+def test_loose_max_context_len_changes_nothing():
+    """A max_context_len several times the longest context (with block-table
+    rows widened to allow it): bit-identical for a given partition size, and
+    the default for the loose bound within tolerance of the oracle."""
+    pa = require_gpu()
+    w = W.multi_custom("loose_multi", 48, [9, 300, 1500], [3, 5, 2], 32, 8, 128, 16)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    nbt = w.block_tables.shape[1]
+    bt = torch.zeros((w.num_seqs, 4 * nbt), dtype=torch.int32, device="cuda")
+    bt[:, :nbt] = t["block_tables"]
+    loose = 4 * nbt * w.block_size
+
+    def run(tables, maxctx, P):
+        return pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], tables, t["context_lens"], t["query_start"],
+                               w.scale, maxctx, w.max_query_len, partition_size=P)
+
+    for P in (-1, 64, 512):
+        say("loose multi, partition", P, "max_context_len", w.max_context_len, "vs", loose)
+        tight, wide = run(t["block_tables"], w.max_context_len, P), run(bt, loose, P)
+        torch.cuda.synchronize()
+        assert bits_equal(tight, wide), P
+    out = run(bt, loose, 0)
+    torch.cuda.synchronize()
+    check_close(out_f64(out), ref, "bf16", "loose multi default")

@@ -117,7 +117,8 @@ def test_decode_over_prefix_cached_pages():
     torch.cuda.synchronize()
 
     # oracle: the same logical rows in a private layout of their own
-    L = [int(n) for n in lens]
+    L = [int(logical[s][0].shape[0]) + 1 for s in live]     # every row written, plus the new one
+    assert lens.tolist() == L
     npages = [-(-n // BS) for n in L]
     pk = np.zeros((sum(npages) + 1, HKV, D // x, BS, x), dtype=np.uint16)
     pv = np.zeros((sum(npages) + 1, HKV, D, BS), dtype=np.uint16)
