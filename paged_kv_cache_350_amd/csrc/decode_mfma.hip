@@ -11,7 +11,9 @@
 // [tokens x D] . [D x G] product and P.V a [D x tokens] . [tokens x G] one.
 // On the vector ALU they cost ~2G FMAs per cached element plus lane
 // reductions, which approaches the VALU rate at G = 8; one 16x16x32 bf16
-// MFMA retires 8192 of them.  G is padded to 16 (zero query rows).
+// MFMA retires 8192 of them.  G is padded to 16 columns; a padding column
+// repeats head 0's query, so it takes exactly column 0's rescale decisions
+// and is never stored.
 //
 // Work unit: a chunk of 32 tokens, tau = 0..31.  Per chunk:
 //   Q.K^T  v_mfma_f32_16x16x32_bf16 on two 16-token row tiles t = 0, 1:
@@ -28,7 +30,8 @@
 //          k-slots of lane group j are the tokens of its 8 scores, so lane
 //          (h, j) already holds its B operand; V pages are dim-major [D][BS],
 //          so the A operand is that lane's 8 tokens of dim 16 dc + r.
-//          Nothing goes through LDS inside the loop.
+//          Nothing goes through LDS inside the loop.  Page ids come through
+//          the scalar cache, one chunk ahead of their use.
 //
 // Two ways to assign tokens to rows, chosen by how the pages are reused:
 //   split (streaming: each page read by one workgroup per step) -- tile t is
@@ -59,7 +62,6 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
 constexpr int kHalf = 16;             // tokens per row tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
-constexpr int kSegPages = 256;        // page ids staged in LDS at a time
 
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
@@ -133,11 +135,9 @@ void decode_mfma_kernel(DecodeParams p) {
     {
         const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
                                (head0 + (hl < G ? hl : 0)) * D;
-        for (int s = 0; s < KSTEPS; ++s) {
-            u32x4_t raw = ld16(qrow + 32 * s + 8 * j);
-            if (hl >= G) raw = u32x4_t{0u, 0u, 0u, 0u};
-            qf[s] = as_bf16x8(raw);
-        }
+        // no select on the loaded values: the first wait on them is the
+        // first MFMA, after the first chunk's K/V loads are in flight
+        for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(ld16(qrow + 32 * s + 8 * j));
     }
 
     // split path: per-lane byte offsets inside a half's K / V tile (loop
@@ -162,13 +162,13 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int dc = 0; dc < DC; ++dc) acc[dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Fused append (pa_decode_append): the workgroup that reads position
-    // L - 1 first stores kv head g's new K and V rows into that slot.  The
-    // barrier after the page-id staging below makes the stores visible to
-    // every wave of the workgroup, which then reads the new token like any
-    // other.  No other workgroup reads that page: without sharing it belongs
-    // to this (sequence, kv head) alone, and a sequence only appends into a
-    // page it owns (copy-on-write happens before).  A page id outside the
-    // pool writes nothing, as pa_kv_append skips an out-of-range slot.
+    // L - 1 first stores kv head g's new K and V rows into that slot.  A
+    // barrier then makes the stores visible to every wave of the workgroup,
+    // which reads the new token like any other.  No other workgroup reads
+    // that page: without sharing it belongs to this (sequence, kv head) alone,
+    // and a sequence only appends into a page it owns (copy-on-write happens
+    // before).  A page id outside the pool writes nothing, as pa_kv_append
+    // skips an out-of-range slot.
     const bool appends = p.k_new != nullptr && end == L &&    // workgroup-uniform
                          (p.append_mask == nullptr || p.append_mask[b] >= 0) &&
                          (uint32_t)row[(L - 1) / BS] < (uint64_t)p.num_blocks;
@@ -184,127 +184,127 @@ void decode_mfma_kernel(DecodeParams p) {
         uint16_t* vw = const_cast<uint16_t*>(vc) + tile;
         for (int c = tid; c < D / 8; c += kThreads) st16(kw + ((size_t)c * BS + off) * 8, ld16(kn + 8 * c));
         for (int d = tid; d < D; d += kThreads) vw[(size_t)d * BS + off] = vn[d];
+        __syncthreads();                 // workgroup-uniform branch
     }
 
-    // The partition's page ids are staged in LDS, up to kSegPages at a time:
-    // one coalesced load by the whole workgroup, then each chunk reads its
-    // ids from LDS (a short on-chip latency) instead of starting with a
-    // dependent global load.  Ids are clamped to the pool.
-    __shared__ int spage[kSegPages];
+    // Page ids: scalar loads through the constant address space (the table
+    // is read-only during the kernel), issued one chunk ahead of their use.
+    // They bypass the vector memory queue that the K/V stream keeps full,
+    // and need no LDS staging or barrier.  Ids outside the pool read page 0.
+    typedef const __attribute__((address_space(4))) int* const_row_t;
+    const const_row_t rowc = (const_row_t)row;
     const int nchunks = (end - start + kChunk - 1) / kChunk;
     const int blk_first = start / BS;
-    const int blk_end = (end + BS - 1) / BS;                 // one past the last page used
-    constexpr int kSegChunks = kSegPages * BS / kChunk;
-    for (int seg = 0; seg < nchunks; seg += kSegChunks) {
-        const int seg_blk = blk_first + seg * (kChunk / BS);
-        const int seg_n = min(kSegPages, blk_end - seg_blk);
-        if (seg > 0) __syncthreads();                        // previous segment fully consumed
-        for (int i = tid; i < seg_n; i += kThreads) {
-            const int pg = row[seg_blk + i];
-            spage[i] = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
-        }
-        __syncthreads();
-        const int seg_end = min(nchunks, seg + kSegChunks);
-        for (int ci = seg + w; ci < seg_end; ci += kWaves) {
-            const int cstart = start + ci * kChunk;
-            const int valid = min(kChunk, end - cstart);
+    const int blk_last = (end - 1) / BS;                     // last page the partition uses
+    // raw ids of chunk ci's pages; at block 16 the second one repeats the
+    // first when the chunk does not reach it
+    auto chunk_pages = [&](int ci, int& first, int& second) {
+        const int blk = blk_first + ci * (kChunk / BS);
+        first = rowc[blk];
+        second = BS == 16 ? rowc[min(blk + 1, blk_last)] : first;
+    };
+    auto clamp_page = [&](int x) { return (uint32_t)x >= (uint64_t)p.num_blocks ? 0 : x; };
+    int next0 = 0, next1 = 0;
+    if (w < nchunks) chunk_pages(w, next0, next1);
+    for (int ci = w; ci < nchunks; ci += kWaves) {
+        const int cstart = start + ci * kChunk;
+        const int valid = min(kChunk, end - cstart);
 
-            // ---- pages of the chunk (wave-uniform)
-            const int lb = (ci - seg) * (kChunk / BS);
-            const int pg0 = __builtin_amdgcn_readfirstlane(spage[lb]);
-            const int pg1 = (BS == 16 && valid > kHalf) ? __builtin_amdgcn_readfirstlane(spage[lb + 1]) : pg0;
+        // ---- pages of the chunk (wave-uniform); the next chunk's ids go in flight
+        const int pg0 = clamp_page(__builtin_amdgcn_readfirstlane(next0));
+        const int pg1 = clamp_page(__builtin_amdgcn_readfirstlane(next1));
+        if (ci + kWaves < nchunks) chunk_pages(ci + kWaves, next0, next1);
 
-            // ---- loads: K of both row tiles, V of every 16-dim tile
-            u32x4_t kraw[2][KSTEPS];
-            u32x4_t vop[DC];                 // V^T operand, 8 bf16 per lane
-            if constexpr (SPLIT) {
-                __amdgpu_buffer_rsrc_t krs[2], vrs[2];
-                for (int t = 0; t < 2; ++t) {
-                    const int page = t ? pg1 : pg0;
-                    const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
-                    const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
-                    // a half with no valid token gets an empty range: loads return 0
-                    const bool live = t == 0 || valid > kHalf;
-                    krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
-                    vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
-                }
-                for (int t = 0; t < 2; ++t)
-                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
-                u32x2_t vh[2][DC];
-                for (int t = 0; t < 2; ++t)
-                    for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
-                // every load of the chunk is in flight before the first MFMA waits on one
-                __builtin_amdgcn_sched_barrier(0);
-                for (int dc = 0; dc < DC; ++dc)
-                    vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
-            } else {
-                const int kpage = (BS == 16 && tk >= kHalf) ? pg1 : pg0;
-                const uint16_t* kb = kc + ((size_t)kpage * kv_heads + g) * tile_elems +
-                                     (size_t)(tk % BS) * 8 + (size_t)j * BS * 8;
-                const int vpage = (BS == 16 && tv >= kHalf) ? pg1 : pg0;
-                const uint16_t* vb = vc + ((size_t)vpage * kv_heads + g) * tile_elems + (tv % BS) +
-                                     (size_t)r * BS;
-                for (int t = 0; t < 2; ++t)
-                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = ld16(kb + 32 * t + (size_t)s * 4 * BS * 8);
-                for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-
-            // ---- S = K . Q^T
-            f32x4_t st[2];
+        // ---- loads: K of both row tiles, V of every 16-dim tile
+        u32x4_t kraw[2][KSTEPS];
+        u32x4_t vop[DC];                 // V^T operand, 8 bf16 per lane
+        if constexpr (SPLIT) {
+            __amdgpu_buffer_rsrc_t krs[2], vrs[2];
             for (int t = 0; t < 2; ++t) {
-                st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                for (int s = 0; s < KSTEPS; ++s)
-                    st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[s], st[t], 0, 0, 0);
+                const int page = t ? pg1 : pg0;
+                const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
+                const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
+                // a half with no valid token gets an empty range: loads return 0
+                const bool live = t == 0 || valid > kHalf;
+                krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
+                vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
             }
-
-            // ---- online softmax; slot 4 t + i of lane (hl, j) is token slot_token(t, i, j)
-            float sc[8];
             for (int t = 0; t < 2; ++t)
-                for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
-            if (valid < kChunk) {
-                for (int t = 0; t < 2; ++t)
-                    for (int i = 0; i < 4; ++i)
-                        sc[4 * t + i] = (slot_token<SPLIT>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
-            }
-            float mx = sc[0];
-            for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-            mx = max_xor16(mx);
-            mx = max_xor32(mx);
-            // Lazy rescaling: the reference max moves only when a score exceeds it
-            // by more than kRescaleSlack (always on the first chunk, m_run = -inf).
-            // Between moves the weights are 2^(s - m_run) <= 2^kRescaleSlack; acc
-            // and l share the reference, so the result is the same.
-            const bool grow = mx > m_run + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {       // wave-uniform branch
-                const float mn = grow ? mx : m_run;
-                const float alpha = fast_exp2(m_run - mn);      // 0 on the first chunk
-                for (int dc = 0; dc < DC; ++dc) acc[dc] = acc[dc] * alpha;
-                l_run *= alpha;
-                m_run = mn;
-            }
-            bf16x8_t pf;
-            float psum = 0.f;
-            for (int k = 0; k < 8; ++k) {
-                const bf16_t pb = (bf16_t)fast_exp2(sc[k] - m_run);
-                pf[k] = pb;
-                psum += (float)pb;           // normalise with the weights actually used
-            }
-            l_run += psum;
-
-            // ---- O^T += V^T . P^T
-            if (valid < kChunk) {
-                // zero the value slots past the context: dword q holds slots 2 q, 2 q + 1
-                for (int q = 0; q < 4; ++q) {
-                    const int tok = slot_token<SPLIT>(q / 2, 2 * (q % 2), j);
-                    const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
-                    const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
-                    for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
-                }
-            }
+                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
+            u32x2_t vh[2][DC];
+            for (int t = 0; t < 2; ++t)
+                for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
+            // every load of the chunk is in flight before the first MFMA waits on one
+            __builtin_amdgcn_sched_barrier(0);
             for (int dc = 0; dc < DC; ++dc)
-                acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf, acc[dc], 0, 0, 0);
+                vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+        } else {
+            const int kpage = (BS == 16 && tk >= kHalf) ? pg1 : pg0;
+            const uint16_t* kb = kc + ((size_t)kpage * kv_heads + g) * tile_elems +
+                                 (size_t)(tk % BS) * 8 + (size_t)j * BS * 8;
+            const int vpage = (BS == 16 && tv >= kHalf) ? pg1 : pg0;
+            const uint16_t* vb = vc + ((size_t)vpage * kv_heads + g) * tile_elems + (tv % BS) +
+                                 (size_t)r * BS;
+            for (int t = 0; t < 2; ++t)
+                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = ld16(kb + 32 * t + (size_t)s * 4 * BS * 8);
+            for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
+            __builtin_amdgcn_sched_barrier(0);
         }
+
+        // ---- S = K . Q^T
+        f32x4_t st[2];
+        for (int t = 0; t < 2; ++t) {
+            st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < KSTEPS; ++s)
+                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[s], st[t], 0, 0, 0);
+        }
+
+        // ---- online softmax; slot 4 t + i of lane (hl, j) is token slot_token(t, i, j)
+        float sc[8];
+        for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
+        if (valid < kChunk) {
+            for (int t = 0; t < 2; ++t)
+                for (int i = 0; i < 4; ++i)
+                    sc[4 * t + i] = (slot_token<SPLIT>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
+        }
+        float mx = sc[0];
+        for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
+        mx = max_xor16(mx);
+        mx = max_xor32(mx);
+        // Lazy rescaling: the reference max moves only when a score exceeds it
+        // by more than kRescaleSlack (always on the first chunk, m_run = -inf).
+        // Between moves the weights are 2^(s - m_run) <= 2^kRescaleSlack; acc
+        // and l share the reference, so the result is the same.
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {       // wave-uniform branch
+            const float mn = grow ? mx : m_run;
+            const float alpha = fast_exp2(m_run - mn);      // 0 on the first chunk
+            for (int dc = 0; dc < DC; ++dc) acc[dc] = acc[dc] * alpha;
+            l_run *= alpha;
+            m_run = mn;
+        }
+        bf16x8_t pf;
+        float psum = 0.f;
+        for (int k = 0; k < 8; ++k) {
+            const bf16_t pb = (bf16_t)fast_exp2(sc[k] - m_run);
+            pf[k] = pb;
+            psum += (float)pb;           // normalise with the weights actually used
+        }
+        l_run += psum;
+
+        // ---- O^T += V^T . P^T
+        if (valid < kChunk) {
+            // zero the value slots past the context: dword q holds slots 2 q, 2 q + 1
+            for (int q = 0; q < 4; ++q) {
+                const int tok = slot_token<SPLIT>(q / 2, 2 * (q % 2), j);
+                const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
+                const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
+                for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
+            }
+        }
+        for (int dc = 0; dc < DC; ++dc)
+            acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf, acc[dc], 0, 0, 0);
     }
 
     // ---- merge the four waves; lane (hl, j) holds dims 16 dc + 4 j + i of head hl

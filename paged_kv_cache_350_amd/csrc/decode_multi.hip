@@ -38,7 +38,6 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
 constexpr int kHalf = 16;             // tokens per row tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
-constexpr int kSegPages = 256;        // page ids staged in LDS at a time
 
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
@@ -74,7 +73,6 @@ void decode_multi_kernel(DecodeParams p) {
     float* sm_m = smem;                          // [kWaves][16]
     float* sm_l = sm_m + kWaves * 16;            // [kWaves][16]
     float* sacc = sm_l + kWaves * 16;            // [kWaves][16][D]
-    __shared__ int spage[kSegPages];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -119,11 +117,10 @@ void decode_multi_kernel(DecodeParams p) {
         lim[nt] = live ? L - n + jq : -1;
         const size_t qrow = ((size_t)(qr.row0 + (live ? jq : 0)) * p.num_heads + (size_t)g * G + c % G) * D;
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qrow;
-        for (int s = 0; s < KSTEPS; ++s) {
-            u32x4_t raw = ld16(qp + 32 * s + 8 * j);
-            if (!live) raw = u32x4_t{0u, 0u, 0u, 0u};
-            qf[nt][s] = as_bf16x8(raw);
-        }
+        // a padding column repeats token 0's query of its head and is masked
+        // out entirely; no select on the loaded values, so the first wait on
+        // them is the first MFMA
+        for (int s = 0; s < KSTEPS; ++s) qf[nt][s] = as_bf16x8(ld16(qp + 32 * s + 8 * j));
     }
 
     const uint32_t kofs = (uint32_t)((j * BS + r) * 16);
@@ -148,9 +145,8 @@ void decode_multi_kernel(DecodeParams p) {
     // Fused append (pa_decode_multi_append): new token j's K and V rows (row
     // row0 + j of k_new / v_new, aligned with q) belong at position
     // L - n + j.  Every workgroup stores the new rows that fall inside the
-    // positions it reads, before the first barrier below, which makes them
-    // visible to all its waves; so whoever reads a new row has written it
-    // itself.  Column groups of one (sequence, kv head) store the same bytes,
+    // positions it reads, then a barrier makes them visible to all its
+    // waves; so whoever reads a new row has written it itself.  Column groups of one (sequence, kv head) store the same bytes,
     // which cannot change what either reads.  A page id outside the pool
     // writes nothing.
     if (p.k_new != nullptr) {
@@ -178,110 +174,112 @@ void decode_multi_kernel(DecodeParams p) {
             const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
             vw[tile + (size_t)d * BS + pos % BS] = vn[src + d];
         }
+        __syncthreads();                 // k_new is a launch parameter: uniform
     }
 
+    // Page ids: scalar loads through the constant address space (the table
+    // is read-only during the kernel), one chunk ahead of their use; ids
+    // outside the pool read page 0.
+    typedef const __attribute__((address_space(4))) int* const_row_t;
+    const const_row_t rowc = (const_row_t)row;
     const int nchunks = (end - start + kChunk - 1) / kChunk;
     const int blk_first = start / BS;
-    const int blk_end = (end + BS - 1) / BS;
-    constexpr int kSegChunks = kSegPages * BS / kChunk;
-    for (int seg = 0; seg < nchunks; seg += kSegChunks) {
-        const int seg_blk = blk_first + seg * (kChunk / BS);
-        const int seg_n = min(kSegPages, blk_end - seg_blk);
-        if (seg > 0) __syncthreads();
-        for (int i = tid; i < seg_n; i += kThreads) {
-            const int pg = row[seg_blk + i];
-            spage[i] = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
+    const int blk_last = (end - 1) / BS;                     // last page the partition uses
+    auto chunk_pages = [&](int ci, int& first, int& second) {
+        const int blk = blk_first + ci * (kChunk / BS);
+        first = rowc[blk];
+        second = BS == 16 ? rowc[min(blk + 1, blk_last)] : first;
+    };
+    auto clamp_page = [&](int x) { return (uint32_t)x >= (uint64_t)p.num_blocks ? 0 : x; };
+    int next0 = 0, next1 = 0;
+    if (w < nchunks) chunk_pages(w, next0, next1);
+    for (int ci = w; ci < nchunks; ci += kWaves) {
+        const int cstart = start + ci * kChunk;
+        const int valid = min(kChunk, end - cstart);
+
+        const int pg0 = clamp_page(__builtin_amdgcn_readfirstlane(next0));
+        const int pg1 = clamp_page(__builtin_amdgcn_readfirstlane(next1));
+        if (ci + kWaves < nchunks) chunk_pages(ci + kWaves, next0, next1);
+
+        u32x4_t kraw[2][KSTEPS];
+        u32x4_t vop[DC];
+        {
+            __amdgpu_buffer_rsrc_t krs[2], vrs[2];
+            for (int t = 0; t < 2; ++t) {
+                const int page = t ? pg1 : pg0;
+                const int toff = BS == 32 ? kHalf * t : 0;
+                const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
+                const bool half_live = t == 0 || valid > kHalf;
+                krs[t] = make_rsrc(kc + tile + toff * 8, half_live ? kTileBytes - toff * 16 : 0);
+                vrs[t] = make_rsrc(vc + tile + toff, half_live ? kTileBytes - toff * 2 : 0);
+            }
+            for (int t = 0; t < 2; ++t)
+                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16<POLICY>(krs[t], kofs, s * kStepBytes);
+            u32x2_t vh[2][DC];
+            for (int t = 0; t < 2; ++t)
+                for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8<POLICY>(vrs[t], vofs, dc * kTileStep);
+            __builtin_amdgcn_sched_barrier(0);
+            for (int dc = 0; dc < DC; ++dc)
+                vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
         }
-        __syncthreads();
-        const int seg_end = min(nchunks, seg + kSegChunks);
-        for (int ci = seg + w; ci < seg_end; ci += kWaves) {
-            const int cstart = start + ci * kChunk;
-            const int valid = min(kChunk, end - cstart);
 
-            const int lb = (ci - seg) * (kChunk / BS);
-            const int pg0 = __builtin_amdgcn_readfirstlane(spage[lb]);
-            const int pg1 = (BS == 16 && valid > kHalf) ? __builtin_amdgcn_readfirstlane(spage[lb + 1]) : pg0;
-
-            u32x4_t kraw[2][KSTEPS];
-            u32x4_t vop[DC];
-            {
-                __amdgpu_buffer_rsrc_t krs[2], vrs[2];
-                for (int t = 0; t < 2; ++t) {
-                    const int page = t ? pg1 : pg0;
-                    const int toff = BS == 32 ? kHalf * t : 0;
-                    const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
-                    const bool half_live = t == 0 || valid > kHalf;
-                    krs[t] = make_rsrc(kc + tile + toff * 8, half_live ? kTileBytes - toff * 16 : 0);
-                    vrs[t] = make_rsrc(vc + tile + toff, half_live ? kTileBytes - toff * 2 : 0);
-                }
-                for (int t = 0; t < 2; ++t)
-                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16<POLICY>(krs[t], kofs, s * kStepBytes);
-                u32x2_t vh[2][DC];
-                for (int t = 0; t < 2; ++t)
-                    for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8<POLICY>(vrs[t], vofs, dc * kTileStep);
-                __builtin_amdgcn_sched_barrier(0);
-                for (int dc = 0; dc < DC; ++dc)
-                    vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+        // wave-uniform: does any score of this chunk need masking?
+        const bool masked = valid < kChunk || cstart + kChunk - 1 > lo_lim;
+        bf16x8_t pf[NT];
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4_t st[2];
+            for (int t = 0; t < 2; ++t) {
+                st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < KSTEPS; ++s)
+                    st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[nt][s], st[t], 0, 0, 0);
             }
-
-            // wave-uniform: does any score of this chunk need masking?
-            const bool masked = valid < kChunk || cstart + kChunk - 1 > lo_lim;
-            bf16x8_t pf[NT];
-            for (int nt = 0; nt < NT; ++nt) {
-                f32x4_t st[2];
-                for (int t = 0; t < 2; ++t) {
-                    st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    for (int s = 0; s < KSTEPS; ++s)
-                        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][s]), qf[nt][s], st[t], 0, 0, 0);
-                }
-                float sc[8];
+            float sc[8];
+            for (int t = 0; t < 2; ++t)
+                for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
+            if (masked) {
+                // keep chunk tokens < cut: inside the partition and visible to this column
+                const int cut = min(valid, lim[nt] - cstart + 1);
                 for (int t = 0; t < 2; ++t)
-                    for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[t][i] * p.scale_log2;
-                if (masked) {
-                    // keep chunk tokens < cut: inside the partition and visible to this column
-                    const int cut = min(valid, lim[nt] - cstart + 1);
-                    for (int t = 0; t < 2; ++t)
-                        for (int i = 0; i < 4; ++i)
-                            sc[4 * t + i] = slot_token(t, i, j) < cut ? sc[4 * t + i] : neg_inf();
-                }
-                float mx = sc[0];
-                for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-                mx = max_xor16(mx);
-                mx = max_xor32(mx);
-                const bool grow = mx > m_run[nt] + kRescaleSlack;
-                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                    const float mn = grow ? mx : m_run[nt];
-                    // A column with nothing accumulated yet (running max -inf)
-                    // takes factor 0, not 2^(-inf - -inf) = NaN: another column
-                    // of the tile may be what took the branch.
-                    const float alpha = m_run[nt] == neg_inf() ? 0.f : fast_exp2(m_run[nt] - mn);
-                    for (int dc = 0; dc < DC; ++dc) acc[nt][dc] = acc[nt][dc] * alpha;
-                    l_run[nt] *= alpha;
-                    m_run[nt] = mn;
-                }
-                // -inf running max: nothing visible yet, every score here is -inf too
-                const float mref = m_run[nt] == neg_inf() ? 0.f : m_run[nt];
-                float psum = 0.f;
-                for (int k = 0; k < 8; ++k) {
-                    const bf16_t pb = (bf16_t)fast_exp2(sc[k] - mref);
-                    pf[nt][k] = pb;
-                    psum += (float)pb;
-                }
-                l_run[nt] += psum;
+                    for (int i = 0; i < 4; ++i)
+                        sc[4 * t + i] = slot_token(t, i, j) < cut ? sc[4 * t + i] : neg_inf();
             }
-
-            if (valid < kChunk) {
-                for (int q = 0; q < 4; ++q) {
-                    const int tok = slot_token(q / 2, 2 * (q % 2), j);
-                    const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
-                    const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
-                    for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
-                }
+            float mx = sc[0];
+            for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
+            mx = max_xor16(mx);
+            mx = max_xor32(mx);
+            const bool grow = mx > m_run[nt] + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float mn = grow ? mx : m_run[nt];
+                // A column with nothing accumulated yet (running max -inf)
+                // takes factor 0, not 2^(-inf - -inf) = NaN: another column
+                // of the tile may be what took the branch.
+                const float alpha = m_run[nt] == neg_inf() ? 0.f : fast_exp2(m_run[nt] - mn);
+                for (int dc = 0; dc < DC; ++dc) acc[nt][dc] = acc[nt][dc] * alpha;
+                l_run[nt] *= alpha;
+                m_run[nt] = mn;
             }
-            for (int nt = 0; nt < NT; ++nt)
-                for (int dc = 0; dc < DC; ++dc)
-                    acc[nt][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf[nt], acc[nt][dc], 0, 0, 0);
+            // -inf running max: nothing visible yet, every score here is -inf too
+            const float mref = m_run[nt] == neg_inf() ? 0.f : m_run[nt];
+            float psum = 0.f;
+            for (int k = 0; k < 8; ++k) {
+                const bf16_t pb = (bf16_t)fast_exp2(sc[k] - mref);
+                pf[nt][k] = pb;
+                psum += (float)pb;
+            }
+            l_run[nt] += psum;
         }
+
+        if (valid < kChunk) {
+            for (int q = 0; q < 4; ++q) {
+                const int tok = slot_token(q / 2, 2 * (q % 2), j);
+                const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
+                const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
+                for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
+            }
+        }
+        for (int nt = 0; nt < NT; ++nt)
+            for (int dc = 0; dc < DC; ++dc)
+                acc[nt][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf[nt], acc[nt][dc], 0, 0, 0);
     }
 
     // ---- merge the four waves, one tile at a time through the same LDS
