@@ -526,10 +526,10 @@ def main(argv=None) -> int:
 
     # the load path a caller picks: its block manager knows whether pages are shared
     reuse = a.reuse if a.reuse != "auto" else ("shared" if w.extra.get("shared_pages") else "stream")
-    P = pa.decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, ps_req)
+    P = pa.decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, ps_req, reuse)
     split = P > 0
     out = torch.empty_like(t["q"])
-    ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P) if split else None
+    ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P, reuse) if split else None
     kernel_name = "decode_mfma" if (a.kernel == "mfma" or (a.kernel == "auto" and w.dtype == "bf16")) \
         else "decode_valu"
     stream = torch.cuda.current_stream()

@@ -213,25 +213,37 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
 /*
  * Partition size pa_decode uses for a request: > 0 = split path with that
  * many tokens per partition, 0 = single pass, < 0 = invalid request
- * (PA_ERR_ARG).  Pure host arithmetic.  An explicit partition_size (a
- * multiple of 32) is returned as is and -1 gives 0.  The library default
- * (partition_size 0) is a single pass when max_context_len <= 512;
- * otherwise the largest power of two P in [512, 4096] with
- * 4 P <= max_context_len and num_seqs * num_kv_heads * ceil(max_context_len / P)
- * >= 1024 workgroups (512 if none qualifies), lowered to 256 when that
- * leaves fewer than 1024 workgroups.
+ * (PA_ERR_ARG, or an unknown `reuse`).  Pure host arithmetic.  An explicit
+ * partition_size (a multiple of 32) is returned as is and -1 gives 0.
+ * The library default (partition_size 0) depends on the load path `reuse`
+ * selects, with pairs = num_seqs * num_kv_heads:
+ *   streaming loads (PA_KV_AUTO, PA_KV_STREAM): a single pass when
+ *     max_context_len <= 512, when pairs >= 2048, or when pairs >= 1024
+ *     and max_context_len <= 4096; otherwise the largest power of two P in
+ *     [1024, 8192] with P < max_context_len and
+ *     pairs * ceil(max_context_len / P) >= 768; otherwise the shared-page rule.
+ *   shared pages (PA_KV_SHARED): a single pass when max_context_len <= 512;
+ *     otherwise the largest power of two P in [512, 4096] with
+ *     4 P <= max_context_len and pairs * ceil(max_context_len / P) >= 1024
+ *     (512 if none qualifies), lowered to 256 when that leaves fewer than
+ *     1024 workgroups.
+ * On the streaming path, partitions of 2048 tokens or more and single
+ * passes over >= 1024 pairs (contexts over 512) run 12-wave workgroups that
+ * fill a compute unit each; everything else runs 4-wave workgroups.  The
+ * choice changes speed only: either gives results within the same bounds.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t partition_size);
+                                 int32_t partition_size, pa_kv_reuse reuse);
 
 /*
  * Workspace bytes pa_decode needs (0 for the single pass):
  * num_seqs * num_heads * ceil(max_context_len / P) * (head_dim + 2) * 4,
  * P = pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
- * partition_size).  Returns 0 for invalid arguments as well.
+ * partition_size, reuse).  Returns 0 for invalid arguments as well.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_context_len, int32_t partition_size);
+                                int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                                pa_kv_reuse reuse);
 
 /*
  * pa_decode_partition -- first stage of the split path on its own: every

@@ -42,8 +42,8 @@ _c_int, _c_i64, _c_size, _c_float, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes
 _SIGNATURES = {
     "pa_status_string": ([_c_int], ctypes.c_char_p),
     "pa_version": ([], _c_int),
-    "pa_decode_partition_size": ([_c_int, _c_int, _c_int, _c_int], _c_int),
-    "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
+    "pa_decode_partition_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_int),
+    "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
     "pa_kv_append": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
@@ -137,14 +137,15 @@ def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
 
 
 def decode_partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int,
-                          partition_size: int = 0) -> int:
-    return lib().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size)
+                          partition_size: int = 0, reuse: str = "auto") -> int:
+    return lib().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size,
+                                          REUSE[reuse])
 
 
 def decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
-                          max_context_len: int, partition_size: int = 0) -> int:
+                          max_context_len: int, partition_size: int = 0, reuse: str = "auto") -> int:
     return lib().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                          max_context_len, partition_size)
+                                          max_context_len, partition_size, REUSE[reuse])
 
 
 def kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
@@ -191,10 +192,10 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_le
 
 
 def make_workspace(q: torch.Tensor, num_kv_heads: int, max_context_len: int,
-                   partition_size: int = 0):
+                   partition_size: int = 0, reuse: str = "auto"):
     """Allocate the split-path workspace (or None) for a decode call."""
     B, hq, d = q.shape
-    n = decode_workspace_size(B, hq, num_kv_heads, d, max_context_len, partition_size)
+    n = decode_workspace_size(B, hq, num_kv_heads, d, max_context_len, partition_size, reuse)
     if n == 0:
         return None
     return torch.empty(n // 4, dtype=torch.float32, device=q.device)
@@ -218,7 +219,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     if workspace is None:
-        workspace = make_workspace(q, hkv, max_context_len, partition_size)
+        workspace = make_workspace(q, hkv, max_context_len, partition_size, reuse)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().pa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -256,7 +257,7 @@ def decode_append(k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, k_c
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     if workspace is None:
-        workspace = make_workspace(q, hkv, max_context_len, partition_size)
+        workspace = make_workspace(q, hkv, max_context_len, partition_size, reuse)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().pa_decode_append(k_new.data_ptr(), v_new.data_ptr(), sm_ptr, q.data_ptr(),

@@ -57,8 +57,6 @@ namespace pa_impl {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
 constexpr int kHalf = 16;             // tokens per row tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
@@ -88,9 +86,11 @@ __device__ __forceinline__ int slot_token(int t, int i, int j) {
     return SPLIT ? kHalf * t + 4 * j + i : 8 * j + 4 * t + i;
 }
 
-template <int D, int BS, bool SPLIT>
-__global__ __launch_bounds__(kThreads)
+template <int D, int BS, bool SPLIT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave)
 void decode_mfma_kernel(DecodeParams p) {
+    constexpr int kWaves = WAVES;
+    constexpr int kThreads = kWaves * kWave;
     constexpr int KSTEPS = D / 32;   // Q.K^T k-steps
     constexpr int DC = D / 16;       // 16-dim output tiles of P.V
     constexpr uint32_t kTileBytes = (uint32_t)D * BS * 2;
@@ -161,39 +161,62 @@ void decode_mfma_kernel(DecodeParams p) {
     f32x4_t acc[DC];
     for (int dc = 0; dc < DC; ++dc) acc[dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    const int nchunks = (end - start + kChunk - 1) / kChunk;
+
     // Fused append (pa_decode_append): the workgroup that reads position
-    // L - 1 first stores kv head g's new K and V rows into that slot.  A
-    // barrier then makes the stores visible to every wave of the workgroup,
-    // which reads the new token like any other.  No other workgroup reads
-    // that page: without sharing it belongs to this (sequence, kv head) alone,
-    // and a sequence only appends into a page it owns (copy-on-write happens
-    // before).  A page id outside the pool writes nothing, as pa_kv_append
-    // skips an out-of-range slot.
-    const bool appends = p.k_new != nullptr && end == L &&    // workgroup-uniform
-                         (p.append_mask == nullptr || p.append_mask[b] >= 0) &&
-                         (uint32_t)row[(L - 1) / BS] < (uint64_t)p.num_blocks;
-    if (appends) {
+    // L - 1 stores kv head g's new K and V rows into that slot, and the wave
+    // that reads it (the one whose last chunk holds L - 1) stores them
+    // itself.  Its loads of the new row go out with its first loads; the
+    // stores follow its first chunk's K/V loads, and it waits for them only
+    // before its last chunk's loads, so no wave waits on the row's latency.
+    // The first chunk never holds the appended page unless it is also the
+    // last; then the row is stored and waited for before any K/V load.  No
+    // other workgroup reads that page: without sharing it belongs to this
+    // (sequence, kv head) alone, and a sequence only appends into a page it
+    // owns (copy-on-write happens before).  A page id outside the pool
+    // writes nothing, as pa_kv_append skips an out-of-range slot.
+    //
+    // Only the appending wave reads the mask and the page id, through the
+    // scalar cache (both are read-only here).
+    typedef const __attribute__((address_space(4))) int* const_row_t;
+    typedef const __attribute__((address_space(4))) int64_t* const_mask_t;
+    const const_row_t rowc = (const_row_t)row;
+    bool append_wave = false;                                // wave-uniform
+    if (p.k_new != nullptr && end == L && w == (nchunks - 1) % kWaves) {
+        const bool masked_out = p.append_mask != nullptr && ((const_mask_t)p.append_mask)[b] < 0;
+        append_wave = !masked_out && (uint32_t)rowc[(L - 1) / BS] < (uint64_t)p.num_blocks;
+    }
+    const bool store_first = append_wave && nchunks - 1 < kWaves;       // its only chunk holds L - 1
+    // lane c < D / 8 holds K bytes 16 c .. 16 c + 15 of the new row; lane
+    // l holds V dims l and l + 64 (D = 128) or l (D = 64)
+    u32x4_t new_k = u32x4_t{0u, 0u, 0u, 0u};
+    uint16_t new_v[D / kWave];
+    uint16_t* new_kdst = nullptr;
+    uint16_t* new_vdst = nullptr;
+    if (append_wave) {
         const int pos = L - 1;
-        const int pg = row[pos / BS];
-        const int off = pos % BS;
-        const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
+        const size_t tile = ((size_t)rowc[pos / BS] * kv_heads + g) * tile_elems;
         const size_t src = ((size_t)b * kv_heads + g) * D;
         const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + src;
         const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + src;
-        uint16_t* kw = const_cast<uint16_t*>(kc) + tile;
-        uint16_t* vw = const_cast<uint16_t*>(vc) + tile;
-        for (int c = tid; c < D / 8; c += kThreads) st16(kw + ((size_t)c * BS + off) * 8, ld16(kn + 8 * c));
-        for (int d = tid; d < D; d += kThreads) vw[(size_t)d * BS + off] = vn[d];
-        __syncthreads();                 // workgroup-uniform branch
+        if (lane < D / 8) new_k = ld16(kn + 8 * lane);
+        for (int i = 0; i < D / kWave; ++i) new_v[i] = vn[lane + kWave * i];
+        new_kdst = const_cast<uint16_t*>(kc) + tile + ((size_t)lane * BS + pos % BS) * 8;
+        new_vdst = const_cast<uint16_t*>(vc) + tile + pos % BS;
+    }
+    auto store_new_row = [&]() {
+        if (lane < D / 8) st16(new_kdst, new_k);
+        for (int i = 0; i < D / kWave; ++i) new_vdst[(size_t)(lane + kWave * i) * BS] = new_v[i];
+    };
+    if (store_first) {
+        store_new_row();
+        __builtin_amdgcn_s_waitcnt(0);                       // stored before any K/V load
     }
 
     // Page ids: scalar loads through the constant address space (the table
     // is read-only during the kernel), issued one chunk ahead of their use.
     // They bypass the vector memory queue that the K/V stream keeps full,
     // and need no LDS staging or barrier.  Ids outside the pool read page 0.
-    typedef const __attribute__((address_space(4))) int* const_row_t;
-    const const_row_t rowc = (const_row_t)row;
-    const int nchunks = (end - start + kChunk - 1) / kChunk;
     const int blk_first = start / BS;
     const int blk_last = (end - 1) / BS;                     // last page the partition uses
     // raw ids of chunk ci's pages; at block 16 the second one repeats the
@@ -214,6 +237,9 @@ void decode_mfma_kernel(DecodeParams p) {
         const int pg0 = clamp_page(__builtin_amdgcn_readfirstlane(next0));
         const int pg1 = clamp_page(__builtin_amdgcn_readfirstlane(next1));
         if (ci + kWaves < nchunks) chunk_pages(ci + kWaves, next0, next1);
+        // the appended row is in this (last) chunk: this wave's own stores of
+        // it complete before the chunk's loads are issued
+        if (append_wave && !store_first && ci == nchunks - 1) __builtin_amdgcn_s_waitcnt(0);
 
         // ---- loads: K of both row tiles, V of every 16-dim tile
         u32x4_t kraw[2][KSTEPS];
@@ -250,6 +276,8 @@ void decode_mfma_kernel(DecodeParams p) {
             for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the appending wave stores the new row behind its first chunk's loads
+        if (append_wave && !store_first && ci == w) store_new_row();
 
         // ---- S = K . Q^T
         f32x4_t st[2];
@@ -348,28 +376,34 @@ void decode_mfma_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int BS, bool SPLIT>
+template <int D, int BS, bool SPLIT, int WAVES>
 hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
-    const size_t smem = sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * p.group * D);
+    const size_t smem = sizeof(float) * (2 * WAVES * 16 + (size_t)WAVES * p.group * D);
     const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * p.max_parts;
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, SPLIT>), dim3((unsigned)nwg), dim3(kThreads), smem,
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, SPLIT, WAVES>), dim3((unsigned)nwg), dim3(WAVES * kWave), smem,
                        stream, p);
     return hipGetLastError();
 }
 
-template <bool SPLIT>
+template <bool SPLIT, int WAVES>
 hipError_t launch_path(const DecodeParams& p, hipStream_t stream) {
     if (p.head_dim == 64)
-        return p.block_size == 16 ? launch_shape<64, 16, SPLIT>(p, stream)
-                                  : launch_shape<64, 32, SPLIT>(p, stream);
-    return p.block_size == 16 ? launch_shape<128, 16, SPLIT>(p, stream)
-                              : launch_shape<128, 32, SPLIT>(p, stream);
+        return p.block_size == 16 ? launch_shape<64, 16, SPLIT, WAVES>(p, stream)
+                                  : launch_shape<64, 32, SPLIT, WAVES>(p, stream);
+    return p.block_size == 16 ? launch_shape<128, 16, SPLIT, WAVES>(p, stream)
+                              : launch_shape<128, 32, SPLIT, WAVES>(p, stream);
 }
 
 }  // namespace
 
+// Streaming loads come in two workgroup sizes: 4 waves (three workgroups
+// share a compute unit, so one's set-up and merge overlap the others'
+// streaming) and 12 waves (one workgroup fills a compute unit, three times
+// the bytes in flight for one (sequence, kv head, partition), which drains
+// long and ragged work units faster).  Shared-page loads always use 4.
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-    return p.stream_kv ? launch_path<true>(p, stream) : launch_path<false>(p, stream);
+    if (!p.stream_kv) return launch_path<false, 4>(p, stream);
+    return p.waves == kWideWaves ? launch_path<true, kWideWaves>(p, stream) : launch_path<true, 4>(p, stream);
 }
 
 }  // namespace pa_impl

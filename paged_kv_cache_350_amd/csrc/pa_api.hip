@@ -23,6 +23,14 @@ constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
 constexpr int32_t kMaxQueryLen = 1024;       // multi-query: new tokens per sequence
 constexpr int64_t kMultiFill = 256;          // multi-query: workgroups that keep every CU busy
 constexpr int32_t kMultiMaxPartition = 8192;
+// streaming-load decode default (see default_stream_partition)
+constexpr int64_t kOnePassPairs = 2048;      // (sequence, kv head) pairs that make a single pass
+constexpr int64_t kOnePassShortPairs = 1024; // ... or this many when no context exceeds
+constexpr int32_t kOnePassShortContext = 4096;
+constexpr int32_t kStreamMinPartition = 1024;
+constexpr int32_t kStreamMaxPartition = 8192;
+constexpr int64_t kStreamFillUnits = 768;    // three 12-wave workgroups per compute unit
+constexpr int32_t kWidePartition = 2048;     // streaming partitions this long run 12-wave workgroups
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -56,11 +64,31 @@ int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_co
     return P;
 }
 
+// Library default for streaming loads (no page shared between sequences).
+// Measured on MI355X over uniform and ragged batches: when the (sequence,
+// kv head) pairs alone give several rounds of 12-wave workgroups, a single
+// pass wins -- no partials, no merge, and the unequal lengths even out over
+// the rounds.  Otherwise the longest power-of-two partition in
+// [kStreamMinPartition, kStreamMaxPartition], shorter than the longest
+// context, that still gives kStreamFillUnits workgroups; the shared-page
+// rule when none does.
+int32_t default_stream_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+    if (max_context_len <= kSplitAbove) return 0;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+    if (pairs >= kOnePassPairs || (pairs >= kOnePassShortPairs && max_context_len <= kOnePassShortContext))
+        return 0;
+    for (int32_t P = kStreamMaxPartition; P >= kStreamMinPartition; P /= 2)
+        if (P < max_context_len && pairs * parts_for(max_context_len, P) >= kStreamFillUnits) return P;
+    return default_partition(num_seqs, num_kv_heads, max_context_len);
+}
+
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                          int32_t partition_size) {
+                          int32_t partition_size, bool stream) {
     if (max_context_len < 0) return -1;
     if (partition_size == -1) return 0;
-    if (partition_size == 0) return default_partition(num_seqs, num_kv_heads, max_context_len);
+    if (partition_size == 0)
+        return stream ? default_stream_partition(num_seqs, num_kv_heads, max_context_len)
+                      : default_partition(num_seqs, num_kv_heads, max_context_len);
     if (partition_size < kChunk || partition_size % kChunk != 0) return -1;
     return partition_size;
 }
@@ -102,7 +130,8 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_ARG;
     if (num_blocks > (int64_t)INT32_MAX + 1) return PA_ERR_ARG;      // table entries are int32
     if (!isfinite(scale)) return PA_ERR_ARG;
-    int32_t partition = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+    int32_t partition = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size,
+                                          reuse != PA_KV_SHARED);
     if (partition < 0) return PA_ERR_ARG;
     if (force_split && partition <= 0) return PA_ERR_ARG;
     if (!force_split && partition > 0 && max_context_len == 0) partition = 0;   // nothing to split
@@ -153,6 +182,12 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.max_context_len = max_context_len;
     p.num_blocks = num_blocks;
     p.stream_kv = reuse != PA_KV_SHARED;
+    // 12-wave workgroups for long streaming work units: partitions of
+    // kWidePartition tokens or more, or a single pass over enough pairs
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    p.waves = p.stream_kv && (partition >= kWidePartition ||
+                              (partition == 0 && pairs >= kOnePassShortPairs && max_context_len > kSplitAbove))
+                  ? pa_impl::kWideWaves : 4;
     p.query_start = nullptr;
     p.num_tokens = 0;
     p.max_query_len = 0;
@@ -227,7 +262,7 @@ int32_t resolve_multi_partition(int32_t num_seqs, int32_t num_heads, int32_t num
     if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0 || max_query_len < 1)
         return -1;
     if (partition_size != 0)
-        return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+        return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size, true);
     if (max_context_len < 0) return -1;
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) *
                           multi_col_groups(num_heads / num_kv_heads, max_query_len) * num_kv_heads;
@@ -254,17 +289,21 @@ const char* pa_status_string(pa_status status) {
     return "unknown status";
 }
 
-int32_t pa_version(void) { return 310; }
+int32_t pa_version(void) { return 320; }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t partition_size) {
-    return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+                                 int32_t partition_size, pa_kv_reuse reuse) {
+    if (reuse != PA_KV_AUTO && reuse != PA_KV_STREAM && reuse != PA_KV_SHARED) return -1;
+    return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size, reuse != PA_KV_SHARED);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+                                int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                                pa_kv_reuse reuse) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-    const int32_t partition = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+    if (reuse != PA_KV_AUTO && reuse != PA_KV_STREAM && reuse != PA_KV_SHARED) return 0;
+    const int32_t partition = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size,
+                                                reuse != PA_KV_SHARED);
     if (partition <= 0) return 0;
     return workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, partition);
 }
@@ -387,7 +426,7 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     if (!valid_dtype(dtype)) return PA_ERR_ARG;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size <= 0) return PA_ERR_ARG;
-    const int32_t partition = resolve_partition(num_seqs, 1, max_context_len, partition_size);
+    const int32_t partition = resolve_partition(num_seqs, 1, max_context_len, partition_size, true);
     if (partition <= 0) return PA_ERR_ARG;
     if ((uint64_t)num_seqs * (uint64_t)num_heads >= kMaxGrid) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;

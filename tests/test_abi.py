@@ -50,7 +50,7 @@ def test_status_strings(L):
         assert pa.status_string(code)
     assert pa.status_string(0) == "ok"
     assert pa.status_string(-99) == "unknown status"
-    assert L.pa_version() == 310
+    assert L.pa_version() == 320
 
 
 def test_partition_policy_and_workspace_size(L):
@@ -60,20 +60,33 @@ def test_partition_policy_and_workspace_size(L):
     assert pa.decode_partition_size(64, 8, 4096, 100) < 0        # not a multiple of 32
     assert pa.decode_partition_size(64, 8, 4096, 16) < 0
     assert pa.decode_partition_size(64, 8, -1, 0) < 0
-    # library default, worked through the rule in pa.h:
+    # library default for streaming loads, worked through the rule in pa.h:
     assert pa.decode_partition_size(64, 8, 512, 0) == 0          # short: single pass
-    assert pa.decode_partition_size(64, 8, 4027, 0) == 512       # 8B-shaped batch: 4 partitions per long context
-    assert pa.decode_partition_size(256, 8, 8192, 0) == 2048     # 70B-shaped batch
+    assert pa.decode_partition_size(64, 8, 4027, 0) == 2048      # 8B-shaped batch: 512 pairs
+    assert pa.decode_partition_size(256, 8, 8192, 0) == 0        # 70B-shaped batch: 2,048 pairs, one pass
+    assert pa.decode_partition_size(128, 8, 2048, 0) == 0        # 1,024 pairs, contexts <= 4,096: one pass
+    assert pa.decode_partition_size(128, 8, 8192, 0) == 4096     # 1,024 pairs, longer contexts
     assert pa.decode_partition_size(8, 8, 32768, 0) == 2048      # long context: 4096 gives only 512 units
-    assert pa.decode_partition_size(100, 8, 10512, 0) == 2048    # prefix sharing
-    assert pa.decode_partition_size(8, 8, 32774, 0) == 2048      # beams
-    assert pa.decode_partition_size(512, 8, 32768, 0) == 4096    # plenty of work
-    assert pa.decode_partition_size(1, 8, 32768, 0) == 256       # one sequence: parallelism first
+    assert pa.decode_partition_size(32, 8, 16384, 0) == 4096
+    assert pa.decode_partition_size(512, 8, 32768, 0) == 0       # plenty of pairs
+    assert pa.decode_partition_size(1, 8, 32768, 0) == 256       # one sequence: the shared-page rule
     assert pa.decode_partition_size(2, 1, 600, 0) == 256
+    assert pa.decode_partition_size(64, 8, 4027, 0, "stream") == 2048
+    # shared pages: the longest partition with 4 per longest context and 1,024 workgroups
+    assert pa.decode_partition_size(64, 8, 4027, 0, "shared") == 512
+    assert pa.decode_partition_size(256, 8, 8192, 0, "shared") == 2048
+    assert pa.decode_partition_size(100, 8, 10512, 0, "shared") == 2048    # prefix sharing
+    assert pa.decode_partition_size(8, 8, 32774, 0, "shared") == 2048      # beams
+    assert pa.decode_partition_size(512, 8, 32768, 0, "shared") == 4096
+    assert pa.decode_partition_size(1, 8, 32768, 0, "shared") == 256
+    assert L.pa_decode_partition_size(64, 8, 4027, 0, 7) < 0            # unknown load path
+    assert L.pa_decode_workspace_size(64, 32, 8, 128, 4027, 0, 7) == 0
     # workspace = seqs x heads x parts x (D + 2) floats
     assert pa.decode_workspace_size(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 64 * 32 * 4 * 130 * 4   # P = 1024 at 4,096
-    assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0) == 256 * 64 * 4 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 64 * 32 * 2 * 130 * 4   # P = 2048 at 4,096
+    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0, "shared") == 64 * 32 * 4 * 130 * 4   # P = 1024
+    assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0) == 0                      # one pass
+    assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0, "shared") == 256 * 64 * 4 * 130 * 4
     assert pa.decode_workspace_size(64, 32, 8, 128, 500, 0) == 0
     assert pa.decode_workspace_size(64, 32, 8, 128, 4096, -1) == 0
     assert pa.decode_workspace_size(3, 4, 4, 64, 33, 32) == 3 * 4 * 2 * 66 * 4

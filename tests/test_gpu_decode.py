@@ -30,7 +30,7 @@ SHAPES = [  # (dtype, block_size, num_heads, num_kv_heads, head_dim)
     ("bf16", 16, 4, 4, 64),
     ("bf16", 16, 10, 2, 128),
 ]
-PATHS = [-1, 0, 32, 96, 512]
+PATHS = [-1, 0, 32, 96, 512, 2048]      # 2048 on streaming loads: 12-wave workgroups
 
 
 def _kernels(dtype):
@@ -212,10 +212,35 @@ def test_group_of_sixteen_and_head_dim_64():
     ref = step_and_reference(pa, w, t, range(w.num_seqs))
     for kernel in ("valu", "mfma"):
         for reuse in REUSE:
-            for ps in (-1, 0, 128):
+            for ps in (-1, 0, 128, 2048):
                 out = run_decode(pa, w, t, kernel, ps, reuse)
                 torch.cuda.synchronize()
                 check_close(out_f64(out), ref, "bf16", f"g16 {kernel} {reuse} P={ps}")
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 8, 128), (32, 32, 2, 128), (32, 16, 8, 64)],
+                         ids=lambda s: "-".join(map(str, s)))
+def test_single_pass_over_many_pairs(shape):
+    """1,024 and more (sequence, kv head) pairs with contexts past 512: the
+    streaming default is one pass of 12-wave workgroups (16 query heads per
+    kv head in the second shape); sampled sequences against the oracle, and
+    the 4-wave split path as a cross-check."""
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    nseq = 1024 // hkv
+    lens = np.random.default_rng(14).integers(1, 1500, size=nseq)
+    lens[3] = 1500
+    w = W.custom("many_pairs", 14, "bf16", lens.tolist(), hq, hkv, d, bs)
+    assert pa.decode_partition_size(w.num_seqs, hkv, w.max_context_len, 0) == 0
+    say("many pairs", shape, w.summary())
+    t = W.make_tensors(w, "cuda")
+    seqs = _sample(w, 10, 15)
+    ref = step_and_reference(pa, w, t, seqs)
+    for ps in (0, -1, 256):
+        out = run_decode(pa, w, t, "mfma", ps, "stream")
+        torch.cuda.synchronize()
+        check_close(out_f64(out)[seqs], ref, "bf16", f"many pairs {shape} P={ps}")
+        assert np.isfinite(out_f64(out)).all()
 
 
 def test_bad_table_entries_stay_in_bounds():
