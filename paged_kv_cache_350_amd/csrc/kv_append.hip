@@ -41,14 +41,56 @@ void kv_append_kernel(const E* __restrict__ k, const E* __restrict__ v,
     const int64_t tile = (page * num_kv_heads + h) * (int64_t)head_dim * block_size;
 
     if (lane < nchunk) {
-        st16(k_cache + tile + ((int64_t)lane * block_size + off) * X, ld16(krow + lane * X));
+        st16_nt(k_cache + tile + ((int64_t)lane * block_size + off) * X, ld16(krow + lane * X));
     }
     for (int d = lane; d < head_dim; d += kWave) {
-        v_cache[tile + (int64_t)d * block_size + off] = vrow[d];
+        st_nt(&v_cache[tile + (int64_t)d * block_size + off], vrow[d]);
     }
 }
 
+// The newest row of each sequence (pa_decode_append's rows, [num_seqs]
+// [num_kv_heads][head_dim]) to position L - 1, with L clamped as the decode
+// kernels clamp it; sequences with L == 0, a negative mask entry or a page
+// id outside the pool store nothing -- the fused append's rules exactly.
+template <typename E>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void append_newest_kernel(DecodeParams p) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    if (row >= (int64_t)p.num_seqs * p.num_kv_heads) return;
+    const int b = (int)(row / p.num_kv_heads);
+    const int h = (int)(row % p.num_kv_heads);
+    const int bs = p.block_size;
+    const int cap = min(p.max_context_len, p.max_blocks_per_seq * bs);
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    if (L == 0 || (p.append_mask != nullptr && p.append_mask[b] < 0)) return;
+    const int page = p.block_tables[(size_t)b * p.max_blocks_per_seq + (L - 1) / bs];
+    if ((uint32_t)page >= (uint64_t)p.num_blocks) return;
+    const int off = (L - 1) % bs;
+    constexpr int X = 16 / sizeof(E);
+    const int D = p.head_dim;
+    const E* krow = reinterpret_cast<const E*>(p.k_new) + row * D;
+    const E* vrow = reinterpret_cast<const E*>(p.v_new) + row * D;
+    const int64_t tile = ((int64_t)page * p.num_kv_heads + h) * (int64_t)D * bs;
+    E* kc = const_cast<E*>(reinterpret_cast<const E*>(p.k_cache));
+    E* vc = const_cast<E*>(reinterpret_cast<const E*>(p.v_cache));
+    if (lane < D / X) st16_nt(kc + tile + ((int64_t)lane * bs + off) * X, ld16(krow + lane * X));
+    for (int d = lane; d < D; d += kWave) st_nt(&vc[tile + (int64_t)d * bs + off], vrow[d]);
+}
+
 }  // namespace
+
+hipError_t launch_append_newest(const DecodeParams& p, pa_dtype dtype, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.num_seqs * p.num_kv_heads;
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    const dim3 block(kRowsPerBlock * kWave);
+    if (dtype == PA_BF16)
+        hipLaunchKernelGGL(append_newest_kernel<uint16_t>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(append_newest_kernel<uint32_t>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slot_mapping,
                             void* k_cache, void* v_cache, int32_t num_tokens,

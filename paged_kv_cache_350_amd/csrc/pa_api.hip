@@ -388,6 +388,16 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = slot_mapping;
+    if (plan.use_mfma && plan.p.waves == pa_impl::kWideWaves && plan.partition == 0) {
+        // One pass of 12-wave workgroups: every workgroup would store its row
+        // while the others stream, which measured 9% slower on a 70B-shaped
+        // batch than storing all rows first in a launch of their own.
+        st = hip_status(pa_impl::launch_append_newest(plan.p, dtype, stream));
+        if (st != PA_OK) return st;
+        plan.p.k_new = nullptr;
+        plan.p.v_new = nullptr;
+        plan.p.append_mask = nullptr;
+    }
     st = launch_plan(plan, stream);
     if (st != PA_OK || plan.partition == 0) return st;
     return launch_reduce(plan, context_lens, out, stream);

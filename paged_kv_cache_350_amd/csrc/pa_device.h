@@ -84,6 +84,20 @@ __device__ __forceinline__ u32x4_t ld16_kv(const void* p) {
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
     *reinterpret_cast<u32x4_t*>(p) = v;
 }
+// Non-temporal stores for K/V rows appended by pa_kv_append: the rows are
+// read by a later kernel, and lines left dirty in L2 by scattered row writes
+// measurably slow that kernel's read stream (a decode over 2,048 (sequence,
+// kv head) pairs ran 20 us slower after an append kernel with ordinary
+// stores, and not measurably slower with these).  The fused appends keep
+// ordinary stores: their own workgroup reads the row back at once, and
+// non-temporal stores made that 5% slower on an 8B-shaped step.
+__device__ __forceinline__ void st16_nt(void* p, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
 
 // Decode work items are (partition-major group q = part * num_kv_heads + g,
 // sequence b).  Workgroups are handed to the XCDs round-robin (id i runs on

@@ -80,6 +80,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* block
                               int32_t block_size, int64_t num_blocks, pa_dtype dtype,
                               hipStream_t stream);
 
+hipError_t launch_append_newest(const DecodeParams& p, pa_dtype dtype, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype dtype, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceParams& p, pa_dtype dtype, hipStream_t stream);

@@ -203,3 +203,53 @@ def test_fused_append_skips_a_page_outside_the_pool():
     rk, rv = oracle.kv_append(storage_np(k_new)[keep], storage_np(v_new)[keep], mask[keep], kc0, vc0, 16)
     assert np.array_equal(storage_np(t["k_cache"]).view(np.uint16), rk.view(np.uint16))
     assert np.array_equal(storage_np(t["v_cache"]).view(np.uint16), rv.view(np.uint16))
+
+
+def test_one_pass_of_wide_workgroups_appends_in_its_own_launch():
+    """1,024 (sequence, kv head) pairs with contexts past 512: the default is
+    one pass of 12-wave workgroups, where pa_decode_append stores the rows in
+    a launch of its own first.  Caches bit-identical to the oracle's append
+    (masked and empty sequences included), output bit-identical to
+    pa_kv_append + pa_decode, sampled rows within tolerance of the oracle."""
+    pa = require_gpu()
+    rng = np.random.default_rng(23)
+    lens = rng.integers(1, 1400, size=128)
+    lens[5] = 1400
+    w = W.custom("wide_fused", 23, "bf16", lens.tolist(), 32, 8, 128, 16)
+    assert pa.decode_partition_size(w.num_seqs, 8, w.max_context_len, 0) == 0
+    t = W.make_tensors(w, "cuda")
+    k_new, v_new, mask, older = newest_rows(w, t)
+    assert not older
+    skip = [7, 40]                                  # appended earlier: nothing to append this step
+    kc0, vc0 = oracle.kv_append(storage_np(k_new[skip]), storage_np(v_new[skip]), mask[skip],
+                                storage_np(t["k_cache"]), storage_np(t["v_cache"]), 16)
+    pa.kv_append(k_new[skip].contiguous(), v_new[skip].contiguous(), torch.from_numpy(mask[skip]).cuda(),
+                 t["k_cache"], t["v_cache"])
+    mask[skip] = -1
+    t["context_lens"][9] = 0                        # and this one has no context at all
+    lens_host = w.context_lens.copy()
+    lens_host[9] = 0
+    written = mask.copy()
+    written[9] = -1
+    rk, rv = oracle.kv_append(storage_np(k_new), storage_np(v_new), written, kc0, vc0, 16)
+    seqs = [0, 5, 7, 9, 40, 77, 127]
+    ref = oracle.decode(storage_np(t["q"])[seqs], rk, rv, w.block_tables[seqs], lens_host[seqs], w.scale, 16,
+                        "bf16")
+    kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+    say("one pass of wide workgroups, fused append")
+    out = pa.decode_append(k_new, v_new, t["q"], kc, vc, t["block_tables"], t["context_lens"], w.scale,
+                           w.max_context_len, slot_mapping=torch.from_numpy(mask).cuda(), reuse="stream")
+    torch.cuda.synchronize()
+    assert np.array_equal(storage_np(kc).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(storage_np(vc).view(np.uint16), rv.view(np.uint16))
+    check_close(out_f64(out)[seqs], ref, "bf16", "wide one pass fused")
+    assert not out_f64(out)[9].any()
+    kc2, vc2 = t["k_cache"].clone(), t["v_cache"].clone()
+    sel = np.flatnonzero(written >= 0)
+    idx = torch.from_numpy(sel).cuda()
+    pa.kv_append(k_new.index_select(0, idx).contiguous(), v_new.index_select(0, idx).contiguous(),
+                 torch.from_numpy(written[sel]).cuda(), kc2, vc2)
+    out2 = pa.decode(t["q"], kc2, vc2, t["block_tables"], t["context_lens"], w.scale, w.max_context_len,
+                     reuse="stream")
+    torch.cuda.synchronize()
+    assert bits_equal(out, out2)
