@@ -108,6 +108,35 @@ __device__ __forceinline__ void st_nt(T* p, T v) {
 // pages they share (a common prefix) are served from that XCD's L2.  Other
 // grids keep the natural order, which spreads consecutive sequences across
 // the XCDs.  Both maps are bijections of [0, num_seqs * nq).
+// Longest-first order: the sequence with the k-th longest context (ties:
+// lower index first), for batches of at most kSortMax sequences (larger ones
+// keep k).  Every workgroup derives it the same way from context_lens, so
+// the map is a bijection of [0, num_seqs): it changes which workgroup runs
+// which sequence, never what any workgroup computes.  Used by one-pass
+// multi-query launches, where every workgroup is resident at once: a
+// random order can leave two long sequences on one compute unit, and
+// ordering by length evens out what each compute unit holds (measured:
+// 120.5 -> 107.7 us on 64 ragged sequences; +1 us on uniform ones).
+constexpr int kSortMax = 256;
+template <int THREADS>
+__device__ __forceinline__ int seq_by_length(const int32_t* lens, int num_seqs, int k, int* s_lens, int* s_pick) {
+    if (num_seqs > kSortMax) return k;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < num_seqs; i += THREADS) s_lens[i] = lens[i];
+    __syncthreads();
+    for (int c = tid; c < num_seqs; c += THREADS) {
+        const int lc = s_lens[c];
+        int rank = 0;
+        for (int j = 0; j < num_seqs; ++j) {
+            const int lj = s_lens[j];
+            rank += (lj > lc) | ((lj == lc) & (j < c));
+        }
+        if (rank == k) *s_pick = c;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_pick);
+}
+
 struct WorkItem {
     int b;
     int q;

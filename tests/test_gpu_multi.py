@@ -224,3 +224,27 @@ def test_loose_max_context_len_changes_nothing():
     out = run(bt, loose, 0)
     torch.cuda.synchronize()
     check_close(out_f64(out), ref, "bf16", "loose multi default")
+
+
+@pytest.mark.parametrize("nseq", [256, 300])
+def test_one_pass_order_by_length_either_side_of_the_limit(nseq):
+    """One-pass launches run sequences longest first for batches of up to 256
+    sequences and in batch order above that; either way every sequence gets
+    its own rows.  Ragged lengths with ties; sampled sequences against the
+    oracle, the rest finite."""
+    pa = require_gpu()
+    rng = np.random.default_rng(49 + nseq)
+    lens = rng.integers(3, 700, size=nseq)
+    lens[::7] = 333                                 # ties, broken by index
+    news = rng.integers(1, 4, size=nseq)
+    w = W.multi_custom("order_limit", 49, lens.tolist(), news.tolist(), 32, 8, 128, 16)
+    t, kc0, vc0, q = prepare(w)
+    seqs = sorted(set([0, 7, 14, int(np.argmax(lens)), int(np.argmin(lens)), nseq - 1] +
+                      rng.choice(nseq, size=6, replace=False).tolist()))
+    ref = oracle_multi(w, kc0, vc0, q, seqs=seqs)
+    say("one pass order, seqs", nseq)
+    out = run_gpu(pa, w, t, partition_size=-1)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(w.query_start[b], w.query_start[b + 1]) for b in seqs])
+    check_close(out_f64(out)[rows], ref[rows], "bf16", f"order {nseq}")
+    assert np.isfinite(out_f64(out)).all()
