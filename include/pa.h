@@ -221,8 +221,10 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
  * The library default (partition_size 0) depends on the load path `reuse`
  * selects, with pairs = num_seqs * num_kv_heads:
  *   streaming loads (PA_KV_AUTO, PA_KV_STREAM): a single pass when
- *     max_context_len <= 512, when pairs >= 2048, or when pairs >= 1024
- *     and max_context_len <= 4096; otherwise the largest power of two P in
+ *     max_context_len <= 512, when pairs >= 2048, when pairs >= 1024 and
+ *     max_context_len <= 4096, or when 512 <= pairs < 1024,
+ *     num_seqs <= 256 and max_context_len <= 8192 (then the workgroups take
+ *     the sequences longest first); otherwise the largest power of two P in
  *     [1024, 8192] with P < max_context_len and
  *     pairs * ceil(max_context_len / P) >= 768; otherwise the shared-page rule.
  *   shared pages (PA_KV_SHARED): a single pass when max_context_len <= 512;
@@ -230,10 +232,12 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
  *     4 P <= max_context_len and pairs * ceil(max_context_len / P) >= 1024
  *     (512 if none qualifies), lowered to 256 when that leaves fewer than
  *     1024 workgroups.
- * On the streaming path, partitions of 2048 tokens or more and single
- * passes over >= 1024 pairs (contexts over 512) run 12-wave workgroups that
- * fill a compute unit each; everything else runs 4-wave workgroups.  The
- * choice changes speed only: either gives results within the same bounds.
+ * On the streaming path, partitions of 2048 tokens or more, single passes
+ * over >= 1024 pairs (contexts over 512) and the longest-first single pass
+ * run 12-wave workgroups that fill a compute unit each; everything else runs
+ * 4-wave workgroups.  These choices change speed only: every one gives
+ * results within the same bounds, and the order in which workgroups take
+ * sequences changes no bit.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size, pa_kv_reuse reuse);

@@ -83,10 +83,10 @@ void decode_multi_kernel(DecodeParams p) {
 
     const WorkItem wi = decode_work_item(blockIdx.x, (uint32_t)p.num_seqs,
                                          (uint32_t)(p.num_kv_heads * p.col_groups * p.max_parts));
-    __shared__ int s_lens[kSortMax];
+    __shared__ __align__(16) int s_lens[kSortMax];
     __shared__ int s_pick;
-    const int b = p.max_parts == 1 ? seq_by_length<kThreads>(p.context_lens, p.num_seqs, wi.b, s_lens, &s_pick)
-                                   : wi.b;                   // launch-uniform choice
+    const int b = p.order_by_length ? seq_by_length<kThreads>(p.context_lens, p.num_seqs, wi.b, s_lens, &s_pick)
+                                    : wi.b;                  // launch-uniform choice
     const int g = wi.q % p.num_kv_heads;
     const int cg = (wi.q / p.num_kv_heads) % p.col_groups;
     const int slot = wi.q / (p.num_kv_heads * p.col_groups);

@@ -31,6 +31,11 @@ constexpr int32_t kStreamMinPartition = 1024;
 constexpr int32_t kStreamMaxPartition = 8192;
 constexpr int64_t kStreamFillUnits = 768;    // three 12-wave workgroups per compute unit
 constexpr int32_t kWidePartition = 2048;     // streaming partitions this long run 12-wave workgroups
+constexpr int64_t kOrderedPairs = 512;       // one pass, longest sequences first, from this many pairs ...
+constexpr int64_t kOrderedPairsEnd = 1024;   // ... up to (not including) this many: two to four rounds
+constexpr int32_t kOrderedContext = 8192;    // and no context longer than this
+constexpr int64_t kMultiOrderedUnits = 1024; // multi-query one pass: longest first up to this many workgroups
+constexpr int32_t kSortMaxSeqs = pa_impl::kSortMax;   // the kernels rank at most this many sequences
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -64,11 +69,21 @@ int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_co
     return P;
 }
 
+// One pass with the workgroups taking sequences longest first: 512 to 1023
+// (sequence, kv head) pairs (two to four rounds of 12-wave workgroups), at
+// most kSortMaxSeqs sequences, no context past kOrderedContext.
+bool ordered_one_pass(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    return pairs >= kOrderedPairs && pairs < kOrderedPairsEnd && num_seqs <= kSortMaxSeqs &&
+           max_context_len > kSplitAbove && max_context_len <= kOrderedContext;
+}
+
 // Library default for streaming loads (no page shared between sequences).
 // Measured on MI355X over uniform and ragged batches: when the (sequence,
 // kv head) pairs alone give several rounds of 12-wave workgroups, a single
 // pass wins -- no partials, no merge, and the unequal lengths even out over
-// the rounds.  Otherwise the longest power-of-two partition in
+// the rounds; with two to four rounds it wins when the workgroups take the
+// longest sequences first.  Otherwise the longest power-of-two partition in
 // [kStreamMinPartition, kStreamMaxPartition], shorter than the longest
 // context, that still gives kStreamFillUnits workgroups; the shared-page
 // rule when none does.
@@ -77,6 +92,7 @@ int32_t default_stream_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t
     const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
     if (pairs >= kOnePassPairs || (pairs >= kOnePassShortPairs && max_context_len <= kOnePassShortContext))
         return 0;
+    if (ordered_one_pass(num_seqs, num_kv_heads, max_context_len)) return 0;
     for (int32_t P = kStreamMaxPartition; P >= kStreamMinPartition; P /= 2)
         if (P < max_context_len && pairs * parts_for(max_context_len, P) >= kStreamFillUnits) return P;
     return default_partition(num_seqs, num_kv_heads, max_context_len);
@@ -185,9 +201,11 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     // 12-wave workgroups for long streaming work units: partitions of
     // kWidePartition tokens or more, or a single pass over enough pairs
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-    p.waves = p.stream_kv && (partition >= kWidePartition ||
+    const bool ordered = p.stream_kv && partition == 0 && ordered_one_pass(num_seqs, num_kv_heads, max_context_len);
+    p.waves = p.stream_kv && (partition >= kWidePartition || ordered ||
                               (partition == 0 && pairs >= kOnePassShortPairs && max_context_len > kSplitAbove))
                   ? pa_impl::kWideWaves : 4;
+    p.order_by_length = ordered ? 1 : 0;
     p.query_start = nullptr;
     p.num_tokens = 0;
     p.max_query_len = 0;
@@ -555,6 +573,9 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
     p.col_groups = col_groups;
     p.k_new = k_new;
     p.v_new = v_new;
+    // one pass of at most four rounds of workgroups: longest sequences first
+    p.order_by_length = partition == 0 && num_seqs <= kSortMaxSeqs &&
+                        (int64_t)num_seqs * col_groups * num_kv_heads <= kMultiOrderedUnits;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;

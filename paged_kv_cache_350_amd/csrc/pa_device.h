@@ -99,6 +99,45 @@ __device__ __forceinline__ void st_nt(T* p, T v) {
     __builtin_nontemporal_store(v, p);
 }
 
+// Longest-first order: the sequence with the k-th longest context (ties:
+// lower index first; negative lengths count as 0), for batches of at most
+// kSortMax sequences (s_lens holds kSortMax entries).  Every workgroup
+// derives it the same way from context_lens, so the map is a bijection of
+// [0, num_seqs): it changes which workgroup runs which sequence, never what
+// any workgroup computes.  The host turns it on for one-pass launches of
+// two to four rounds of workgroups, where a random order leaves the longest
+// sequences for the last round or puts two of them on one compute unit
+// (measured: 8B-shaped decode 101.2 -> 92.7 us, 64 ragged speculative-
+// verification sequences 120.5 -> 107.7 us).  Each workgroup pays a load of
+// every length and a rank loop, which costs more than it gains once there
+// are many rounds of short work.
+template <int THREADS>
+__device__ __forceinline__ int seq_by_length(const int32_t* lens, int num_seqs, int k, int* s_lens, int* s_pick) {
+    const int tid = threadIdx.x;
+    const int padded = (num_seqs + 3) & ~3;
+    for (int i = tid; i < padded; i += THREADS) {
+        const int v = i < num_seqs ? lens[i] : 0;
+        s_lens[i] = i < num_seqs ? (v < 0 ? 0 : v) : INT_MIN;     // padding ranks last
+    }
+    __syncthreads();
+    for (int c = tid; c < num_seqs; c += THREADS) {
+        const int lc = s_lens[c];
+        int rank = 0;
+        const int4* s4 = reinterpret_cast<const int4*>(s_lens);
+        for (int j4 = 0; j4 < padded / 4; ++j4) {
+            const int4 v = s4[j4];
+            const int j = 4 * j4;
+            rank += (v.x > lc) | ((v.x == lc) & (j < c));
+            rank += (v.y > lc) | ((v.y == lc) & (j + 1 < c));
+            rank += (v.z > lc) | ((v.z == lc) & (j + 2 < c));
+            rank += (v.w > lc) | ((v.w == lc) & (j + 3 < c));
+        }
+        if (rank == k) *s_pick = c;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_pick);
+}
+
 // Decode work items are (partition-major group q = part * num_kv_heads + g,
 // sequence b).  Workgroups are handed to the XCDs round-robin (id i runs on
 // XCD i % 8).  When the number of groups nq is a multiple of 8, XCD x is given
@@ -108,35 +147,6 @@ __device__ __forceinline__ void st_nt(T* p, T v) {
 // pages they share (a common prefix) are served from that XCD's L2.  Other
 // grids keep the natural order, which spreads consecutive sequences across
 // the XCDs.  Both maps are bijections of [0, num_seqs * nq).
-// Longest-first order: the sequence with the k-th longest context (ties:
-// lower index first), for batches of at most kSortMax sequences (larger ones
-// keep k).  Every workgroup derives it the same way from context_lens, so
-// the map is a bijection of [0, num_seqs): it changes which workgroup runs
-// which sequence, never what any workgroup computes.  Used by one-pass
-// multi-query launches, where every workgroup is resident at once: a
-// random order can leave two long sequences on one compute unit, and
-// ordering by length evens out what each compute unit holds (measured:
-// 120.5 -> 107.7 us on 64 ragged sequences; +1 us on uniform ones).
-constexpr int kSortMax = 256;
-template <int THREADS>
-__device__ __forceinline__ int seq_by_length(const int32_t* lens, int num_seqs, int k, int* s_lens, int* s_pick) {
-    if (num_seqs > kSortMax) return k;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < num_seqs; i += THREADS) s_lens[i] = lens[i];
-    __syncthreads();
-    for (int c = tid; c < num_seqs; c += THREADS) {
-        const int lc = s_lens[c];
-        int rank = 0;
-        for (int j = 0; j < num_seqs; ++j) {
-            const int lj = s_lens[j];
-            rank += (lj > lc) | ((lj == lc) & (j < c));
-        }
-        if (rank == k) *s_pick = c;
-    }
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(*s_pick);
-}
-
 struct WorkItem {
     int b;
     int q;

@@ -11,6 +11,7 @@ namespace pa_impl {
 
 // Everything a decode launch needs, resolved and validated on the host.
 constexpr int kWideWaves = 12;   // decode workgroup that fills a compute unit (3 waves per SIMD)
+constexpr int kSortMax = 256;    // sequences the kernels rank for longest-first order
 
 struct DecodeParams {
     const void* q;
@@ -38,6 +39,7 @@ struct DecodeParams {
     int32_t split;         // 1: write partials to ws, 0: write out
     int32_t stream_kv;     // 1: no page is shared between sequences (streaming loads)
     int32_t waves;         // decode kernel: waves per workgroup (4, or 12 to fill a compute unit)
+    int32_t order_by_length;  // 1: workgroups take sequences longest first (one-pass launches)
     // multi-query launches only (null / 0 otherwise)
     const int32_t* query_start;   // [num_seqs + 1]: query rows of each sequence
     int32_t num_tokens;    // rows of q / out

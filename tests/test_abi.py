@@ -62,7 +62,7 @@ def test_partition_policy_and_workspace_size(L):
     assert pa.decode_partition_size(64, 8, -1, 0) < 0
     # library default for streaming loads, worked through the rule in pa.h:
     assert pa.decode_partition_size(64, 8, 512, 0) == 0          # short: single pass
-    assert pa.decode_partition_size(64, 8, 4027, 0) == 2048      # 8B-shaped batch: 512 pairs
+    assert pa.decode_partition_size(64, 8, 4027, 0) == 0         # 8B-shaped batch: 512 pairs, longest first
     assert pa.decode_partition_size(256, 8, 8192, 0) == 0        # 70B-shaped batch: 2,048 pairs, one pass
     assert pa.decode_partition_size(128, 8, 2048, 0) == 0        # 1,024 pairs, contexts <= 4,096: one pass
     assert pa.decode_partition_size(128, 8, 8192, 0) == 4096     # 1,024 pairs, longer contexts
@@ -71,7 +71,10 @@ def test_partition_policy_and_workspace_size(L):
     assert pa.decode_partition_size(512, 8, 32768, 0) == 0       # plenty of pairs
     assert pa.decode_partition_size(1, 8, 32768, 0) == 256       # one sequence: the shared-page rule
     assert pa.decode_partition_size(2, 1, 600, 0) == 256
-    assert pa.decode_partition_size(64, 8, 4027, 0, "stream") == 2048
+    assert pa.decode_partition_size(64, 8, 4027, 0, "stream") == 0
+    assert pa.decode_partition_size(64, 8, 16384, 0) == 8192     # 512 pairs, but contexts past 8,192
+    assert pa.decode_partition_size(300, 2, 4027, 0) == 2048     # 600 pairs, but more than 256 sequences
+    assert pa.decode_partition_size(63, 8, 4027, 0) == 2048      # 504 pairs: below the ordered one pass
     # shared pages: the longest partition with 4 per longest context and 1,024 workgroups
     assert pa.decode_partition_size(64, 8, 4027, 0, "shared") == 512
     assert pa.decode_partition_size(256, 8, 8192, 0, "shared") == 2048
@@ -83,7 +86,8 @@ def test_partition_policy_and_workspace_size(L):
     assert L.pa_decode_workspace_size(64, 32, 8, 128, 4027, 0, 7) == 0
     # workspace = seqs x heads x parts x (D + 2) floats
     assert pa.decode_workspace_size(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 64 * 32 * 2 * 130 * 4   # P = 2048 at 4,096
+    assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0) == 0                       # one pass
+    assert pa.decode_workspace_size(63, 32, 8, 128, 4096, 0) == 63 * 32 * 2 * 130 * 4   # P = 2048 at 4,096
     assert pa.decode_workspace_size(64, 32, 8, 128, 4096, 0, "shared") == 64 * 32 * 4 * 130 * 4   # P = 1024
     assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0) == 0                      # one pass
     assert pa.decode_workspace_size(256, 64, 8, 128, 8192, 0, "shared") == 256 * 64 * 4 * 130 * 4

@@ -292,3 +292,39 @@ def test_loose_max_context_len_changes_nothing():
                         partition_size=0, kernel=kernel)
         torch.cuda.synchronize()
         check_close(out_f64(out), ref, "bf16", f"loose default {kernel}")
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 8, 128), (32, 16, 4, 64)], ids=lambda s: "-".join(map(str, s)))
+def test_longest_first_one_pass(shape):
+    """512 to 1,023 (sequence, kv head) pairs: one pass of 12-wave workgroups
+    taking the sequences longest first.  Ragged lengths with ties and a
+    sequence of length 0; bit-identical to the same one pass in batch order
+    reached through a permuted batch (the order changes no bit), and sampled
+    sequences against the oracle."""
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    nseq = 768 // hkv
+    rng = np.random.default_rng(16)
+    lens = rng.integers(1, 3000, size=nseq)
+    lens[::5] = 1234                                 # ties
+    w = W.custom("longest_first", 16, "bf16", lens.tolist(), hq, hkv, d, bs)
+    assert pa.decode_partition_size(w.num_seqs, hkv, w.max_context_len, 0) == 0
+    t = W.make_tensors(w, "cuda")
+    t["context_lens"][2] = 0
+    w.context_lens = w.context_lens.copy()
+    w.context_lens[2] = 0
+    seqs = sorted(set([0, 2, 5, 10, int(np.argmax(w.context_lens)), nseq - 1] +
+                      rng.choice(nseq, size=6, replace=False).tolist()))
+    ref = step_and_reference(pa, w, t, seqs)
+    say("longest first", shape, w.summary())
+    out = run_decode(pa, w, t, "mfma", 0, "stream")
+    torch.cuda.synchronize()
+    check_close(out_f64(out)[seqs], ref, "bf16", f"longest first {shape}")
+    assert not out_f64(out)[2].any()
+    # the same batch reversed: each sequence lands in another workgroup
+    perm = torch.arange(nseq - 1, -1, -1, device="cuda")
+    out_r = pa.decode(t["q"][perm].contiguous(), t["k_cache"], t["v_cache"], t["block_tables"][perm].contiguous(),
+                      t["context_lens"][perm].contiguous(), w.scale, w.max_context_len, partition_size=0,
+                      kernel="mfma", reuse="stream")
+    torch.cuda.synchronize()
+    assert bits_equal(out_r[perm].contiguous(), out)
