@@ -185,8 +185,8 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * which uses the new rows directly.  The result -- cache contents and
  * output -- is bit-identical to pa_kv_append with those slots followed by
  * pa_decode with the same arguments, and saves one launch and the append's
- * dependent memory round trips.  One exception in how, not what: when the
- * streaming default is a single pass of 12-wave workgroups (see
+ * dependent memory round trips.  One exception in how, not what: on a
+ * single pass of 12-wave workgroups over >= 1024 pairs (see
  * pa_decode_partition_size), the rows are stored by a launch of their own
  * just before the decode, which measured faster there.  [Internals, "How
  * PagedAttention Works" items 2 and 3]

@@ -406,10 +406,12 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = slot_mapping;
-    if (plan.use_mfma && plan.p.waves == pa_impl::kWideWaves && plan.partition == 0) {
-        // One pass of 12-wave workgroups: every workgroup would store its row
-        // while the others stream, which measured 9% slower on a 70B-shaped
-        // batch than storing all rows first in a launch of their own.
+    if (plan.use_mfma && plan.p.waves == pa_impl::kWideWaves && plan.partition == 0 && !plan.p.order_by_length) {
+        // One pass of 12-wave workgroups over many rounds: every workgroup
+        // would store its row while the others stream, which measured 9%
+        // slower on a 70B-shaped batch than storing all rows first in a
+        // launch of their own.  The longest-first pass (two to four rounds)
+        // keeps the fused stores: 95.2 against 96.9 us on an 8B-shaped step.
         st = hip_status(pa_impl::launch_append_newest(plan.p, dtype, stream));
         if (st != PA_OK) return st;
         plan.p.k_new = nullptr;
