@@ -54,11 +54,12 @@ int32_t parts_for(int32_t max_context_len, int32_t partition) {
     return (int32_t)(((int64_t)max_context_len + partition - 1) / partition);
 }
 
-// Library default: the longest partition that still leaves at least 4
-// partitions in the longest context and kFillUnits (sequence, kv head,
-// partition) workgroups; longer partitions mean fewer partials to write and
-// merge and less per-workgroup set-up, shorter ones better balance over
-// ragged lengths.  Tiny batches drop to kMinPartition for parallelism.
+// Library default for shared pages (and the streaming rule's fallback): the
+// longest partition that still leaves at least 4 partitions in the longest
+// context and kFillUnits (sequence, kv head, partition) workgroups; longer
+// partitions mean fewer partials to write and merge and less per-workgroup
+// set-up, shorter ones better balance over ragged lengths.  Tiny batches drop
+// to kMinPartition for parallelism.
 int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
     if (max_context_len <= kSplitAbove) return 0;
     const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
