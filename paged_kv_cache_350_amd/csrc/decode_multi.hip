@@ -147,16 +147,24 @@ void decode_multi_kernel(DecodeParams p) {
 
     // Fused append (pa_decode_multi_append): new token j's K and V rows (row
     // row0 + j of k_new / v_new, aligned with q) belong at position
-    // L - n + j.  Every workgroup stores the new rows that fall inside the
-    // positions it reads, then a barrier makes them visible to all its
-    // waves; so whoever reads a new row has written it itself.  Column groups of one (sequence, kv head) store the same bytes,
-    // which cannot change what either reads.  A page id outside the pool
-    // writes nothing.
-    if (p.k_new != nullptr) {
-        const int first_new = max(start, L - n);
-        const int count = end - first_new;                   // may be <= 0
-        const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new);
-        const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new);
+    // L - n + j.  A workgroup handles the new rows that fall inside the
+    // positions it reads.  Up to kPatchRows of them (the usual case): it
+    // copies them into LDS, its waves patch them into the registers of the
+    // chunk that holds them (whose loads read the slots before the append),
+    // and the rows go to the cache after the loop, when this workgroup reads
+    // nothing more -- nothing waits on the stores.  More rows: they are
+    // stored first and a barrier publishes them to every wave.  Column
+    // groups of one (sequence, kv head) store the same bytes, which cannot
+    // change what either reads.  A page id outside the pool writes nothing.
+    constexpr int kPatchRows = 32;                           // LDS: 32 x 2 x D bf16 fits in sacc
+    const int first_new = p.k_new != nullptr ? max(start, L - n) : end;
+    const int count = end - first_new;                       // new rows read here (<= 0: none)
+    const bool patch = count > 0 && count <= kPatchRows;     // workgroup-uniform
+    uint16_t* s_new = reinterpret_cast<uint16_t*>(sacc);     // [count][K row | V row]
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new);
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new);
+    auto new_src = [&](int pos) { return ((size_t)(qr.row0 + pos - (L - n)) * kv_heads + g) * D; };
+    auto store_new_rows = [&]() {                            // rows [first_new, end) to the cache
         uint16_t* kw = const_cast<uint16_t*>(kc);
         uint16_t* vw = const_cast<uint16_t*>(vc);
         for (int e = tid; e < count * (D / 8); e += kThreads) {          // K: 16-byte chunks
@@ -164,20 +172,32 @@ void decode_multi_kernel(DecodeParams p) {
             const int c = e % (D / 8);
             const int pg = row[pos / BS];
             if ((uint32_t)pg >= (uint64_t)p.num_blocks) continue;
-            const size_t src = ((size_t)(qr.row0 + pos - (L - n)) * kv_heads + g) * D;
             const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
-            st16(kw + tile + ((size_t)c * BS + pos % BS) * 8, ld16(kn + src + 8 * c));
+            const u32x4_t v = patch ? *reinterpret_cast<const u32x4_t*>(s_new + (size_t)(pos - first_new) * 2 * D + 8 * c)
+                                    : ld16(kn + new_src(pos) + 8 * c);
+            st16(kw + tile + ((size_t)c * BS + pos % BS) * 8, v);
         }
         for (int e = tid; e < count * D; e += kThreads) {                // V: one element per dim
             const int pos = first_new + e / D;
             const int d = e % D;
             const int pg = row[pos / BS];
             if ((uint32_t)pg >= (uint64_t)p.num_blocks) continue;
-            const size_t src = ((size_t)(qr.row0 + pos - (L - n)) * kv_heads + g) * D;
             const size_t tile = ((size_t)pg * kv_heads + g) * tile_elems;
-            vw[tile + (size_t)d * BS + pos % BS] = vn[src + d];
+            vw[tile + (size_t)d * BS + pos % BS] = patch ? s_new[(size_t)(pos - first_new) * 2 * D + D + d]
+                                                         : vn[new_src(pos) + d];
         }
-        __syncthreads();                 // k_new is a launch parameter: uniform
+    };
+    if (patch) {
+        for (int e = tid; e < count * (D / 4); e += kThreads) {          // K and V rows, 16 bytes at a time
+            const int rr = e / (D / 4);
+            const int c = e % (D / 4);                       // chunks 0 .. D/8-1: K, then V
+            const uint16_t* src = (c < D / 8 ? kn : vn) + new_src(first_new + rr) + 8 * (c % (D / 8));
+            *reinterpret_cast<u32x4_t*>(s_new + (size_t)rr * 2 * D + 8 * c) = ld16(src);
+        }
+        __syncthreads();
+    } else if (count > 0) {
+        store_new_rows();
+        __syncthreads();
     }
 
     // Page ids: scalar loads through the constant address space (the table
@@ -224,6 +244,35 @@ void decode_multi_kernel(DecodeParams p) {
             __builtin_amdgcn_sched_barrier(0);
             for (int dc = 0; dc < DC; ++dc)
                 vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+        }
+        if (patch && cstart + kChunk > first_new) {          // wave-uniform: new rows in this chunk
+            // One small group at a time (scheduling barriers between them), so the
+            // patch never holds more than a few LDS values in registers.
+            // K: lane (r, j) holds token 16 t + r, 16-byte columns 4 s + j
+            for (int t = 0; t < 2; ++t) {
+                const int pos = cstart + kHalf * t + r;
+                const bool is_new = pos >= first_new && pos < end;
+                const uint16_t* src = s_new + (size_t)(is_new ? pos - first_new : 0) * 2 * D;
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + 8 * (4 * s + j));
+                    kraw[t][s] = is_new ? v : kraw[t][s];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // V: dword q of vop[dc] holds tokens slot_token(q / 2, 2 (q % 2), j) and the next, dim 16 dc + r
+            for (int q = 0; q < 4; ++q) {
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int pos = cstart + slot_token(q / 2, 2 * (q % 2) + hh, j);
+                    const bool is_new = pos >= first_new && pos < end;
+                    const uint16_t* src = s_new + (size_t)(is_new ? pos - first_new : 0) * 2 * D + D;
+                    const uint32_t sh = 16u * (uint32_t)hh;
+                    for (int dc = 0; dc < DC; ++dc) {
+                        const uint32_t nv = ((uint32_t)src[16 * dc + r] << sh) | (vop[dc][q] & ~(0xffffu << sh));
+                        vop[dc][q] = is_new ? nv : vop[dc][q];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
 
         // wave-uniform: does any score of this chunk need masking?
@@ -283,6 +332,11 @@ void decode_multi_kernel(DecodeParams p) {
         for (int nt = 0; nt < NT; ++nt)
             for (int dc = 0; dc < DC; ++dc)
                 acc[nt][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf[nt], acc[nt][dc], 0, 0, 0);
+    }
+
+    if (patch) {
+        store_new_rows();                                    // from LDS; nothing here reads them
+        __syncthreads();                                     // before the merge reuses that LDS
     }
 
     // ---- merge the four waves, one tile at a time through the same LDS
