@@ -2,7 +2,9 @@
 //
 // Same contract as the vector-ALU kernel: one workgroup per (sequence, kv
 // head, partition), all G <= 16 query heads of the kv head at once, K/V read
-// in place through the block table.  [PagedAttention Internals, "How
+// in place through the block table.  A workgroup has 4 or 12 waves (the
+// template parameter WAVES); its waves take the partition's 32-token chunks
+// in turn and merge their partial softmax states in LDS at the end.  [PagedAttention Internals, "How
 // PagedAttention Works" item 3; What is PagedAttention?, "On-the-Fly CUDA
 // Block Fetching"]
 //
@@ -338,7 +340,7 @@ void decode_mfma_kernel(DecodeParams p) {
             acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[dc]), pf, acc[dc], 0, 0, 0);
     }
 
-    // ---- merge the four waves; lane (hl, j) holds dims 16 dc + 4 j + i of head hl
+    // ---- merge the waves; lane (hl, j) holds dims 16 dc + 4 j + i of head hl
     l_run = sum_xor16(l_run);
     l_run = sum_xor32(l_run);
     if (lane < 16) {
