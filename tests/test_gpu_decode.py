@@ -328,3 +328,26 @@ def test_longest_first_one_pass(shape):
                       kernel="mfma", reuse="stream")
     torch.cuda.synchronize()
     assert bits_equal(out_r[perm].contiguous(), out)
+
+
+@pytest.mark.parametrize("nseq", [256, 257])
+def test_longest_first_limit_on_sequences(nseq):
+    """512-odd pairs from 256 sequences of 2 kv heads take the longest-first
+    pass; 257 sequences exceed what the kernels rank and take the split rule.
+    Both against the oracle on sampled sequences, contexts ragged with ties."""
+    pa = require_gpu()
+    rng = np.random.default_rng(17 + nseq)
+    lens = rng.integers(1, 1200, size=nseq)
+    lens[::9] = 700
+    lens[1] = 1200
+    w = W.custom("seq_limit", 17, "bf16", lens.tolist(), 16, 2, 128, 16)
+    P = pa.decode_partition_size(w.num_seqs, 2, w.max_context_len, 0)
+    assert (P == 0) == (nseq == 256)
+    t = W.make_tensors(w, "cuda")
+    seqs = sorted(set([0, 1, 9, 18, nseq - 1] + rng.choice(nseq, size=7, replace=False).tolist()))
+    ref = step_and_reference(pa, w, t, seqs)
+    say("sequence limit", nseq, "partition", P)
+    out = run_decode(pa, w, t, "mfma", 0, "stream")
+    torch.cuda.synchronize()
+    check_close(out_f64(out)[seqs], ref, "bf16", f"seq limit {nseq}")
+    assert np.isfinite(out_f64(out)).all()
