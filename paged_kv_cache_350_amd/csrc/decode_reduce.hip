@@ -88,28 +88,32 @@ void decode_reduce_kernel(ReduceParams p) {
     const size_t pairs = (size_t)p.num_seqs * p.num_heads;
     if (bh >= pairs) return;
     const int b = (int)(bh / (size_t)p.num_heads);
-    const int L = p.query_start ? token_context(p, b) : clamp_len(p.context_lens[b], p.max_context_len);
-    int n = (L + p.partition - 1) / p.partition;
-    n = n > p.max_parts ? p.max_parts : n;
-
     const size_t rows = ws_rows(p.num_seqs, p.num_heads, p.max_parts);
     const float* acc = p.ws + bh * p.max_parts * D;
     const float* wm = p.ws + rows * D + bh * p.max_parts;
     const float* wl = p.ws + rows * D + rows + bh * p.max_parts;
     E* out = reinterpret_cast<E*>(p.out) + bh * D;
 
-    // The first kPre partitions' accumulator slices do not depend on the
-    // maxima: their loads go out together with those of m and l.
+    // Loads that do not depend on the context length go out before it is
+    // known: the first kPre partitions' accumulator slices and this lane's
+    // max and sum among the first kWave partitions.  Every slot below
+    // max_parts lies inside the workspace row; slots past the sequence's
+    // own partitions hold stale values and are masked once n is known.
     vec_t pre[kPre];
     {
         const float* row = acc + DPL * lane;
-        for (int u = 0; u < kPre; ++u) {
-            if (u < n) pre[u] = *reinterpret_cast<const vec_t*>(row + (size_t)u * D);
-            else pre[u] = vec_t{};
-        }
+        for (int u = 0; u < kPre; ++u)
+            pre[u] = u < p.max_parts ? *reinterpret_cast<const vec_t*>(row + (size_t)u * D) : vec_t{};
     }
-    float M = neg_inf();
-    for (int q = lane; q < n; q += kWave) M = fmaxf(M, wm[q]);
+    const float m0 = lane < p.max_parts ? wm[lane] : neg_inf();
+    const float l0 = lane < p.max_parts ? wl[lane] : 0.f;
+
+    const int L = p.query_start ? token_context(p, b) : clamp_len(p.context_lens[b], p.max_context_len);
+    int n = (L + p.partition - 1) / p.partition;
+    n = n > p.max_parts ? p.max_parts : n;
+
+    float M = lane < n ? m0 : neg_inf();
+    for (int q = lane + kWave; q < n; q += kWave) M = fmaxf(M, wm[q]);
     M = wave_max(M);
 
     float a[DPL];
@@ -117,8 +121,9 @@ void decode_reduce_kernel(ReduceParams p) {
     float den = 0.f;
     for (int base = 0; base < n; base += kWave) {
         const int q = base + lane;
-        const float wq = q < n ? fast_exp2(wm[q] - M) : 0.f;
-        den = fmaf(wq, q < n ? wl[q] : 0.f, den);
+        const float mq = q < n ? (base == 0 ? m0 : wm[q]) : 0.f;
+        const float wq = q < n ? fast_exp2(mq - M) : 0.f;
+        den = fmaf(wq, q < n ? (base == 0 ? l0 : wl[q]) : 0.f, den);
         const int cnt = min(kWave, n - base);
         const float* row = acc + (size_t)base * D + DPL * lane;
         int k = 0;

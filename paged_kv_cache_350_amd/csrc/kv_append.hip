@@ -16,6 +16,41 @@ namespace pa_impl {
 namespace {
 
 constexpr int kRowsPerBlock = 4;   // four wavefronts, one row pair each
+constexpr int kMaxVPerLane = 2;    // V elements per lane: head_dim <= 128
+
+// A row pair's source values, loaded before the destination is known: the
+// loads go out together with the slot (or length and table) loads instead
+// of after them, so a launch waits for one memory round trip less.
+template <typename E>
+struct SourceRow {
+    u32x4_t k;                 // lane's 16-byte K chunk (lanes < head_dim * sizeof(E) / 16)
+    E v[kMaxVPerLane];         // V elements lane, lane + 64
+};
+
+template <typename E>
+__device__ __forceinline__ SourceRow<E> load_source(const E* krow, const E* vrow, int lane, int head_dim) {
+    constexpr int X = 16 / sizeof(E);
+    SourceRow<E> src;
+    src.k = lane < head_dim / X ? ld16(krow + lane * X) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kMaxVPerLane; ++i) {
+        const int d = lane + kWave * i;
+        src.v[i] = d < head_dim ? vrow[d] : E{};
+    }
+    return src;
+}
+
+// Store a row pair into slot `off` of page tile `tile` (bit copy): K as
+// 16-byte chunks into [chunk][off][X], V element by element into [d][off].
+template <typename E>
+__device__ __forceinline__ void store_row(E* k_cache, E* v_cache, int64_t tile, int off, int block_size,
+                                          int head_dim, int lane, const SourceRow<E>& src) {
+    constexpr int X = 16 / sizeof(E);
+    if (lane < head_dim / X) st16_nt(k_cache + tile + ((int64_t)lane * block_size + off) * X, src.k);
+    for (int i = 0; i < kMaxVPerLane; ++i) {
+        const int d = lane + kWave * i;
+        if (d < head_dim) st_nt(&v_cache[tile + (int64_t)d * block_size + off], src.v[i]);
+    }
+}
 
 template <typename E>
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
@@ -29,23 +64,13 @@ void kv_append_kernel(const E* __restrict__ k, const E* __restrict__ v,
     if (row >= (int64_t)num_tokens * num_kv_heads) return;
     const int64_t tok = row / num_kv_heads;
     const int h = (int)(row % num_kv_heads);
+    const SourceRow<E> src = load_source(k + row * head_dim, v + row * head_dim, lane, head_dim);
     const int64_t slot = slot_mapping[tok];
     if (slot < 0 || slot >= num_blocks * block_size) return;   // padding / out of range
     const int64_t page = slot / block_size;
     const int off = (int)(slot % block_size);
-
-    constexpr int X = 16 / sizeof(E);          // elements per 16-byte chunk
-    const int nchunk = head_dim / X;
-    const E* krow = k + row * head_dim;
-    const E* vrow = v + row * head_dim;
     const int64_t tile = (page * num_kv_heads + h) * (int64_t)head_dim * block_size;
-
-    if (lane < nchunk) {
-        st16_nt(k_cache + tile + ((int64_t)lane * block_size + off) * X, ld16(krow + lane * X));
-    }
-    for (int d = lane; d < head_dim; d += kWave) {
-        st_nt(&v_cache[tile + (int64_t)d * block_size + off], vrow[d]);
-    }
+    store_row(k_cache, v_cache, tile, off, block_size, head_dim, lane, src);
 }
 
 // The newest row of each sequence (pa_decode_append's rows, [num_seqs]
@@ -61,6 +86,9 @@ void append_newest_kernel(DecodeParams p) {
     const int b = (int)(row / p.num_kv_heads);
     const int h = (int)(row % p.num_kv_heads);
     const int bs = p.block_size;
+    const int D = p.head_dim;
+    const SourceRow<E> src = load_source(reinterpret_cast<const E*>(p.k_new) + row * D,
+                                         reinterpret_cast<const E*>(p.v_new) + row * D, lane, D);
     const int cap = min(p.max_context_len, p.max_blocks_per_seq * bs);
     int L = p.context_lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -68,15 +96,9 @@ void append_newest_kernel(DecodeParams p) {
     const int page = p.block_tables[(size_t)b * p.max_blocks_per_seq + (L - 1) / bs];
     if ((uint32_t)page >= (uint64_t)p.num_blocks) return;
     const int off = (L - 1) % bs;
-    constexpr int X = 16 / sizeof(E);
-    const int D = p.head_dim;
-    const E* krow = reinterpret_cast<const E*>(p.k_new) + row * D;
-    const E* vrow = reinterpret_cast<const E*>(p.v_new) + row * D;
     const int64_t tile = ((int64_t)page * p.num_kv_heads + h) * (int64_t)D * bs;
-    E* kc = const_cast<E*>(reinterpret_cast<const E*>(p.k_cache));
-    E* vc = const_cast<E*>(reinterpret_cast<const E*>(p.v_cache));
-    if (lane < D / X) st16_nt(kc + tile + ((int64_t)lane * bs + off) * X, ld16(krow + lane * X));
-    for (int d = lane; d < D; d += kWave) st_nt(&vc[tile + (int64_t)d * bs + off], vrow[d]);
+    store_row(const_cast<E*>(reinterpret_cast<const E*>(p.k_cache)), const_cast<E*>(reinterpret_cast<const E*>(p.v_cache)),
+              tile, off, bs, D, lane, src);
 }
 
 }  // namespace
