@@ -46,9 +46,11 @@ def _args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--step", default="fused", choices=["fused", "separate"],
+    ap.add_argument("--step", default="fused", choices=["fused", "separate", "prefix"],
                     help="fused: the append runs inside the decode kernel (pa_decode_append); "
-                         "separate: pa_kv_append, then pa_decode")
+                         "separate: pa_kv_append, then pa_decode; prefix: pa_kv_append, then "
+                         "pa_decode_shared_prefix with the longest prefix the block tables share "
+                         "(whole partitions, partition 2048 unless --partition-size is given)")
     ap.add_argument("--reuse", default="auto", choices=["auto", "stream", "shared"],
                     help="K/V load path (auto: shared when the workload's sequences share pages)")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -526,12 +528,22 @@ def main(argv=None) -> int:
 
     # the load path a caller picks: its block manager knows whether pages are shared
     reuse = a.reuse if a.reuse != "auto" else ("shared" if w.extra.get("shared_pages") else "stream")
-    P = pa.decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, ps_req, reuse)
+    prefix = a.step == "prefix"
+    if prefix:
+        reuse = "shared"
+        P = ps_req if ps_req and ps_req > 0 else 2048
+        # host bookkeeping, as a block manager would know it: the leading
+        # block-table entries every sequence shares, in whole partitions
+        shared_len = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size, P)
+    else:
+        P = pa.decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, ps_req, reuse)
+        shared_len = None
     split = P > 0
     out = torch.empty_like(t["q"])
     ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P, reuse) if split else None
     kernel_name = "decode_mfma" if (a.kernel == "mfma" or (a.kernel == "auto" and w.dtype == "bf16")) \
         else "decode_valu"
+    main_name = "decode_shared_prefix" if prefix else kernel_name + ("_partition" if split else "_single")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -542,7 +554,13 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[1].record(stream)
         app = dict(k_new=step_k, v_new=step_v, slot_mapping=step_slots) if fused else {}
-        if split:
+        if prefix:
+            # prefix launch + partition kernel + merge: one call, timed as a whole
+            pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                    w.scale, w.max_context_len, shared_len, P, out=out, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+        elif split:
             pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                 t["context_lens"], w.scale, w.max_context_len, P, ws, kernel=a.kernel,
                                 reuse=reuse, **app)
@@ -599,7 +617,7 @@ def main(argv=None) -> int:
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": _traffic(kernel_name, w.name, digest),
-        "kernel": kernel_name + ("_partition" if split else "_single"),
+        "kernel": main_name,
         "avg_launch_us": round(main_ms * 1e3, 2),
         "algorithmic_bytes_per_launch": kv_bytes,
         "source_digest": digest,
@@ -624,14 +642,15 @@ def main(argv=None) -> int:
             "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "sum_context_tokens": int(w.context_lens.sum()),
             "max_context_len": w.max_context_len, "num_blocks": w.num_blocks,
-            "partition_size": P, "kernel": kernel_name, "reuse": reuse, "seed": w.seed,
+            "partition_size": P, "kernel": main_name if prefix else kernel_name, "reuse": reuse,
+            "seed": w.seed, "shared_len": shared_len,
             "kv_bytes_per_step": kv_bytes, "appended_tokens_per_step": int((slots >= 0).sum()),
             "step": a.step,
         },
         "kernels_avg_us": {
             "kv_append": None if fused else round(append_ms * 1e3, 2),
-            (kernel_name + ("_partition" if split else "_single")): round(main_ms * 1e3, 2),
-            "decode_reduce": round(reduce_ms * 1e3, 2) if split else None,
+            main_name: round(main_ms * 1e3, 2),
+            "decode_reduce": round(reduce_ms * 1e3, 2) if split and not prefix else None,
             "decode_total": round(decode_ms * 1e3, 2),
         },
         "roofline": roofline,

@@ -292,6 +292,45 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
                            int32_t max_context_len, int32_t partition_size, pa_dtype dtype);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode for a batch whose sequences all
+ * begin with the same `shared_len` tokens in the same physical pages (their
+ * block tables agree on the first shared_len / block_size entries), as
+ * after forking one prompt.  [Internals, "Copy-on-Write and Prefix
+ * Sharing"; Glossary, "Copy-on-Write Memory Forking"]
+ *
+ * The shared pages are read once per kv head for up to 32 (sequence, query
+ * head) pairs at a time -- a matrix-core launch whose columns are the
+ * decode queries of several sequences, each seeing all shared_len
+ * positions -- instead of once per sequence; the rest of every context is
+ * read per sequence by the split decode kernel.  Both write the split
+ * path's partials (the shared partitions are partitions 0 .. shared_len /
+ * partition_size - 1 of every sequence), which the merge kernel combines.
+ * The result is the same attention as pa_decode, within the same bounds.
+ *
+ *   shared_len      a multiple of partition_size, 0 <= shared_len <=
+ *                   max_context_len (0: the plain split path)
+ *   partition_size  > 0, a multiple of 32
+ *   workspace       >= pa_decode_workspace_size(num_seqs, num_heads,
+ *                   num_kv_heads, head_dim, max_context_len,
+ *                   partition_size, PA_KV_SHARED) bytes
+ * Other arguments as for pa_decode (bf16 only; it always uses the
+ * matrix-core kernels and the shared-page load path).  Preconditions, not
+ * checked: every context_lens[b] >= shared_len, and the first
+ * shared_len / block_size table entries are equal in every row (the
+ * shared pages are read through row 0); otherwise the output is
+ * unspecified, and memory accesses stay in bounds as for pa_decode.
+ * Returns PA_ERR_UNSUPPORTED for fp32 and for more than 1024 sequences.
+ */
+pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t block_size, int32_t num_kv_heads, float scale,
+                                  void* out, hipStream_t stream,
+                                  int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int64_t num_blocks, pa_dtype dtype, int32_t shared_len,
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes);
+
+/*
  * pa_copy_blocks -- copy whole pages (K and V, every kv head) for
  * copy-on-write forks: page block_mapping[i][1] becomes a bit-exact copy of
  * page block_mapping[i][0].  Pairs act as if applied at once (sources and

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "pa_decode_partition": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp,
                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                              _c_int, _vp, _c_size, _vp, _vp, _vp], _c_int),
+    "pa_decode_shared_prefix": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
+                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                                 _vp, _c_size], _c_int),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -311,6 +314,50 @@ def decode_reduce(workspace: torch.Tensor, context_lens: torch.Tensor, out: torc
                                 out.data_ptr(), _stream(out), B, hq, d, int(max_context_len),
                                 int(partition_size), _elem_dtype(out))
     _check("pa_decode_reduce", st)
+    return out
+
+
+def shared_prefix_len(block_tables, context_lens, block_size: int, partition_size: int) -> int:
+    """Longest prefix, in whole partitions, that every sequence holds in the
+    same physical pages: the leading block-table entries equal in all rows,
+    capped by the shortest context (host arrays or tensors; host-side
+    bookkeeping for pa_decode_shared_prefix, no device work)."""
+    import numpy as np
+    tables = block_tables.cpu().numpy() if hasattr(block_tables, "cpu") else np.asarray(block_tables)
+    lens = context_lens.cpu().numpy() if hasattr(context_lens, "cpu") else np.asarray(context_lens)
+    if len(lens) == 0:
+        return 0
+    same = (tables == tables[:1]).all(axis=0)
+    pages = int(np.argmin(same)) if not same.all() else tables.shape[1]
+    tokens = min(pages * block_size, int(lens.min()))
+    return tokens // partition_size * partition_size
+
+
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                         max_context_len: int, shared_len: int, partition_size: int,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode a batch whose sequences share their first ``shared_len`` tokens
+    in the same pages: the shared pages are read once for many sequences'
+    queries (see pa_decode_shared_prefix)."""
+    nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dtype=q.dtype, ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if workspace is None:
+        workspace = make_workspace(q, hkv, max_context_len, partition_size, "shared")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().pa_decode_shared_prefix(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,
+                                       float(scale), out.data_ptr(), _stream(q), B, hq, d,
+                                       block_tables.shape[1], int(max_context_len), nb, _elem_dtype(q),
+                                       int(shared_len), int(partition_size), ws_ptr, ws_bytes)
+    _check("pa_decode_shared_prefix", st)
     return out
 
 

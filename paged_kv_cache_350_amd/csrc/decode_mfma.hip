@@ -132,6 +132,7 @@ void decode_mfma_kernel(DecodeParams p) {
         }
         return;
     }
+    if (part < p.first_part) return;          // read by the shared-prefix launch
     const int start = part * p.partition;
     const int end = min(start + p.partition, L);
 

@@ -92,17 +92,22 @@ void decode_multi_kernel(DecodeParams p) {
     const int slot = wi.q / (p.num_kv_heads * p.col_groups);
     const int G = p.group;
 
-    int L = p.context_lens[b];
+    int L = p.uniform_len > 0 ? p.uniform_len : p.context_lens[b];
     const int cap = min(p.max_context_len, p.max_blocks_per_seq * BS);
     L = L < 0 ? 0 : (L > cap ? cap : L);
-    const QueryRows qr = query_rows(p.query_start, b, L, p.num_tokens, p.max_query_len);
+    // rows that all see the whole context are not bounded by its length
+    const QueryRows qr = query_rows(p.query_start, b, p.all_visible ? INT_MAX : L, p.num_tokens, p.max_query_len);
     const int n = qr.n;
     const int col0 = cg * COLS;
     if (col0 >= G * n) return;                               // no query in this column group
     const int first_jq = col0 / G;
     const int last_jq = min(n - 1, (col0 + COLS - 1) / G);
-    const int lo_lim = L - n + first_jq;                     // smallest last visible position
-    const int hi_lim = L - n + last_jq;                      // largest
+    // causal rows: query token jq sees positions <= L - n + jq; with
+    // all_visible (the queries of sequences that share these L positions as
+    // their prefix) every row sees all of them
+    const int vis = p.all_visible ? L - 1 : L - n;           // + jq when causal
+    const int lo_lim = p.all_visible ? vis : vis + first_jq; // smallest last visible position
+    const int hi_lim = p.all_visible ? vis : vis + last_jq;  // largest
     const int part = partition_of(slot, p.max_parts, L, p.partition, p.stream_kv != 0);
     if (part < 0) return;
     const int start = part * p.partition;
@@ -117,7 +122,7 @@ void decode_multi_kernel(DecodeParams p) {
         const int c = col0 + 16 * nt + hl;
         const int jq = c / G;
         const bool live = jq < n;
-        lim[nt] = live ? L - n + jq : -1;
+        lim[nt] = live ? (p.all_visible ? vis : vis + jq) : -1;
         const size_t qrow = ((size_t)(qr.row0 + (live ? jq : 0)) * p.num_heads + (size_t)g * G + c % G) * D;
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qrow;
         // a padding column repeats token 0's query of its head and is masked

@@ -211,6 +211,9 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.num_tokens = 0;
     p.max_query_len = 0;
     p.col_groups = 0;
+    p.first_part = 0;
+    p.all_visible = 0;
+    p.uniform_len = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -308,7 +311,7 @@ const char* pa_status_string(pa_status status) {
     return "unknown status";
 }
 
-int32_t pa_version(void) { return 320; }
+int32_t pa_version(void) { return 330; }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size, pa_kv_reuse reuse) {
@@ -478,6 +481,75 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     plan.p.max_context_len = max_context_len;
     plan.p.partition = partition;
     plan.p.max_parts = parts_for(max_context_len, partition);
+    return launch_reduce(plan, context_lens, out, stream);
+}
+
+pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t block_size, int32_t num_kv_heads, float scale,
+                                  void* out, hipStream_t stream,
+                                  int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int64_t num_blocks, pa_dtype dtype, int32_t shared_len,
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (partition_size <= 0) return PA_ERR_ARG;
+    if (num_seqs > kMaxQueryLen) return PA_ERR_UNSUPPORTED;     // the prefix launch's query rows
+    Plan plan;
+    pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                             scale, out, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                             max_context_len, num_blocks, dtype, partition_size, PA_KERNEL_MFMA,
+                             PA_KV_SHARED, workspace, workspace_bytes,
+                             /*need_out=*/true, /*force_split=*/true, &plan);
+    if (st != PA_OK) return st;
+    if (shared_len < 0 || shared_len % plan.partition != 0 || shared_len > max_context_len) return PA_ERR_ARG;
+    if (num_seqs == 0) return PA_OK;
+
+    // Prefix partitions: one multi-query launch over sequence 0's table row
+    // whose query rows are all num_seqs decode queries, every row seeing
+    // all shared_len positions.  Its partials land in the rows and
+    // partition slots the split path uses for those tokens.
+    const int32_t prefix_parts = shared_len / plan.partition;
+    if (prefix_parts > 0) {
+        DecodeParams m{};
+        m.q = q;
+        m.k_cache = k_cache;
+        m.v_cache = v_cache;
+        m.block_tables = block_tables;
+        m.context_lens = context_lens;        // not read: uniform_len
+        m.out = out;
+        m.ws = plan.p.ws;
+        m.scale_log2 = plan.p.scale_log2;
+        m.num_seqs = 1;
+        m.num_heads = num_heads;
+        m.num_kv_heads = num_kv_heads;
+        m.group = plan.p.group;
+        m.head_dim = head_dim;
+        m.block_size = block_size;
+        m.max_blocks_per_seq = max_blocks_per_seq;
+        m.max_context_len = max_context_len;
+        m.num_blocks = num_blocks;
+        m.partition = plan.partition;
+        m.max_parts = plan.p.max_parts;
+        m.split = 1;
+        m.stream_kv = 0;
+        m.waves = 4;
+        m.query_start = nullptr;              // rows 0 .. num_seqs - 1
+        m.num_tokens = num_seqs;
+        m.max_query_len = num_seqs;
+        m.col_groups = multi_col_groups(m.group, num_seqs);
+        m.all_visible = 1;
+        m.uniform_len = shared_len;
+        if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
+        st = hip_status(pa_impl::launch_decode_multi(m, multi_col_tiles(m.group, num_seqs), stream));
+        if (st != PA_OK) return st;
+    }
+    // The rest of every context, sequence by sequence, then the usual merge
+    // over all partitions.
+    plan.p.first_part = prefix_parts;
+    st = launch_plan(plan, stream);
+    if (st != PA_OK) return st;
     return launch_reduce(plan, context_lens, out, stream);
 }
 

@@ -182,9 +182,10 @@ __device__ __forceinline__ int partition_of(int slot, int max_parts, int L, int 
 }
 
 // Multi-query launches: the query rows of sequence b are row0 .. row0 + n - 1,
-// taken from query_start[b] and query_start[b + 1] and clamped so that every
-// row lies in [0, num_tokens), n <= max_query_len and n <= L (the sequence's
-// clamped context length).  The partition and merge kernels both go through
+// taken from query_start[b] and query_start[b + 1] (or, with no query_start,
+// rows b * max_query_len onwards) and clamped so that every row lies in
+// [0, num_tokens), n <= max_query_len and n <= L (the sequence's clamped
+// context length).  The partition and merge kernels both go through
 // this function, so they agree on which rows a sequence covers even when the
 // offsets are inconsistent.
 struct QueryRows {
@@ -194,8 +195,8 @@ struct QueryRows {
 
 __device__ __forceinline__ QueryRows query_rows(const int32_t* query_start, int b, int L, int num_tokens,
                                                 int max_query_len) {
-    int r0 = query_start[b];
-    int r1 = query_start[b + 1];
+    int r0 = query_start ? query_start[b] : b * max_query_len;
+    int r1 = query_start ? query_start[b + 1] : r0 + max_query_len;
     r0 = r0 < 0 ? 0 : r0;
     r1 = r1 > num_tokens ? num_tokens : r1;
     int n = r1 - r0;

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -35,7 +36,7 @@ def test_header_declares_the_boundary():
     for want in ["pa_kv_append", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_size",
                  "pa_status_string", "pa_decode_partition", "pa_decode_reduce",
                  "pa_decode_partition_size", "pa_version", "pa_probe_stream_read",
-                 "pa_decode_append"]:
+                 "pa_decode_append", "pa_decode_shared_prefix"]:
         assert want in names
 
 
@@ -50,7 +51,7 @@ def test_status_strings(L):
         assert pa.status_string(code)
     assert pa.status_string(0) == "ok"
     assert pa.status_string(-99) == "unknown status"
-    assert L.pa_version() == 320
+    assert L.pa_version() == 330
 
 
 def test_partition_policy_and_workspace_size(L):
@@ -269,3 +270,41 @@ def test_decode_multi_append_validates(L):
     assert call(kn=FAKE + 2) == pa.PA_ERR_ARG
     assert call(kn=None, vn=None, B=0) == pa.PA_OK          # nothing to do
     assert call(maxq=0) == pa.PA_ERR_ARG
+
+
+def _shared(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, bs=16, hkv=8, scale=0.1, out=FAKE,
+             stream=None, B=4, hq=32, d=128, maxb=16, maxctx=256, nb=100, dtype=1, S=128, part=64,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.pa_decode_shared_prefix(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bs"], a["hkv"], a["scale"],
+                                     a["out"], a["stream"], a["B"], a["hq"], a["d"], a["maxb"], a["maxctx"],
+                                     a["nb"], a["dtype"], a["S"], a["part"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), pa.PA_ERR_UNSUPPORTED),           # matrix-core kernels: bf16 only
+    (dict(dtype=5), pa.PA_ERR_ARG),
+    (dict(B=1025), pa.PA_ERR_UNSUPPORTED),            # prefix launch rows
+    (dict(part=0), pa.PA_ERR_ARG),                    # an explicit partition is required
+    (dict(part=48), pa.PA_ERR_ARG),
+    (dict(S=100), pa.PA_ERR_ARG),                     # not a multiple of the partition
+    (dict(S=-64), pa.PA_ERR_ARG),
+    (dict(S=320), pa.PA_ERR_ARG),                     # beyond max_context_len
+    (dict(ws=None, wsb=0), pa.PA_ERR_WORKSPACE),
+    (dict(wsb=16), pa.PA_ERR_WORKSPACE),
+    (dict(q=None), pa.PA_ERR_NULL),
+    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(B=0), pa.PA_OK),                            # nothing to do, nothing launched
+])
+def test_decode_shared_prefix_validates(L, kw, status):
+    assert _shared(L, **kw) == status
+
+
+def test_shared_prefix_len_from_tables():
+    t = np.array([[1, 2, 3, 4], [1, 2, 5, 6], [1, 2, 3, 7]])
+    assert pa.shared_prefix_len(t, np.array([60, 50, 64]), 16, 32) == 32
+    assert pa.shared_prefix_len(t, np.array([60, 20, 64]), 16, 32) == 0      # shortest context caps it
+    assert pa.shared_prefix_len(t[:1], np.array([60]), 16, 32) == 32
+    assert pa.shared_prefix_len(t[:, :0], np.array([5, 5, 5]), 16, 32) == 0
+    assert pa.shared_prefix_len(t, np.array([], dtype=np.int32), 16, 32) == 0

@@ -1,0 +1,132 @@
+"""pa_decode_shared_prefix on the GPU against the float64 oracle.
+
+The shared pages are read once for many sequences' queries (a multi-query
+launch whose rows all see the whole shared prefix), the rest of each context
+per sequence, and the partials merged as in the split path.  The oracle is
+the plain decode definition over each sequence's own block table: sharing
+only changes how often a page is read, never the result.
+
+Shared-prefix batches of any head shape are built from independent ragged
+sequences by pointing every row's leading table entries at row 0's pages (the
+oracle reads through the same tables, so both sides see the same bytes); the
+named prefix-sharing and beam workloads are checked at full size."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, step_and_reference
+
+pytestmark = pytest.mark.gpu
+
+
+def _share_rows(w, t, shared_tokens):
+    """Make every sequence read row 0's pages for its first shared_tokens
+    positions (whole pages), on the host copy and the device copy alike."""
+    n = shared_tokens // w.block_size
+    tables = w.block_tables.copy()
+    tables[:, :n] = tables[0, :n]
+    w.block_tables = tables
+    t["block_tables"].copy_(torch.from_numpy(tables))
+
+
+def _shared_batch(name, seed, hq, hkv, d, bs, shared_tokens, nseq=24):
+    rng = np.random.default_rng(seed)
+    lens = shared_tokens + 2 + rng.integers(0, 400, size=nseq)
+    lens[1] = shared_tokens + 2                     # the shortest context allowed
+    w = W.custom(name, seed, "bf16", lens.tolist(), hq, hkv, d, bs)
+    t = W.make_tensors(w, "cuda")
+    _share_rows(w, t, shared_tokens)
+    return w, t
+
+
+def _run(pa, w, t, shared_len, P):
+    return pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                   w.scale, w.max_context_len, shared_len, P)
+
+
+SHAPES = [  # (num_heads, num_kv_heads, head_dim, block_size)
+    (32, 8, 128, 16),
+    (32, 8, 128, 32),
+    (64, 8, 128, 16),     # G = 8: 4 sequences per 32-column group
+    (32, 2, 64, 16),      # G = 16: 2 sequences per group, D 64
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_shared_prefix_matches_oracle(shape):
+    pa = require_gpu()
+    hq, hkv, d, bs = shape
+    w, t = _shared_batch("shared", 41, hq, hkv, d, bs, shared_tokens=640)
+    say("shared prefix", shape, w.summary())
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    for P in (32, 64, 128, 256):
+        S = pa.shared_prefix_len(w.block_tables, w.context_lens, bs, P)
+        say("  partition", P, "shared_len", S)
+        assert S > 0 and S % P == 0
+        out = _run(pa, w, t, S, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"shared {shape} P={P} S={S}")
+        again = _run(pa, w, t, S, P)
+        torch.cuda.synchronize()
+        assert bits_equal(out, again), f"repeat {shape} P={P}"
+        # a shorter shared length is as valid: fewer prefix partitions
+        out2 = _run(pa, w, t, S - P, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out2), ref, "bf16", f"shared {shape} P={P} S={S - P}")
+
+
+def test_zero_shared_length_is_the_split_path():
+    """shared_len 0 launches no prefix work: bit-identical to pa_decode's
+    split path on the matrix-core kernel with shared-page loads."""
+    pa = require_gpu()
+    w, t = _shared_batch("shared_zero", 42, 32, 8, 128, 16, shared_tokens=320)
+    say("shared prefix, shared_len 0", w.summary())
+    step_and_reference(pa, w, t, [0])
+    for P in (64, 256):
+        one = _run(pa, w, t, 0, P)
+        two = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], w.scale,
+                        w.max_context_len, partition_size=P, kernel="mfma", reuse="shared")
+        torch.cuda.synchronize()
+        assert bits_equal(one, two), P
+
+
+def test_many_sequences_fill_several_column_groups():
+    """200 sequences x 4 heads = 800 columns: 25 column groups of 32 over the
+    prefix; sampled sequences against the oracle."""
+    pa = require_gpu()
+    w, t = _shared_batch("shared_many", 43, 32, 8, 128, 16, shared_tokens=1024, nseq=200)
+    say("shared prefix, 200 sequences", w.summary())
+    seqs = [0, 1, 7, 31, 32, 33, 99, 150, 198, 199]
+    ref = step_and_reference(pa, w, t, seqs)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16, 256)
+    assert S == 1024
+    out = _run(pa, w, t, S, 256)
+    torch.cuda.synchronize()
+    check_close(out_f64(out)[seqs], ref, "bf16", "shared 200 seqs")
+
+
+@pytest.mark.parametrize("name", ["prefix_share", "beam_fork"])
+def test_named_workload_full_size(name):
+    """The 100 x 10,000-token prefix batch and the 8 beams over a 32,768-token
+    prompt, after the step's copy-on-write copies and appends, with the shared
+    length the block tables give at partition 2048; sampled sequences against
+    the oracle."""
+    pa = require_gpu()
+    w = W.by_name(name)
+    say("shared prefix full", name, w.summary())
+    t = W.make_tensors(w, "cuda")
+    rng = np.random.default_rng(23)
+    order = np.argsort(w.context_lens)
+    seqs = sorted({int(order[0]), int(order[-1])} |
+                  set(int(s) for s in rng.choice(w.num_seqs, size=min(6, w.num_seqs), replace=False)))
+    ref = step_and_reference(pa, w, t, seqs)
+    P = 2048
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size, P)
+    say("  shared_len", S)
+    assert S >= 8192
+    out = _run(pa, w, t, S, P)
+    torch.cuda.synchronize()
+    stats = check_close(out_f64(out)[seqs], ref, "bf16", f"shared {name}")
+    say("  ", stats)
