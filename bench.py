@@ -48,8 +48,8 @@ def _args(argv=None):
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--step", default="fused", choices=["fused", "separate", "prefix"],
                     help="fused: the append runs inside the decode kernel (pa_decode_append); "
-                         "separate: pa_kv_append, then pa_decode; prefix: pa_kv_append, then "
-                         "pa_decode_shared_prefix with the longest prefix the block tables share "
+                         "separate: pa_kv_append, then pa_decode; prefix: pa_decode_shared_prefix "
+                         "(append fused) with the longest prefix the block tables share "
                          "(whole partitions, partition 2048 unless --partition-size is given)")
     ap.add_argument("--reuse", default="auto", choices=["auto", "stream", "shared"],
                     help="K/V load path (auto: shared when the workload's sequences share pages)")
@@ -523,7 +523,7 @@ def main(argv=None) -> int:
         step_v[b] = t["v_new"][i]
         slots[b] = w.append_slots[i]
     step_slots = torch.from_numpy(slots).cuda()
-    fused = a.step == "fused"
+    fused = a.step in ("fused", "prefix")
     torch.cuda.synchronize()
 
     # the load path a caller picks: its block manager knows whether pages are shared
@@ -557,7 +557,7 @@ def main(argv=None) -> int:
         if prefix:
             # prefix launch + partition kernel + merge: one call, timed as a whole
             pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                                    w.scale, w.max_context_len, shared_len, P, out=out, workspace=ws)
+                                    w.scale, w.max_context_len, shared_len, P, out=out, workspace=ws, **app)
             if ev is not None:
                 ev[2].record(stream)
         elif split:

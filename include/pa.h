@@ -313,6 +313,11 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
  *   workspace       >= pa_decode_workspace_size(num_seqs, num_heads,
  *                   num_kv_heads, head_dim, max_context_len,
  *                   partition_size, PA_KV_SHARED) bytes
+ *   k_new, v_new, slot_mapping  NULL for a plain decode; otherwise each
+ *                   sequence's newest rows are appended as by
+ *                   pa_decode_append (the position L - 1 must lie past
+ *                   shared_len, which every appending sequence gives since
+ *                   it owns its last page)
  * Other arguments as for pa_decode (bf16 only; it always uses the
  * matrix-core kernels and the shared-page load path).  Preconditions, not
  * checked: every context_lens[b] >= shared_len, and the first
@@ -328,7 +333,8 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
                                   int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t max_context_len,
                                   int64_t num_blocks, pa_dtype dtype, int32_t shared_len,
-                                  int32_t partition_size, void* workspace, size_t workspace_bytes);
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                  const void* k_new, const void* v_new, const int64_t* slot_mapping);
 
 /*
  * pa_copy_blocks -- copy whole pages (K and V, every kv head) for

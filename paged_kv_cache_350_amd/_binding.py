@@ -56,7 +56,7 @@ _SIGNATURES = {
                              _c_int, _vp, _c_size, _vp, _vp, _vp], _c_int),
     "pa_decode_shared_prefix": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
-                                 _vp, _c_size], _c_int),
+                                 _vp, _c_size, _vp, _vp, _vp], _c_int),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -273,6 +273,25 @@ def decode_append(k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, k_c
     return out
 
 
+def _append_args(k_new, v_new, slot_mapping, B: int, hkv: int, d: int, dtype):
+    """Pointers for an optional fused append of each sequence's newest rows
+    (k_new / v_new [B, Hkv, D], slot_mapping [B] int64 or None); all None
+    when no rows are given."""
+    if k_new is None and v_new is None:
+        return None, None, None
+    _dev_tensor("k_new", k_new, dtype=dtype, ndim=3)
+    _dev_tensor("v_new", v_new, dtype=dtype, ndim=3)
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError("k_new / v_new must be [num_seqs, num_kv_heads, head_dim]")
+    sm = None
+    if slot_mapping is not None:
+        _dev_tensor("slot_mapping", slot_mapping, dtype=torch.int64, ndim=1)
+        if slot_mapping.shape[0] != B:
+            raise ValueError("slot_mapping must have one entry per sequence")
+        sm = slot_mapping.data_ptr()
+    return k_new.data_ptr(), v_new.data_ptr(), sm
+
+
 def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                      max_context_len: int, partition_size: int, workspace: torch.Tensor,
                      kernel: str = "auto", reuse: str = "auto", k_new=None, v_new=None,
@@ -282,18 +301,7 @@ def decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale: flo
     nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len)
     _dev_tensor("workspace", workspace, dtype=torch.float32)
-    kn = vn = sm = None
-    if k_new is not None or v_new is not None:
-        _dev_tensor("k_new", k_new, dtype=q.dtype, ndim=3)
-        _dev_tensor("v_new", v_new, dtype=q.dtype, ndim=3)
-        if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
-            raise ValueError("k_new / v_new must be [num_seqs, num_kv_heads, head_dim]")
-        kn, vn = k_new.data_ptr(), v_new.data_ptr()
-        if slot_mapping is not None:
-            _dev_tensor("slot_mapping", slot_mapping, dtype=torch.int64, ndim=1)
-            if slot_mapping.shape[0] != B:
-                raise ValueError("slot_mapping must have one entry per sequence")
-            sm = slot_mapping.data_ptr()
+    kn, vn, sm = _append_args(k_new, v_new, slot_mapping, B, hkv, d, q.dtype)
     st = lib().pa_decode_partition(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                    block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,
                                    float(scale), _stream(q), B, hq, d, block_tables.shape[1],
@@ -337,10 +345,13 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                          block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                          max_context_len: int, shared_len: int, partition_size: int,
                          out: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         workspace: Optional[torch.Tensor] = None, k_new=None, v_new=None,
+                         slot_mapping=None) -> torch.Tensor:
     """Decode a batch whose sequences share their first ``shared_len`` tokens
     in the same pages: the shared pages are read once for many sequences'
-    queries (see pa_decode_shared_prefix)."""
+    queries (see pa_decode_shared_prefix).  With ``k_new`` / ``v_new``
+    ([B, Hkv, D]) each sequence's newest rows are appended as by
+    decode_append (``slot_mapping`` [B] int64: a negative entry skips)."""
     nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len)
     if out is None:
@@ -352,11 +363,12 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         workspace = make_workspace(q, hkv, max_context_len, partition_size, "shared")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kn, vn, sm = _append_args(k_new, v_new, slot_mapping, B, hkv, d, q.dtype)
     st = lib().pa_decode_shared_prefix(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                        block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,
                                        float(scale), out.data_ptr(), _stream(q), B, hq, d,
                                        block_tables.shape[1], int(max_context_len), nb, _elem_dtype(q),
-                                       int(shared_len), int(partition_size), ws_ptr, ws_bytes)
+                                       int(shared_len), int(partition_size), ws_ptr, ws_bytes, kn, vn, sm)
     _check("pa_decode_shared_prefix", st)
     return out
 

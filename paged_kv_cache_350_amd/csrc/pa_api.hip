@@ -491,7 +491,8 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
                                   int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t max_context_len,
                                   int64_t num_blocks, pa_dtype dtype, int32_t shared_len,
-                                  int32_t partition_size, void* workspace, size_t workspace_bytes) {
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                  const void* k_new, const void* v_new, const int64_t* slot_mapping) {
     if (!valid_dtype(dtype)) return PA_ERR_ARG;
     if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     if (partition_size <= 0) return PA_ERR_ARG;
@@ -504,6 +505,8 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
                              /*need_out=*/true, /*force_split=*/true, &plan);
     if (st != PA_OK) return st;
     if (shared_len < 0 || shared_len % plan.partition != 0 || shared_len > max_context_len) return PA_ERR_ARG;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
     if (num_seqs == 0) return PA_OK;
 
     // Prefix partitions: one multi-query launch over sequence 0's table row
@@ -533,21 +536,27 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.partition = plan.partition;
         m.max_parts = plan.p.max_parts;
         m.split = 1;
-        m.stream_kv = 0;
         m.waves = 4;
         m.query_start = nullptr;              // rows 0 .. num_seqs - 1
         m.num_tokens = num_seqs;
         m.max_query_len = num_seqs;
         m.col_groups = multi_col_groups(m.group, num_seqs);
+        // one column group reads each shared page once: streaming loads;
+        // several read it together from L2: ordinary loads
+        m.stream_kv = m.col_groups == 1 ? 1 : 0;
         m.all_visible = 1;
         m.uniform_len = shared_len;
         if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
         st = hip_status(pa_impl::launch_decode_multi(m, multi_col_tiles(m.group, num_seqs), stream));
         if (st != PA_OK) return st;
     }
-    // The rest of every context, sequence by sequence, then the usual merge
-    // over all partitions.
+    // The rest of every context, sequence by sequence (with the fused append
+    // of pa_decode_append when new rows are given: position L - 1 lies past
+    // the shared prefix), then the usual merge over all partitions.
     plan.p.first_part = prefix_parts;
+    plan.p.k_new = k_new;
+    plan.p.v_new = v_new;
+    plan.p.append_mask = k_new ? slot_mapping : nullptr;
     st = launch_plan(plan, stream);
     if (st != PA_OK) return st;
     return launch_reduce(plan, context_lens, out, stream);

@@ -275,11 +275,12 @@ def test_decode_multi_append_validates(L):
 def _shared(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, bs=16, hkv=8, scale=0.1, out=FAKE,
              stream=None, B=4, hq=32, d=128, maxb=16, maxctx=256, nb=100, dtype=1, S=128, part=64,
-             ws=FAKE, wsb=1 << 30)
+             ws=FAKE, wsb=1 << 30, kn=None, vn=None, sm=None)
     a.update(kw)
     return L.pa_decode_shared_prefix(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bs"], a["hkv"], a["scale"],
                                      a["out"], a["stream"], a["B"], a["hq"], a["d"], a["maxb"], a["maxctx"],
-                                     a["nb"], a["dtype"], a["S"], a["part"], a["ws"], a["wsb"])
+                                     a["nb"], a["dtype"], a["S"], a["part"], a["ws"], a["wsb"],
+                                     a["kn"], a["vn"], a["sm"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -296,6 +297,8 @@ def _shared(L, **kw):
     (dict(q=None), pa.PA_ERR_NULL),
     (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
     (dict(B=0), pa.PA_OK),                            # nothing to do, nothing launched
+    (dict(kn=FAKE), pa.PA_ERR_NULL),                  # K rows without V rows
+    (dict(kn=FAKE, vn=FAKE + 8), pa.PA_ERR_ARG),      # misaligned
 ])
 def test_decode_shared_prefix_validates(L, kw, status):
     assert _shared(L, **kw) == status

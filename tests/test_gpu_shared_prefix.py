@@ -15,8 +15,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
-from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, step_and_reference
+from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, step_and_reference, storage_np
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +131,43 @@ def test_named_workload_full_size(name):
     torch.cuda.synchronize()
     stats = check_close(out_f64(out)[seqs], ref, "bf16", f"shared {name}")
     say("  ", stats)
+
+
+def test_fused_append():
+    """Each sequence's newest rows appended by the partition kernel of the
+    shared-prefix call (position L - 1 lies past the shared prefix): caches bit
+    for bit against the oracle's append, output within tolerance of the oracle
+    and bit-identical to pa_kv_append followed by the same call without rows."""
+    pa = require_gpu()
+    w, t = _shared_batch("shared_fused", 44, 32, 8, 128, 16, shared_tokens=512)
+    say("shared prefix, fused append", w.summary())
+    B = w.num_seqs
+    assert sorted(w.append_seq.tolist()) == list(range(B))
+    k_new = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=t["k_new"].dtype, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    mask = np.full(B, -1, dtype=np.int64)
+    for i, b in enumerate(w.append_seq.tolist()):
+        k_new[b] = t["k_new"][i]
+        v_new[b] = t["v_new"][i]
+        mask[b] = w.append_slots[i]
+    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
+    rk, rv = oracle.kv_append(storage_np(k_new), storage_np(v_new), mask, kc0, vc0, w.block_size)
+    ref = oracle.decode(storage_np(t["q"]), rk, rv, w.block_tables, w.context_lens, w.scale, w.block_size,
+                        "bf16")
+    slots = torch.from_numpy(mask).cuda()
+    for P in (64, 256):
+        S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size, P)
+        say("  partition", P, "shared_len", S)
+        kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+        out = pa.decode_shared_prefix(t["q"], kc, vc, t["block_tables"], t["context_lens"], w.scale,
+                                      w.max_context_len, S, P, k_new=k_new, v_new=v_new, slot_mapping=slots)
+        torch.cuda.synchronize()
+        assert np.array_equal(storage_np(kc).view(np.uint16), rk.view(np.uint16))
+        assert np.array_equal(storage_np(vc).view(np.uint16), rv.view(np.uint16))
+        check_close(out_f64(out), ref, "bf16", f"shared fused P={P}")
+        kc2, vc2 = t["k_cache"].clone(), t["v_cache"].clone()
+        pa.kv_append(k_new, v_new, slots, kc2, vc2)
+        out2 = pa.decode_shared_prefix(t["q"], kc2, vc2, t["block_tables"], t["context_lens"], w.scale,
+                                       w.max_context_len, S, P)
+        torch.cuda.synchronize()
+        assert bits_equal(out, out2), f"fused != separate P={P}"
