@@ -541,9 +541,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.num_tokens = num_seqs;
         m.max_query_len = num_seqs;
         m.col_groups = multi_col_groups(m.group, num_seqs);
-        // one column group reads each shared page once: streaming loads;
-        // several read it together from L2: ordinary loads
-        m.stream_kv = m.col_groups == 1 ? 1 : 0;
+        m.stream_kv = 0;                      // ordinary loads: the pages are shared
         m.all_visible = 1;
         m.uniform_len = shared_len;
         if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
