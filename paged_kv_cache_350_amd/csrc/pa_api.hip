@@ -23,6 +23,7 @@ constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
 constexpr int32_t kMaxQueryLen = 1024;       // multi-query: new tokens per sequence
 constexpr int64_t kMultiFill = 256;          // multi-query: workgroups that keep every CU busy
 constexpr int32_t kMultiMaxPartition = 8192;
+constexpr int64_t kPrefixFill = 512;         // shared-prefix launch: workgroups that fill the chip (two per CU)
 // streaming-load decode default (see default_stream_partition)
 constexpr int64_t kOnePassPairs = 2048;      // (sequence, kv head) pairs that make a single pass
 constexpr int64_t kOnePassShortPairs = 1024; // ... or this many when no context exceeds
@@ -540,12 +541,24 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.query_start = nullptr;              // rows 0 .. num_seqs - 1
         m.num_tokens = num_seqs;
         m.max_query_len = num_seqs;
-        m.col_groups = multi_col_groups(m.group, num_seqs);
+        // Two 16-column tiles per workgroup halve how often a shared page is
+        // read; one tile runs three waves per SIMD instead of two and doubles
+        // the workgroups.  One only when two would leave a single column
+        // group and fewer than kPrefixFill workgroups (two per compute unit
+        // at this kernel's occupancy).  Measured: 8 beams over 32,768 tokens
+        // (one group of 32 columns) 41.2 us with two tiles, 37.3 with one;
+        // 100 sequences over a 9,216-token prefix (13 groups) 108 us with
+        // two, 125 with one, and at 416 workgroups still 111 against 138.
+        int32_t tiles = multi_col_tiles(m.group, num_seqs);
+        if (tiles == 2 && multi_col_groups(m.group, num_seqs) == 1 &&
+            (int64_t)num_kv_heads * prefix_parts < kPrefixFill)
+            tiles = 1;
+        m.col_groups = (int32_t)(((int64_t)m.group * num_seqs + 16 * tiles - 1) / (16 * tiles));
         m.stream_kv = 0;                      // ordinary loads: the pages are shared
         m.all_visible = 1;
         m.uniform_len = shared_len;
         if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
-        st = hip_status(pa_impl::launch_decode_multi(m, multi_col_tiles(m.group, num_seqs), stream));
+        st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
         if (st != PA_OK) return st;
     }
     // The rest of every context, sequence by sequence (with the fused append

@@ -35,7 +35,7 @@ def _share_rows(w, t, shared_tokens):
 def _shared_batch(name, seed, hq, hkv, d, bs, shared_tokens, nseq=24):
     rng = np.random.default_rng(seed)
     lens = shared_tokens + 2 + rng.integers(0, 400, size=nseq)
-    lens[1] = shared_tokens + 2                     # the shortest context allowed
+    lens[min(1, nseq - 1)] = shared_tokens + 2      # the shortest context allowed
     w = W.custom(name, seed, "bf16", lens.tolist(), hq, hkv, d, bs)
     t = W.make_tensors(w, "cuda")
     _share_rows(w, t, shared_tokens)
@@ -171,3 +171,20 @@ def test_fused_append():
                                        w.max_context_len, S, P)
         torch.cuda.synchronize()
         assert bits_equal(out, out2), f"fused != separate P={P}"
+
+
+@pytest.mark.parametrize("nseq", [8, 4, 1])
+def test_few_sequences(nseq):
+    """8 sequences x 4 heads fill one group of 32 columns (the prefix launch
+    then runs one 16-column tile per workgroup over two groups), 4 fit one
+    tile, and a single sequence shares a prefix with itself."""
+    pa = require_gpu()
+    w, t = _shared_batch("shared_few", 45 + nseq, 32, 8, 128, 16, shared_tokens=768, nseq=nseq)
+    say("shared prefix,", nseq, "sequences", w.summary())
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    for P in (128, 256):
+        S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16, P)
+        assert S == 768
+        out = _run(pa, w, t, S, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"shared {nseq} seqs P={P}")
