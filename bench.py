@@ -50,7 +50,7 @@ def _args(argv=None):
                     help="fused: the append runs inside the decode kernel (pa_decode_append); "
                          "separate: pa_kv_append, then pa_decode; prefix: pa_decode_shared_prefix "
                          "(append fused) with the longest prefix the block tables share "
-                         "(whole partitions, partition 1024 unless --partition-size is given)")
+                         "(whole pages; partition 2048 unless --partition-size is given)")
     ap.add_argument("--reuse", default="auto", choices=["auto", "stream", "shared"],
                     help="K/V load path (auto: shared when the workload's sequences share pages)")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -531,16 +531,20 @@ def main(argv=None) -> int:
     prefix = a.step == "prefix"
     if prefix:
         reuse = "shared"
-        P = ps_req if ps_req and ps_req > 0 else 1024
+        P = ps_req if ps_req and ps_req > 0 else 2048
         # host bookkeeping, as a block manager would know it: the leading
-        # block-table entries every sequence shares, in whole partitions
-        shared_len = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size, P)
+        # block-table entries every sequence shares, in whole pages
+        shared_len = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)
     else:
         P = pa.decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, ps_req, reuse)
         shared_len = None
     split = P > 0
     out = torch.empty_like(t["q"])
-    ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P, reuse) if split else None
+    if prefix:
+        nws = pa.shared_prefix_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.max_context_len, P)
+        ws = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
+    else:
+        ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P, reuse) if split else None
     kernel_name = "decode_mfma" if (a.kernel == "mfma" or (a.kernel == "auto" and w.dtype == "bf16")) \
         else "decode_valu"
     main_name = "decode_shared_prefix" if prefix else kernel_name + ("_partition" if split else "_single")

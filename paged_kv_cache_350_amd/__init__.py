@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     PA_ERR_WORKSPACE, PA_F32, PA_OK, PaError, copy_blocks, decode, decode_append, decode_partition,
     decode_multi, decode_multi_partition_size, decode_multi_workspace_size,
     decode_partition_size, decode_reduce, decode_shared_prefix, decode_workspace_size, kv_append, lib,
-    shared_prefix_len,
+    shared_prefix_len, shared_prefix_workspace_size,
     make_workspace, probe_stream_read, status_string,
 )
 from .block_manager import NativeBlockManager, OutOfPages  # noqa: F401,E402

@@ -57,6 +57,7 @@ _SIGNATURES = {
     "pa_decode_shared_prefix": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                  _vp, _c_size, _vp, _vp, _vp], _c_int),
+    "pa_decode_shared_prefix_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -325,11 +326,11 @@ def decode_reduce(workspace: torch.Tensor, context_lens: torch.Tensor, out: torc
     return out
 
 
-def shared_prefix_len(block_tables, context_lens, block_size: int, partition_size: int) -> int:
-    """Longest prefix, in whole partitions, that every sequence holds in the
-    same physical pages: the leading block-table entries equal in all rows,
-    capped by the shortest context (host arrays or tensors; host-side
-    bookkeeping for pa_decode_shared_prefix, no device work)."""
+def shared_prefix_len(block_tables, context_lens, block_size: int) -> int:
+    """Longest prefix, in whole pages, that every sequence holds in the same
+    physical pages: the leading block-table entries equal in all rows, capped
+    by the shortest context (host arrays or tensors; host-side bookkeeping
+    for pa_decode_shared_prefix, no device work)."""
     import numpy as np
     tables = block_tables.cpu().numpy() if hasattr(block_tables, "cpu") else np.asarray(block_tables)
     lens = context_lens.cpu().numpy() if hasattr(context_lens, "cpu") else np.asarray(context_lens)
@@ -338,7 +339,13 @@ def shared_prefix_len(block_tables, context_lens, block_size: int, partition_siz
     same = (tables == tables[:1]).all(axis=0)
     pages = int(np.argmin(same)) if not same.all() else tables.shape[1]
     tokens = min(pages * block_size, int(lens.min()))
-    return tokens // partition_size * partition_size
+    return tokens // block_size * block_size
+
+
+def shared_prefix_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                                 partition_size: int) -> int:
+    return lib().pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                        partition_size)
 
 
 def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -360,9 +367,10 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     if workspace is None:
-        workspace = make_workspace(q, hkv, max_context_len, partition_size, "shared")
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        n = shared_prefix_workspace_size(B, hq, d, max_context_len, partition_size)
+        workspace = torch.empty(max(n, 16) // 4, dtype=torch.float32, device=q.device)
+    ws_ptr = workspace.data_ptr()
+    ws_bytes = workspace.numel() * workspace.element_size()
     kn, vn, sm = _append_args(k_new, v_new, slot_mapping, B, hkv, d, q.dtype)
     st = lib().pa_decode_shared_prefix(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                        block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv,

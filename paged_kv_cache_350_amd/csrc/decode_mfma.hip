@@ -132,9 +132,11 @@ void decode_mfma_kernel(DecodeParams p) {
         }
         return;
     }
-    if (part < p.first_part) return;          // read by the shared-prefix launch
-    const int start = part * p.partition;
-    const int end = min(start + p.partition, L);
+    // positions below first_token are read by a shared-prefix launch
+    const int pstart = part * p.partition;
+    if (pstart + p.partition <= p.first_token) return;
+    const int start = max(pstart, p.first_token);
+    const int end = min(pstart + p.partition, L);
 
     // Q^T as the B operand: lane (hl, j) holds head hl, dims 32 s + 8 j .. + 8.
     bf16x8_t qf[KSTEPS];

@@ -113,6 +113,10 @@ void decode_multi_kernel(DecodeParams p) {
     const int start = part * p.partition;
     if (start > hi_lim) return;                              // nothing here is visible to the group
     const int end = min(start + p.partition, hi_lim + 1);
+    // a shared prefix that ends inside this partition: its partial goes to
+    // the workspace's extra last slot, the rest of the partition is read
+    // per sequence
+    const bool to_extra = p.partial_last && L % p.partition != 0 && part == (L - 1) / p.partition;
 
     // Per tile: this lane's column, its query row and head, and the last
     // position it sees (-1: a padding column past the sequence's queries).
@@ -380,7 +384,7 @@ void decode_multi_kernel(DecodeParams p) {
             }
             const size_t orow = (size_t)(qr.row0 + jq) * p.num_heads + (size_t)g * G + c % G;
             if (p.split) {
-                const size_t rr = orow * p.max_parts + part;
+                const size_t rr = orow * p.max_parts + (to_extra ? p.max_parts - 1 : part);
                 p.ws[rr * D + d] = num;
                 if (d == 0) {
                     p.ws[rows * D + rr] = M;

@@ -212,9 +212,10 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.num_tokens = 0;
     p.max_query_len = 0;
     p.col_groups = 0;
-    p.first_part = 0;
+    p.first_token = 0;
     p.all_visible = 0;
     p.uniform_len = 0;
+    p.partial_last = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -236,11 +237,13 @@ pa_status launch_plan(const Plan& plan, hipStream_t stream) {
     return hip_status(pa_impl::launch_decode_valu(plan.p, plan.dtype, stream));
 }
 
-pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out, hipStream_t stream) {
+pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out, hipStream_t stream,
+                        bool extra_slot = false) {
     ReduceParams r;
     r.query_start = nullptr;
     r.num_groups = 0;
     r.max_query_len = 0;
+    r.extra_slot = extra_slot ? 1 : 0;
     r.ws = plan.p.ws;
     r.context_lens = context_lens;
     r.out = out;
@@ -485,6 +488,15 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     return launch_reduce(plan, context_lens, out, stream);
 }
 
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                              int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+    if (partition_size < kChunk || partition_size % kChunk != 0) return 0;
+    // one partition slot more than the split path: the extra last slot
+    return pa_impl::ws_rows(num_seqs, num_heads, parts_for(max_context_len, partition_size) + 1) *
+           (size_t)(head_dim + 2) * sizeof(float);
+}
+
 pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   int32_t block_size, int32_t num_kv_heads, float scale,
@@ -505,17 +517,26 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
                              PA_KV_SHARED, workspace, workspace_bytes,
                              /*need_out=*/true, /*force_split=*/true, &plan);
     if (st != PA_OK) return st;
-    if (shared_len < 0 || shared_len % plan.partition != 0 || shared_len > max_context_len) return PA_ERR_ARG;
+    if (shared_len < 0 || shared_len % block_size != 0 || shared_len > max_context_len) return PA_ERR_ARG;
     if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
     if (num_seqs == 0) return PA_OK;
+    const size_t need = pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                               plan.partition);
+    if (!workspace) return PA_ERR_WORKSPACE;
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    // Workspace rows hold one slot more than the context's partitions: the
+    // partial of a partition the shared prefix ends inside goes there, the
+    // rest of that partition to its own slot.
+    plan.p.max_parts += 1;
+    const int32_t P = plan.partition;
+    const bool split_part = shared_len % P != 0;
 
-    // Prefix partitions: one multi-query launch over sequence 0's table row
-    // whose query rows are all num_seqs decode queries, every row seeing
-    // all shared_len positions.  Its partials land in the rows and
-    // partition slots the split path uses for those tokens.
-    const int32_t prefix_parts = shared_len / plan.partition;
-    if (prefix_parts > 0) {
+    // Prefix positions: one multi-query launch over sequence 0's table row
+    // whose query rows are all num_seqs decode queries, every row seeing all
+    // shared_len positions.  Its partials land in the rows and slots the
+    // split path uses for those positions.
+    if (shared_len > 0) {
         DecodeParams m{};
         m.q = q;
         m.k_cache = k_cache;
@@ -534,13 +555,14 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.max_blocks_per_seq = max_blocks_per_seq;
         m.max_context_len = max_context_len;
         m.num_blocks = num_blocks;
-        m.partition = plan.partition;
+        m.partition = P;
         m.max_parts = plan.p.max_parts;
         m.split = 1;
         m.waves = 4;
         m.query_start = nullptr;              // rows 0 .. num_seqs - 1
         m.num_tokens = num_seqs;
         m.max_query_len = num_seqs;
+        const int32_t prefix_parts = (shared_len + P - 1) / P;
         // Two 16-column tiles per workgroup halve how often a shared page is
         // read; one tile runs three waves per SIMD instead of two and doubles
         // the workgroups.  One only when two would leave a single column
@@ -557,20 +579,22 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.stream_kv = 0;                      // ordinary loads: the pages are shared
         m.all_visible = 1;
         m.uniform_len = shared_len;
+        m.partial_last = 1;
         if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
         st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
         if (st != PA_OK) return st;
     }
-    // The rest of every context, sequence by sequence (with the fused append
-    // of pa_decode_append when new rows are given: position L - 1 lies past
-    // the shared prefix), then the usual merge over all partitions.
-    plan.p.first_part = prefix_parts;
+    // The rest of every context, sequence by sequence, from shared_len on
+    // (with the fused append of pa_decode_append when new rows are given:
+    // position L - 1 lies past the shared prefix), then the usual merge over
+    // the partitions plus the extra slot.
+    plan.p.first_token = shared_len;
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
     st = launch_plan(plan, stream);
     if (st != PA_OK) return st;
-    return launch_reduce(plan, context_lens, out, stream);
+    return launch_reduce(plan, context_lens, out, stream, split_part);
 }
 
 }  // extern "C"
@@ -697,6 +721,7 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
     r.query_start = query_start;
     r.num_groups = num_seqs;
     r.max_query_len = max_query_len;
+    r.extra_slot = 0;
     return hip_status(pa_impl::launch_decode_reduce(r, dtype, stream));
 }
 

@@ -40,7 +40,7 @@ struct DecodeParams {
     int32_t stream_kv;     // 1: no page is shared between sequences (streaming loads)
     int32_t waves;         // decode kernel: waves per workgroup (4, or 12 to fill a compute unit)
     int32_t order_by_length;  // 1: workgroups take sequences longest first (one-pass launches)
-    int32_t first_part;    // decode_mfma split: partitions below this are left to another launch (0: none)
+    int32_t first_token;   // decode_mfma split: positions below this are left to another launch (0: none)
     // multi-query launches only (null / 0 otherwise)
     const int32_t* query_start;   // [num_seqs + 1]: query rows of each sequence
     int32_t num_tokens;    // rows of q / out
@@ -48,6 +48,7 @@ struct DecodeParams {
     int32_t col_groups;    // column groups of 16 * col_tiles (query token, head) pairs per kv head
     int32_t all_visible;   // 1: every query row sees all L positions (a shared prefix), 0: causal rows
     int32_t uniform_len;   // > 0: every sequence's context length (context_lens is not read)
+    int32_t partial_last;  // 1: a last partition shorter than P writes its partial to slot max_parts - 1
 };
 
 struct ReduceParams {
@@ -65,6 +66,9 @@ struct ReduceParams {
     const int32_t* query_start;
     int32_t num_groups;
     int32_t max_query_len;
+    // 1: every row also merges the partial in slot max_parts - 1 (a shared
+    // prefix's last, partly shared partition)
+    int32_t extra_slot;
 };
 
 // Workspace layout for the split path (all fp32):

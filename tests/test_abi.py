@@ -289,11 +289,12 @@ def _shared(L, **kw):
     (dict(B=1025), pa.PA_ERR_UNSUPPORTED),            # prefix launch rows
     (dict(part=0), pa.PA_ERR_ARG),                    # an explicit partition is required
     (dict(part=48), pa.PA_ERR_ARG),
-    (dict(S=100), pa.PA_ERR_ARG),                     # not a multiple of the partition
+    (dict(S=100), pa.PA_ERR_ARG),                     # not whole pages
     (dict(S=-64), pa.PA_ERR_ARG),
     (dict(S=320), pa.PA_ERR_ARG),                     # beyond max_context_len
     (dict(ws=None, wsb=0), pa.PA_ERR_WORKSPACE),
     (dict(wsb=16), pa.PA_ERR_WORKSPACE),
+    (dict(wsb=4 * 32 * 4 * 130 * 4), pa.PA_ERR_WORKSPACE),   # the split path's size: one slot short
     (dict(q=None), pa.PA_ERR_NULL),
     (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
     (dict(B=0), pa.PA_OK),                            # nothing to do, nothing launched
@@ -306,8 +307,16 @@ def test_decode_shared_prefix_validates(L, kw, status):
 
 def test_shared_prefix_len_from_tables():
     t = np.array([[1, 2, 3, 4], [1, 2, 5, 6], [1, 2, 3, 7]])
-    assert pa.shared_prefix_len(t, np.array([60, 50, 64]), 16, 32) == 32
-    assert pa.shared_prefix_len(t, np.array([60, 20, 64]), 16, 32) == 0      # shortest context caps it
-    assert pa.shared_prefix_len(t[:1], np.array([60]), 16, 32) == 32
-    assert pa.shared_prefix_len(t[:, :0], np.array([5, 5, 5]), 16, 32) == 0
-    assert pa.shared_prefix_len(t, np.array([], dtype=np.int32), 16, 32) == 0
+    assert pa.shared_prefix_len(t, np.array([60, 50, 64]), 16) == 32
+    assert pa.shared_prefix_len(t, np.array([60, 20, 64]), 16) == 16      # shortest context caps it, whole pages
+    assert pa.shared_prefix_len(t[:1], np.array([60]), 16) == 48
+    assert pa.shared_prefix_len(t[:, :0], np.array([5, 5, 5]), 16) == 0
+    assert pa.shared_prefix_len(t, np.array([], dtype=np.int32), 16) == 0
+
+
+def test_shared_prefix_workspace_size():
+    # the split path's layout with one slot more per (sequence, head)
+    assert pa.shared_prefix_workspace_size(3, 4, 64, 33, 32) == 3 * 4 * 3 * 66 * 4
+    assert pa.shared_prefix_workspace_size(100, 32, 128, 10512, 1024) == 100 * 32 * 12 * 130 * 4
+    assert pa.shared_prefix_workspace_size(3, 4, 64, 33, 48) == 0                 # not a multiple of 32
+    assert pa.shared_prefix_workspace_size(-1, 4, 64, 33, 32) == 0

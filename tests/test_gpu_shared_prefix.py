@@ -62,25 +62,25 @@ def test_shared_prefix_matches_oracle(shape):
     w, t = _shared_batch("shared", 41, hq, hkv, d, bs, shared_tokens=640)
     say("shared prefix", shape, w.summary())
     ref = step_and_reference(pa, w, t, range(w.num_seqs))
-    for P in (32, 64, 128, 256):
-        S = pa.shared_prefix_len(w.block_tables, w.context_lens, bs, P)
-        say("  partition", P, "shared_len", S)
-        assert S > 0 and S % P == 0
-        out = _run(pa, w, t, S, P)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, bs)
+    assert S == 640
+    for P in (32, 64, 128, 256, 96):
+        # the whole shared run, and shorter ones (still valid: fewer shared
+        # pages), ending on and inside partitions (the extra slot)
+        for s_len in sorted({S, S - bs, max(S - P - bs, 0), bs}, reverse=True):
+            say("  partition", P, "shared_len", s_len, "ends inside a partition:", s_len % P != 0)
+            out = _run(pa, w, t, s_len, P)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, "bf16", f"shared {shape} P={P} S={s_len}")
+        again = _run(pa, w, t, S - bs, P)
         torch.cuda.synchronize()
-        check_close(out_f64(out), ref, "bf16", f"shared {shape} P={P} S={S}")
-        again = _run(pa, w, t, S, P)
-        torch.cuda.synchronize()
-        assert bits_equal(out, again), f"repeat {shape} P={P}"
-        # a shorter shared length is as valid: fewer prefix partitions
-        out2 = _run(pa, w, t, S - P, P)
-        torch.cuda.synchronize()
-        check_close(out_f64(out2), ref, "bf16", f"shared {shape} P={P} S={S - P}")
+        assert bits_equal(_run(pa, w, t, S - bs, P), again), f"repeat {shape} P={P}"
 
 
 def test_zero_shared_length_is_the_split_path():
     """shared_len 0 launches no prefix work: bit-identical to pa_decode's
-    split path on the matrix-core kernel with shared-page loads."""
+    split path on the matrix-core kernel with shared-page loads (only the
+    workspace rows are one slot longer)."""
     pa = require_gpu()
     w, t = _shared_batch("shared_zero", 42, 32, 8, 128, 16, shared_tokens=320)
     say("shared prefix, shared_len 0", w.summary())
@@ -101,11 +101,12 @@ def test_many_sequences_fill_several_column_groups():
     say("shared prefix, 200 sequences", w.summary())
     seqs = [0, 1, 7, 31, 32, 33, 99, 150, 198, 199]
     ref = step_and_reference(pa, w, t, seqs)
-    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16, 256)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16)
     assert S == 1024
-    out = _run(pa, w, t, S, 256)
-    torch.cuda.synchronize()
-    check_close(out_f64(out)[seqs], ref, "bf16", "shared 200 seqs")
+    for P in (256, 384):                              # 1024 = 2 x 384 + 256: the extra slot
+        out = _run(pa, w, t, S, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out)[seqs], ref, "bf16", f"shared 200 seqs P={P}")
 
 
 @pytest.mark.parametrize("name", ["prefix_share", "beam_fork"])
@@ -123,14 +124,14 @@ def test_named_workload_full_size(name):
     seqs = sorted({int(order[0]), int(order[-1])} |
                   set(int(s) for s in rng.choice(w.num_seqs, size=min(6, w.num_seqs), replace=False)))
     ref = step_and_reference(pa, w, t, seqs)
-    P = 2048
-    S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size, P)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)
     say("  shared_len", S)
-    assert S >= 8192
-    out = _run(pa, w, t, S, P)
-    torch.cuda.synchronize()
-    stats = check_close(out_f64(out)[seqs], ref, "bf16", f"shared {name}")
-    say("  ", stats)
+    assert S >= 9984
+    for P in (1024, 2048):
+        out = _run(pa, w, t, S, P)
+        torch.cuda.synchronize()
+        stats = check_close(out_f64(out)[seqs], ref, "bf16", f"shared {name} P={P}")
+        say("  ", P, stats)
 
 
 def test_fused_append():
@@ -155,8 +156,9 @@ def test_fused_append():
     ref = oracle.decode(storage_np(t["q"]), rk, rv, w.block_tables, w.context_lens, w.scale, w.block_size,
                         "bf16")
     slots = torch.from_numpy(mask).cuda()
-    for P in (64, 256):
-        S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size, P)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)
+    assert S == 512
+    for P in (64, 256, 192):                          # 512 = 2 x 192 + 128: the extra slot
         say("  partition", P, "shared_len", S)
         kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
         out = pa.decode_shared_prefix(t["q"], kc, vc, t["block_tables"], t["context_lens"], w.scale,
@@ -182,9 +184,9 @@ def test_few_sequences(nseq):
     w, t = _shared_batch("shared_few", 45 + nseq, 32, 8, 128, 16, shared_tokens=768, nseq=nseq)
     say("shared prefix,", nseq, "sequences", w.summary())
     ref = step_and_reference(pa, w, t, range(w.num_seqs))
-    for P in (128, 256):
-        S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16, P)
-        assert S == 768
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16)
+    assert S == 768
+    for P in (128, 256, 320):                         # 768 = 2 x 320 + 128: the extra slot
         out = _run(pa, w, t, S, P)
         torch.cuda.synchronize()
         check_close(out_f64(out), ref, "bf16", f"shared {nseq} seqs P={P}")
