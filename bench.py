@@ -541,7 +541,8 @@ def main(argv=None) -> int:
     split = P > 0
     out = torch.empty_like(t["q"])
     if prefix:
-        nws = pa.shared_prefix_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.max_context_len, P)
+        nws = pa.shared_prefix_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                              w.max_context_len, shared_len, P)
         ws = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
     else:
         ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P, reuse) if split else None

@@ -302,19 +302,20 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
  * head) pairs at a time -- a matrix-core launch whose columns are the
  * decode queries of several sequences, each seeing all shared_len
  * positions -- instead of once per sequence; the rest of every context is
- * read per sequence by the split decode kernel.  Both write the split
- * path's partials; the partition that holds position shared_len (when
- * shared_len is not a multiple of partition_size) gets two, the shared part
- * in one extra slot per (sequence, head), and the merge kernel combines
- * them all.  The result is the same attention as pa_decode, within the same
- * bounds.
+ * read per sequence by the split decode kernel from position shared_len
+ * on.  The prefix launch picks its own partition size; its partials take
+ * the first slots of every (sequence, head) workspace row and the
+ * per-sequence partitions follow, so the merge kernel combines one
+ * contiguous run per row.  The result is the same attention as pa_decode,
+ * within the same bounds.
  *
  *   shared_len      a multiple of block_size, 0 <= shared_len <=
  *                   max_context_len (0: the plain split path)
- *   partition_size  > 0, a multiple of 32
+ *   partition_size  > 0, a multiple of 32: the per-sequence launch's
+ *                   partition
  *   workspace       >= pa_decode_shared_prefix_workspace_size(num_seqs,
- *                   num_heads, head_dim, max_context_len, partition_size)
- *                   bytes
+ *                   num_heads, num_kv_heads, head_dim, max_context_len,
+ *                   shared_len, partition_size) bytes
  *   k_new, v_new, slot_mapping  NULL for a plain decode; otherwise each
  *                   sequence's newest rows are appended as by
  *                   pa_decode_append (position L - 1 must lie past
@@ -339,13 +340,14 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
                                   const void* k_new, const void* v_new, const int64_t* slot_mapping);
 
 /*
- * Workspace bytes pa_decode_shared_prefix needs: the split path's layout
- * with one partition slot more per (sequence, head),
- * num_seqs * num_heads * (ceil(max_context_len / partition_size) + 1) *
- * (head_dim + 2) * 4.  Returns 0 for invalid arguments.
+ * Workspace bytes pa_decode_shared_prefix needs for these arguments:
+ * num_seqs * num_heads * (slots per row) * (head_dim + 2) * 4, a row
+ * holding the prefix launch's partials and then the per-sequence ones.
+ * Returns 0 for invalid arguments.
  */
-size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                              int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_context_len, int32_t shared_len,
+                                              int32_t partition_size);
 
 /*
  * pa_copy_blocks -- copy whole pages (K and V, every kv head) for

@@ -57,7 +57,8 @@ _SIGNATURES = {
     "pa_decode_shared_prefix": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                  _vp, _c_size, _vp, _vp, _vp], _c_int),
-    "pa_decode_shared_prefix_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
+    "pa_decode_shared_prefix_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
+                                               _c_size),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -342,10 +343,10 @@ def shared_prefix_len(block_tables, context_lens, block_size: int) -> int:
     return tokens // block_size * block_size
 
 
-def shared_prefix_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
-                                 partition_size: int) -> int:
-    return lib().pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
-                                                        partition_size)
+def shared_prefix_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                 max_context_len: int, shared_len: int, partition_size: int) -> int:
+    return lib().pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                        max_context_len, shared_len, partition_size)
 
 
 def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -367,7 +368,7 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     if workspace is None:
-        n = shared_prefix_workspace_size(B, hq, d, max_context_len, partition_size)
+        n = shared_prefix_workspace_size(B, hq, hkv, d, max_context_len, shared_len, partition_size)
         workspace = torch.empty(max(n, 16) // 4, dtype=torch.float32, device=q.device)
     ws_ptr = workspace.data_ptr()
     ws_bytes = workspace.numel() * workspace.element_size()

@@ -357,7 +357,8 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    const size_t rows = ws_rows(p.num_seqs, p.num_heads, p.max_parts);
+    const int wsp = p.ws_parts > 0 ? p.ws_parts : p.max_parts;      // workspace row length
+    const size_t rows = ws_rows(p.num_seqs, p.num_heads, wsp);
     for (int e = tid; e < G * D; e += kThreads) {
         const int h = e / D;
         const int d = e % D;
@@ -372,7 +373,7 @@ void decode_mfma_kernel(DecodeParams p) {
             }
         }
         if (p.split) {
-            const size_t rr = (head0 + h) * p.max_parts + part;
+            const size_t rr = (head0 + h) * wsp + part + p.slot_shift;
             p.ws[rr * D + d] = num;
             if (d == 0) {
                 p.ws[rows * D + rr] = M;

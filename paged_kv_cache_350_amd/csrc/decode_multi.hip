@@ -113,10 +113,6 @@ void decode_multi_kernel(DecodeParams p) {
     const int start = part * p.partition;
     if (start > hi_lim) return;                              // nothing here is visible to the group
     const int end = min(start + p.partition, hi_lim + 1);
-    // a shared prefix that ends inside this partition: its partial goes to
-    // the workspace's extra last slot, the rest of the partition is read
-    // per sequence
-    const bool to_extra = p.partial_last && L % p.partition != 0 && part == (L - 1) / p.partition;
 
     // Per tile: this lane's column, its query row and head, and the last
     // position it sees (-1: a padding column past the sequence's queries).
@@ -349,7 +345,8 @@ void decode_multi_kernel(DecodeParams p) {
     }
 
     // ---- merge the four waves, one tile at a time through the same LDS
-    const size_t rows = ws_rows(p.num_tokens, p.num_heads, p.max_parts);
+    const int wsp = p.ws_parts > 0 ? p.ws_parts : p.max_parts;      // workspace row length
+    const size_t rows = ws_rows(p.num_tokens, p.num_heads, wsp);
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     for (int nt = 0; nt < NT; ++nt) {
         float l = l_run[nt];
@@ -384,7 +381,7 @@ void decode_multi_kernel(DecodeParams p) {
             }
             const size_t orow = (size_t)(qr.row0 + jq) * p.num_heads + (size_t)g * G + c % G;
             if (p.split) {
-                const size_t rr = orow * p.max_parts + (to_extra ? p.max_parts - 1 : part);
+                const size_t rr = orow * wsp + part;
                 p.ws[rr * D + d] = num;
                 if (d == 0) {
                     p.ws[rows * D + rr] = M;

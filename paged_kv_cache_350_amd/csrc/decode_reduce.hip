@@ -107,24 +107,15 @@ void decode_reduce_kernel(ReduceParams p) {
     }
     const float m0 = lane < p.max_parts ? wm[lane] : neg_inf();
     const float l0 = lane < p.max_parts ? wl[lane] : 0.f;
-    // the extra slot (a shared prefix's partly shared partition) sits at a
-    // fixed index: its loads go out with the others
-    vec_t xrow = vec_t{};
-    float xm = neg_inf(), xl = 0.f;
-    if (p.extra_slot) {
-        xrow = *reinterpret_cast<const vec_t*>(acc + (size_t)(p.max_parts - 1) * D + DPL * lane);
-        xm = wm[p.max_parts - 1];
-        xl = wl[p.max_parts - 1];
-    }
 
     const int L = p.query_start ? token_context(p, b) : clamp_len(p.context_lens[b], p.max_context_len);
     int n = (L + p.partition - 1) / p.partition;
-    n = n > p.max_parts ? p.max_parts : n;
+    n += p.slot_shift;
+    n = n < 0 ? 0 : (n > p.max_parts ? p.max_parts : n);
 
     float M = lane < n ? m0 : neg_inf();
     for (int q = lane + kWave; q < n; q += kWave) M = fmaxf(M, wm[q]);
     M = wave_max(M);
-    M = fmaxf(M, xm);
 
     float a[DPL];
     for (int i = 0; i < DPL; ++i) a[i] = 0.f;
@@ -176,16 +167,6 @@ void decode_reduce_kernel(ReduceParams p) {
         }
     }
     den = wave_sum(den);
-    if (p.extra_slot && xm != neg_inf()) {
-        const float wx = fast_exp2(xm - M);
-        if constexpr (DPL == 1) {
-            a[0] = fmaf(wx, xrow, a[0]);
-        } else {
-            a[0] = fmaf(wx, xrow[0], a[0]);
-            a[1] = fmaf(wx, xrow[1], a[1]);
-        }
-        den = fmaf(wx, xl, den);
-    }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     for (int i = 0; i < DPL; ++i) store_out<E>(out, (size_t)DPL * lane + i, den > 0.f ? a[i] * inv : 0.f);
 }

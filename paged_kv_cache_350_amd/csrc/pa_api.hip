@@ -118,6 +118,51 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim
     return pa_impl::ws_rows(num_seqs, num_heads, parts) * (size_t)(head_dim + 2) * sizeof(float);
 }
 
+// Shared-prefix call: the prefix launch reads positions [0, shared_len) in
+// partitions of Pp tokens, whose partials take workspace slots 0 .. np - 1
+// of every row; the per-sequence launch reads from shared_len on in
+// partitions of P, partition p >= q0 = shared_len / P writing slot p + shift
+// with shift = np - q0, so each row's partials stay contiguous and the merge
+// takes slots 0 .. ceil(L / P) + shift - 1.  Pp = P: prefix partitions of
+// 1024 or 512 tokens under P = 2048 measured no faster (100 sequences over
+// 9,984 shared tokens: 94.5 and 113.8 us against 95.3; 8 beams: 39.7 and
+// 44.2 against 38.2).
+struct PrefixShape {
+    int32_t Pp;
+    int32_t np;
+    int32_t shift;
+    int32_t row;     // slots per workspace row
+    int32_t tiles;   // 16-column tiles per prefix workgroup
+    int32_t col_groups;
+};
+
+int32_t multi_col_tiles(int32_t group, int32_t max_query_len);
+int32_t multi_col_groups(int32_t group, int32_t max_query_len);
+
+PrefixShape prefix_shape(int32_t num_seqs, int32_t group, int32_t num_kv_heads, int32_t max_context_len,
+                         int32_t shared_len, int32_t P) {
+    PrefixShape sh;
+    // Two 16-column tiles per workgroup halve how often a shared page is
+    // read; one tile runs three waves per SIMD instead of two and doubles
+    // the workgroups.  One only when two would leave a single column group
+    // and fewer than kPrefixFill workgroups (two per compute unit at this
+    // kernel's occupancy).  Measured: 8 beams over 32,768 tokens (one group
+    // of 32 columns) 41.2 us with two tiles, 37.3 with one; 100 sequences
+    // over a 9,216-token prefix (13 groups) 108 us with two, 125 with one,
+    // and at 416 workgroups still 111 against 138.
+    sh.tiles = multi_col_tiles(group, num_seqs);
+    const int32_t parts_at_P = (shared_len + P - 1) / P;
+    if (sh.tiles == 2 && multi_col_groups(group, num_seqs) == 1 && (int64_t)num_kv_heads * parts_at_P < kPrefixFill)
+        sh.tiles = 1;
+    sh.col_groups = (int32_t)(((int64_t)group * num_seqs + 16 * sh.tiles - 1) / (16 * sh.tiles));
+    sh.Pp = P;
+    sh.np = shared_len > 0 ? (shared_len + sh.Pp - 1) / sh.Pp : 0;
+    sh.shift = sh.np - shared_len / P;
+    sh.row = parts_for(max_context_len, P) + sh.shift;
+    if (sh.row < 1) sh.row = 1;
+    return sh;
+}
+
 struct Plan {
     DecodeParams p;
     pa_dtype dtype;
@@ -215,7 +260,8 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.first_token = 0;
     p.all_visible = 0;
     p.uniform_len = 0;
-    p.partial_last = 0;
+    p.ws_parts = 0;
+    p.slot_shift = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -237,13 +283,12 @@ pa_status launch_plan(const Plan& plan, hipStream_t stream) {
     return hip_status(pa_impl::launch_decode_valu(plan.p, plan.dtype, stream));
 }
 
-pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out, hipStream_t stream,
-                        bool extra_slot = false) {
+pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out, hipStream_t stream) {
     ReduceParams r;
     r.query_start = nullptr;
     r.num_groups = 0;
     r.max_query_len = 0;
-    r.extra_slot = extra_slot ? 1 : 0;
+    r.slot_shift = plan.p.slot_shift;
     r.ws = plan.p.ws;
     r.context_lens = context_lens;
     r.out = out;
@@ -252,7 +297,7 @@ pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out
     r.head_dim = plan.p.head_dim;
     r.max_context_len = plan.p.max_context_len;
     r.partition = plan.p.partition;
-    r.max_parts = plan.p.max_parts;
+    r.max_parts = plan.p.ws_parts > 0 ? plan.p.ws_parts : plan.p.max_parts;
     return hip_status(pa_impl::launch_decode_reduce(r, plan.dtype, stream));
 }
 
@@ -485,16 +530,20 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     plan.p.max_context_len = max_context_len;
     plan.p.partition = partition;
     plan.p.max_parts = parts_for(max_context_len, partition);
+    plan.p.ws_parts = 0;
+    plan.p.slot_shift = 0;
     return launch_reduce(plan, context_lens, out, stream);
 }
 
-size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                              int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_context_len, int32_t shared_len,
+                                              int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 0;
+    if (head_dim <= 0 || max_context_len < 0 || shared_len < 0 || shared_len > max_context_len) return 0;
     if (partition_size < kChunk || partition_size % kChunk != 0) return 0;
-    // one partition slot more than the split path: the extra last slot
-    return pa_impl::ws_rows(num_seqs, num_heads, parts_for(max_context_len, partition_size) + 1) *
-           (size_t)(head_dim + 2) * sizeof(float);
+    const PrefixShape sh = prefix_shape(num_seqs, num_heads / num_kv_heads, num_kv_heads, max_context_len,
+                                        shared_len, partition_size);
+    return pa_impl::ws_rows(num_seqs, num_heads, sh.row) * (size_t)(head_dim + 2) * sizeof(float);
 }
 
 pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
@@ -521,22 +570,17 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
     if (num_seqs == 0) return PA_OK;
-    const size_t need = pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
-                                                               plan.partition);
+    const int32_t P = plan.partition;
+    const PrefixShape sh = prefix_shape(num_seqs, plan.p.group, num_kv_heads, max_context_len, shared_len, P);
+    const size_t need = pa_impl::ws_rows(num_seqs, num_heads, sh.row) * (size_t)(head_dim + 2) * sizeof(float);
     if (!workspace) return PA_ERR_WORKSPACE;
     if (workspace_bytes < need) return PA_ERR_WORKSPACE;
-    // Workspace rows hold one slot more than the context's partitions: the
-    // partial of a partition the shared prefix ends inside goes there, the
-    // rest of that partition to its own slot.
-    plan.p.max_parts += 1;
-    const int32_t P = plan.partition;
-    const bool split_part = shared_len % P != 0;
 
     // Prefix positions: one multi-query launch over sequence 0's table row
     // whose query rows are all num_seqs decode queries, every row seeing all
-    // shared_len positions.  Its partials land in the rows and slots the
-    // split path uses for those positions.
-    if (shared_len > 0) {
+    // shared_len positions, in partitions of sh.Pp written to slots
+    // 0 .. sh.np - 1 of every row.
+    if (sh.np > 0) {
         DecodeParams m{};
         m.q = q;
         m.k_cache = k_cache;
@@ -555,46 +599,35 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.max_blocks_per_seq = max_blocks_per_seq;
         m.max_context_len = max_context_len;
         m.num_blocks = num_blocks;
-        m.partition = P;
-        m.max_parts = plan.p.max_parts;
+        m.partition = sh.Pp;
+        m.max_parts = sh.np;
+        m.ws_parts = sh.row;
         m.split = 1;
         m.waves = 4;
         m.query_start = nullptr;              // rows 0 .. num_seqs - 1
         m.num_tokens = num_seqs;
         m.max_query_len = num_seqs;
-        const int32_t prefix_parts = (shared_len + P - 1) / P;
-        // Two 16-column tiles per workgroup halve how often a shared page is
-        // read; one tile runs three waves per SIMD instead of two and doubles
-        // the workgroups.  One only when two would leave a single column
-        // group and fewer than kPrefixFill workgroups (two per compute unit
-        // at this kernel's occupancy).  Measured: 8 beams over 32,768 tokens
-        // (one group of 32 columns) 41.2 us with two tiles, 37.3 with one;
-        // 100 sequences over a 9,216-token prefix (13 groups) 108 us with
-        // two, 125 with one, and at 416 workgroups still 111 against 138.
-        int32_t tiles = multi_col_tiles(m.group, num_seqs);
-        if (tiles == 2 && multi_col_groups(m.group, num_seqs) == 1 &&
-            (int64_t)num_kv_heads * prefix_parts < kPrefixFill)
-            tiles = 1;
-        m.col_groups = (int32_t)(((int64_t)m.group * num_seqs + 16 * tiles - 1) / (16 * tiles));
+        m.col_groups = sh.col_groups;
         m.stream_kv = 0;                      // ordinary loads: the pages are shared
         m.all_visible = 1;
         m.uniform_len = shared_len;
-        m.partial_last = 1;
         if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
-        st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
+        st = hip_status(pa_impl::launch_decode_multi(m, sh.tiles, stream));
         if (st != PA_OK) return st;
     }
     // The rest of every context, sequence by sequence, from shared_len on
     // (with the fused append of pa_decode_append when new rows are given:
-    // position L - 1 lies past the shared prefix), then the usual merge over
-    // the partitions plus the extra slot.
+    // position L - 1 lies past the shared prefix), its partitions shifted
+    // past the prefix slots, then the usual merge.
     plan.p.first_token = shared_len;
+    plan.p.ws_parts = sh.row;
+    plan.p.slot_shift = sh.shift;
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
     st = launch_plan(plan, stream);
     if (st != PA_OK) return st;
-    return launch_reduce(plan, context_lens, out, stream, split_part);
+    return launch_reduce(plan, context_lens, out, stream);
 }
 
 }  // extern "C"
@@ -721,7 +754,7 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
     r.query_start = query_start;
     r.num_groups = num_seqs;
     r.max_query_len = max_query_len;
-    r.extra_slot = 0;
+    r.slot_shift = 0;
     return hip_status(pa_impl::launch_decode_reduce(r, dtype, stream));
 }
 

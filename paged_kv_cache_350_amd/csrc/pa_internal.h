@@ -48,7 +48,8 @@ struct DecodeParams {
     int32_t col_groups;    // column groups of 16 * col_tiles (query token, head) pairs per kv head
     int32_t all_visible;   // 1: every query row sees all L positions (a shared prefix), 0: causal rows
     int32_t uniform_len;   // > 0: every sequence's context length (context_lens is not read)
-    int32_t partial_last;  // 1: a last partition shorter than P writes its partial to slot max_parts - 1
+    int32_t ws_parts;      // > 0: partial slots per workspace row (else max_parts)
+    int32_t slot_shift;    // split: partition p writes workspace slot p + slot_shift
 };
 
 struct ReduceParams {
@@ -66,9 +67,9 @@ struct ReduceParams {
     const int32_t* query_start;
     int32_t num_groups;
     int32_t max_query_len;
-    // 1: every row also merges the partial in slot max_parts - 1 (a shared
-    // prefix's last, partly shared partition)
-    int32_t extra_slot;
+    // a row merges slots 0 .. ceil(L / partition) + slot_shift - 1 (a
+    // shared prefix's partials come first, read in partitions of their own)
+    int32_t slot_shift;
 };
 
 // Workspace layout for the split path (all fp32):

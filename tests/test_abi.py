@@ -294,7 +294,7 @@ def _shared(L, **kw):
     (dict(S=320), pa.PA_ERR_ARG),                     # beyond max_context_len
     (dict(ws=None, wsb=0), pa.PA_ERR_WORKSPACE),
     (dict(wsb=16), pa.PA_ERR_WORKSPACE),
-    (dict(wsb=4 * 32 * 4 * 130 * 4), pa.PA_ERR_WORKSPACE),   # the split path's size: one slot short
+    (dict(S=144, wsb=4 * 32 * 4 * 130 * 4), pa.PA_ERR_WORKSPACE),   # the split path's size: a slot short
     (dict(q=None), pa.PA_ERR_NULL),
     (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
     (dict(B=0), pa.PA_OK),                            # nothing to do, nothing launched
@@ -315,8 +315,12 @@ def test_shared_prefix_len_from_tables():
 
 
 def test_shared_prefix_workspace_size():
-    # the split path's layout with one slot more per (sequence, head)
-    assert pa.shared_prefix_workspace_size(3, 4, 64, 33, 32) == 3 * 4 * 3 * 66 * 4
-    assert pa.shared_prefix_workspace_size(100, 32, 128, 10512, 1024) == 100 * 32 * 12 * 130 * 4
-    assert pa.shared_prefix_workspace_size(3, 4, 64, 33, 48) == 0                 # not a multiple of 32
-    assert pa.shared_prefix_workspace_size(-1, 4, 64, 33, 32) == 0
+    # the prefix launch's partitions first, then the per-sequence ones from
+    # shared_len / P on; with the prefix launch at partition P that is the
+    # split path's row plus one slot when shared_len ends inside a partition
+    assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 33, 0, 32) == 3 * 4 * 2 * 66 * 4
+    assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 96, 64, 32) == 3 * 4 * 3 * 66 * 4
+    assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 96, 48, 32) == 3 * 4 * 4 * 66 * 4
+    assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 33, 0, 48) == 0                  # not a multiple of 32
+    assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 33, 40, 32) == 0                 # past max_context_len
+    assert pa.shared_prefix_workspace_size(-1, 4, 4, 64, 33, 0, 32) == 0
