@@ -170,6 +170,16 @@ pa_status pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int32_t n, 
  * unknown id, PA_ERR_ARG if a sequence holds more than max_blocks_per_seq
  * pages or more than 2^31 - 1 tokens.
  */
+/*
+ * Tokens that seq_ids[0 .. n) share in the same physical pages: the leading
+ * pages that are one and the same page in every sequence (a forked prompt,
+ * beams), in whole pages and capped by the shortest sequence.  That is the
+ * shared_len pa_decode_shared_prefix takes for a batch of these sequences in
+ * this order.  0 for n == 0; -1 for a NULL manager, n < 0, seq_ids NULL with
+ * n > 0, or an unknown id.  [Internals, "Copy-on-Write and Prefix Sharing"]
+ */
+int64_t pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n);
+
 pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks_per_seq, int32_t pad_page, int32_t* tables,
                              int32_t* context_lens);

@@ -34,6 +34,7 @@ _SIGNATURES = {
     "pa_bm_free": ([_vp, _i64], _i32),
     "pa_bm_append": ([_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp], _i32),
     "pa_bm_block_tables": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
+    "pa_bm_shared_prefix": ([_vp, _vp, _i32], _i64),
 }
 
 PA_ERR_OUT_OF_PAGES, PA_ERR_NOT_FOUND, PA_ERR_HOST_MEMORY = -6, -7, -8
@@ -233,6 +234,15 @@ class NativeBlockManager:
     def take_copies(self) -> List[Tuple[int, int]]:
         out, self.pending_copies = self.pending_copies, []
         return out
+
+    def shared_prefix(self, seqs: Sequence[int]) -> int:
+        """Tokens the sequences share in the same pages, in whole pages
+        (pa_decode_shared_prefix's shared_len for a batch of them)."""
+        ids = np.ascontiguousarray(np.asarray(list(seqs), dtype=np.int64))
+        n = int(_lib().pa_bm_shared_prefix(self._h, _ptr(ids) if len(ids) else None, int(ids.shape[0])))
+        if n < 0:
+            raise KeyError("unknown sequence id")
+        return n
 
     def block_tables(self, seqs: Sequence[int], max_blocks_per_seq: int,
                      pad_page: int = 0) -> Tuple[np.ndarray, np.ndarray]:

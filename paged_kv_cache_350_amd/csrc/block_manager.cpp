@@ -502,6 +502,30 @@ pa_status pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int32_t n, 
     });
 }
 
+int64_t pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n) {
+    if (!bm || n < 0 || (n > 0 && !seq_ids)) return -1;
+    if (n == 0) return 0;
+    const auto first = bm->seqs.find(seq_ids[0]);
+    if (first == bm->seqs.end()) return -1;
+    const std::vector<int32_t>& p0 = first->second.pages;
+    size_t pages = p0.size();
+    int64_t min_len = first->second.len;
+    for (int32_t i = 1; i < n; ++i) {
+        const auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end()) return -1;
+        const std::vector<int32_t>& pi = it->second.pages;
+        size_t k = 0;
+        const size_t lim = pages < pi.size() ? pages : pi.size();
+        while (k < lim && pi[k] == p0[k]) ++k;
+        pages = k;
+        if (it->second.len < min_len) min_len = it->second.len;
+    }
+    const int64_t bs = bm->block_size;
+    const int64_t by_pages = (int64_t)pages * bs;
+    const int64_t by_len = min_len / bs * bs;
+    return by_pages < by_len ? by_pages : by_len;
+}
+
 pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks_per_seq, int32_t pad_page, int32_t* tables,
                              int32_t* context_lens) {

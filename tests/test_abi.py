@@ -19,7 +19,7 @@ def declared_functions():
     names = set()
     for header in HEADERS:
         text = open(header).read()
-        names |= set(re.findall(r"^\s*(?:pa_status|size_t|int32_t|const char\*)\s+(pa_\w+)\s*\(",
+        names |= set(re.findall(r"^\s*(?:pa_status|size_t|int32_t|int64_t|void|const char\*)\s+(pa_\w+)\s*\(",
                                 text, flags=re.M))
     return sorted(names)
 

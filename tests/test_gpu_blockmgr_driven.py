@@ -104,3 +104,74 @@ def test_decode_loop_driven_by_native_manager():
     assert copies_seen == 5                                  # five children leave the shared page
     assert np.array_equal(storage_np(kc).view(np.uint16), hk.view(np.uint16))
     assert np.array_equal(storage_np(vc).view(np.uint16), hv.view(np.uint16))
+
+
+def test_beams_driven_by_native_manager_through_the_shared_prefix_path():
+    """Eight beams fork one 200-token prompt (its last page partly filled).
+    Every step the manager appends a token to each beam (the first step copies
+    the shared tail page for each of them), its copy pairs go to
+    pa_copy_blocks, and pa_decode_shared_prefix appends the rows and decodes,
+    with the shared length the manager reports.  The oracle's pool runs in
+    lockstep; each step's output is checked against the oracle decode and the
+    caches bit for bit at the end."""
+    pa = require_gpu()
+    bs, hq, hkv, d, nb, maxb, steps = 16, 32, 8, 128, 200, 16, 6
+    rng = np.random.default_rng(41)
+    order = rng.permutation(nb)
+    m = pa.NativeBlockManager(nb, bs, free_order=order)
+    pool = oracle.PrefixCachingPool(nb, bs, free_order=order.tolist())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(42)
+
+    def rows(n):
+        return (torch.randn(n, hkv, d, generator=g, device="cuda").to(torch.bfloat16),
+                torch.randn(n, hkv, d, generator=g, device="cuda").to(torch.bfloat16))
+
+    x = W.chunk_elems("bf16")
+    nan = float("nan")
+    kc = torch.full((nb, hkv, d // x, bs, x), nan, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((nb, hkv, d, bs), nan, dtype=torch.bfloat16, device="cuda")
+    hk, hv = storage_np(kc), storage_np(vc)
+
+    m.allocate(0, 0)
+    pool.allocate(0, 0)
+    slots0, _ = m.append(np.full(200, 0, dtype=np.int64))
+    pslots0 = [pool.append_token(0) for _ in range(200)]
+    assert slots0.tolist() == pslots0
+    k0, v0 = rows(200)
+    pa.kv_append(k0, v0, torch.from_numpy(slots0).cuda(), kc, vc)
+    hk, hv = oracle.kv_append(storage_np(k0), storage_np(v0), pslots0, hk, hv, bs)
+    beams = np.arange(1, 9, dtype=np.int64)
+    for b in beams.tolist():
+        m.fork(0, b)
+        pool.fork(0, b)
+    tables, lens = m.block_tables(beams, maxb, pad_page=nb - 1)
+    tables, lens = tables.copy(), lens.copy()
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    for step in range(steps):
+        slots, copies = m.append(beams, tables, lens)
+        before = len(pool.copies)
+        pslots = [pool.append_token(int(b)) for b in beams]
+        assert slots.tolist() == pslots
+        shared = m.shared_prefix(beams)
+        assert shared == 192                                  # the prompt's 12 whole pages
+        say("beam step", step, "copies", len(copies), "shared_len", shared)
+        if len(copies):
+            pa.copy_blocks(kc, vc, torch.from_numpy(np.ascontiguousarray(copies)).cuda())
+            hk, hv = oracle.copy_blocks(hk, hv, np.array(pool.copies[before:], dtype=np.int64))
+        k, v = rows(len(beams))
+        q = torch.randn(len(beams), hq, d, generator=g, device="cuda").to(torch.bfloat16)
+        out = pa.decode_shared_prefix(q, kc, vc, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                      scale, int(lens.max()), shared, 64, k_new=k, v_new=v,
+                                      slot_mapping=torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        hk, hv = oracle.kv_append(storage_np(k), storage_np(v), pslots, hk, hv, bs)
+        ptables = np.full((len(beams), maxb), nb - 1, dtype=np.int32)
+        for i, b in enumerate(beams.tolist()):
+            ptables[i, :len(pool.pages[b])] = pool.pages[b]
+        plens = np.array([pool.length[b] for b in beams.tolist()], dtype=np.int32)
+        assert np.array_equal(ptables, tables) and np.array_equal(plens, lens)
+        ref = oracle.decode(storage_np(q), hk, hv, ptables, plens, scale, bs, "bf16")
+        check_close(out_f64(out), ref, "bf16", f"beam step {step}")
+    assert np.array_equal(storage_np(kc).view(np.uint16), hk.view(np.uint16))
+    assert np.array_equal(storage_np(vc).view(np.uint16), hv.view(np.uint16))

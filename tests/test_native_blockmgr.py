@@ -279,3 +279,48 @@ def test_in_place_table_update_errors_change_nothing():
             m.append(ids, t, l)
     assert m.length(0) == 7 + 4 and m.length(1) == 8 + 4   # the failing call changed nothing
     assert np.array_equal(t, m.block_tables(ids, 3)[0])
+
+
+def test_shared_prefix_of_forks_and_beams():
+    """The tokens a set of sequences holds in the same pages: all of a forked
+    prompt's whole pages; copy-on-write of the shared tail page ends the
+    sharing there; unrelated sequences share nothing."""
+    m = pa.NativeBlockManager(64, 16)
+    m.allocate(0, 100)                        # 7 pages, the last holding 4 tokens
+    for c in (1, 2, 3):
+        m.fork(0, c)
+    assert m.shared_prefix([1, 2, 3]) == 96   # whole pages, capped by the 100 tokens
+    assert m.shared_prefix([2]) == 96
+    m.append_token(1)                         # copy-on-write of page 6 for sequence 1
+    assert m.shared_prefix([1, 2, 3]) == 96
+    for _ in range(60):
+        m.append_token(2)
+        m.append_token(3)
+    assert m.shared_prefix([2, 3]) == 96      # both copied page 6 (CoW), then own pages
+    m.allocate(9, 40)
+    assert m.shared_prefix([9, 1]) == 0
+    assert m.shared_prefix([]) == 0
+    with pytest.raises(KeyError):
+        m.shared_prefix([1, 77])
+    m.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_shared_prefix_agrees_with_the_tables(seed):
+    """The manager's answer equals the one read off its own block tables
+    (leading entries equal in every row, whole pages, capped by the shortest
+    context)."""
+    rng = np.random.default_rng(seed)
+    bs = 16
+    m = pa.NativeBlockManager(4096, bs)
+    m.allocate(0, int(rng.integers(1, 900)))
+    ids = list(range(1, 9))
+    for c in ids:
+        m.fork(0, c)
+    for _ in range(200):
+        m.append_token(int(rng.choice(ids)))
+    for k in range(1, len(ids) + 1):
+        pick = [int(x) for x in rng.choice(ids, size=k, replace=False)]
+        tables, lens = m.block_tables(pick, 128, pad_page=4095)
+        assert m.shared_prefix(pick) == pa.shared_prefix_len(tables, lens, bs), pick
+    m.close()
