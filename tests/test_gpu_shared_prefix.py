@@ -190,3 +190,20 @@ def test_few_sequences(nseq):
         out = _run(pa, w, t, S, P)
         torch.cuda.synchronize()
         check_close(out_f64(out), ref, "bf16", f"shared {nseq} seqs P={P}")
+
+
+def test_largest_batch():
+    """1,024 sequences, the most one call takes: 4,096 (sequence, head)
+    columns in 128 groups over the shared prefix; sampled sequences, the
+    first and last column groups included."""
+    pa = require_gpu()
+    w, t = _shared_batch("shared_max", 47, 32, 8, 128, 16, shared_tokens=96, nseq=1024)
+    say("shared prefix, 1,024 sequences", w.summary())
+    seqs = [0, 1, 2, 7, 8, 511, 512, 1015, 1016, 1023]
+    ref = step_and_reference(pa, w, t, seqs)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16)
+    assert S == 96
+    for P in (64, 256):
+        out = _run(pa, w, t, S, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out)[seqs], ref, "bf16", f"shared 1024 seqs P={P}")
