@@ -20,6 +20,6 @@ invariants, worked examples the pages print).  No function is unpinned.
 from .formats import bf16_bits_to_f64, f32_to_bf16_bits, to_f64  # noqa: F401
 from .paged_attention import decode, gather_sequence, resolve_slot  # noqa: F401
 from .cache_ops import copy_blocks, kv_append  # noqa: F401
-from .streaming import online_decode_sequence, split_decode_sequence  # noqa: F401
+from .streaming import online_decode_sequence, segmented_decode_sequence, split_decode_sequence  # noqa: F401
 from .prefix_cache import PrefixCachingPool  # noqa: F401
 from .multi_query import decode_multi  # noqa: F401

@@ -62,3 +62,31 @@ def split_decode_sequence(qb, K, V, scale: float, group: int, partition: int, ch
         den = sum(wi * p[1] for wi, p in zip(w, parts))
         out[h] = num / den
     return out
+
+
+def segmented_decode_sequence(qb, K, V, scale: float, group: int, cuts, chunk: int):
+    """Attention over consecutive segments [cuts[i], cuts[i + 1]) of one
+    sequence's context, each reduced to (m, l, acc) on its own and merged as
+    the partitions are.  The cuts need not be equally spaced: a prefix shared
+    by several sequences can end inside a partition, and the partition is
+    then read as two segments.  An empty segment leaves m = -inf, l = 0 and
+    weighs nothing in the merge."""
+    hq, d = qb.shape
+    out = np.zeros((hq, d), dtype=np.float64)
+    if K.shape[0] == 0:
+        return out
+    cuts = list(cuts)
+    for h in range(hq):
+        g = h // group
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if b > a:
+                parts.append(_online(qb[h], K[a:b, g, :], V[a:b, g, :], scale, chunk))
+            else:
+                parts.append((-np.inf, 0.0, np.zeros(d, dtype=np.float64)))
+        M = max(p[0] for p in parts)
+        w = [np.exp(p[0] - M) if p[0] > -np.inf else 0.0 for p in parts]
+        num = sum(wi * p[2] for wi, p in zip(w, parts))
+        den = sum(wi * p[1] for wi, p in zip(w, parts))
+        out[h] = num / den
+    return out
