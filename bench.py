@@ -531,7 +531,7 @@ def main(argv=None) -> int:
     prefix = a.step == "prefix"
     if prefix:
         reuse = "shared"
-        P = ps_req if ps_req and ps_req > 0 else 2048
+        P = ps_req if ps_req and ps_req > 0 else 2048      # the library's default for this call
         # host bookkeeping, as a block manager would know it: the leading
         # block-table entries every sequence shares, in whole pages
         shared_len = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)

@@ -351,7 +351,7 @@ def shared_prefix_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: in
 
 def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                         max_context_len: int, shared_len: int, partition_size: int,
+                         max_context_len: int, shared_len: int, partition_size: int = 0,
                          out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, k_new=None, v_new=None,
                          slot_mapping=None) -> torch.Tensor:

@@ -287,7 +287,7 @@ def _shared(L, **kw):
     (dict(dtype=0), pa.PA_ERR_UNSUPPORTED),           # matrix-core kernels: bf16 only
     (dict(dtype=5), pa.PA_ERR_ARG),
     (dict(B=1025), pa.PA_ERR_UNSUPPORTED),            # prefix launch rows
-    (dict(part=0), pa.PA_ERR_ARG),                    # an explicit partition is required
+    (dict(part=-32), pa.PA_ERR_ARG),
     (dict(part=48), pa.PA_ERR_ARG),
     (dict(S=100), pa.PA_ERR_ARG),                     # not whole pages
     (dict(S=-64), pa.PA_ERR_ARG),
@@ -324,3 +324,7 @@ def test_shared_prefix_workspace_size():
     assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 33, 0, 48) == 0                  # not a multiple of 32
     assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 33, 40, 32) == 0                 # past max_context_len
     assert pa.shared_prefix_workspace_size(-1, 4, 4, 64, 33, 0, 32) == 0
+    # partition 0 is the library default, 2048: 5 prefix slots, then the
+    # per-sequence partitions 4 and 5 -> 7 slots per row
+    assert pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 0) == \
+        pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 2048) == 100 * 32 * 7 * 130 * 4

@@ -127,7 +127,7 @@ def test_named_workload_full_size(name):
     S = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)
     say("  shared_len", S)
     assert S >= 9984
-    for P in (1024, 2048):
+    for P in (1024, 2048, 0):                        # 0: the library default
         out = _run(pa, w, t, S, P)
         torch.cuda.synchronize()
         stats = check_close(out_f64(out)[seqs], ref, "bf16", f"shared {name} P={P}")
