@@ -346,6 +346,55 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
  * holding the prefix launch's partials and then the per-sequence ones.
  * Returns 0 for invalid arguments.
  */
+/*
+ * pa_decode_shared_prefix_groups -- the same for a batch of several groups
+ * of sequences, each group sharing its own prefix (several prompts forked
+ * at once, multi-tenant batches).  [Internals, "Copy-on-Write and Prefix
+ * Sharing"]
+ *
+ *   num_groups        >= 0
+ *   group_start       device, [num_groups + 1] int32: group g is sequences
+ *                     group_start[g] .. group_start[g + 1] - 1 (consecutive,
+ *                     ascending); sequences in no group share nothing
+ *   group_shared_len  device, [num_groups] int32: tokens group g's sequences
+ *                     hold in the same pages, whole pages (their table rows
+ *                     agree on the first group_shared_len[g] / block_size
+ *                     entries; read through the group's first row)
+ *   seq_shared_len    device, [num_seqs] int32: each sequence's group's
+ *                     shared length (0 for a sequence in no group)
+ *   max_group_size    host bound on group sizes, 1 .. 1024
+ *   max_shared_len    host bound on group_shared_len, <= max_context_len
+ *   partition_size    a multiple of 32 (0: 2048)
+ *   workspace         >= pa_decode_shared_prefix_groups_workspace_size()
+ * Each group's shared pages are read once per kv head and column group for
+ * all its sequences' queries; the rest of every context per sequence; the
+ * merge as in the split path.  Other arguments, preconditions and returns
+ * as for pa_decode_shared_prefix (context_lens[b] >= seq_shared_len[b], an
+ * appended position past it); inconsistent group arrays give unspecified
+ * output with memory accesses in bounds.
+ */
+pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t block_size, int32_t num_kv_heads, float scale,
+                                         void* out, hipStream_t stream,
+                                         int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int64_t num_blocks, pa_dtype dtype, int32_t num_groups,
+                                         const int32_t* group_start, const int32_t* group_shared_len,
+                                         const int32_t* seq_shared_len, int32_t max_group_size,
+                                         int32_t max_shared_len, int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, const void* k_new, const void* v_new,
+                                         const int64_t* slot_mapping);
+
+/*
+ * Workspace bytes for pa_decode_shared_prefix_groups: the split path's
+ * layout with one slot more per (sequence, head) row,
+ * num_seqs * num_heads * (ceil(max_context_len / P) + 1) * (head_dim + 2) * 4
+ * (P = partition_size, 0 meaning 2048).  0 for invalid arguments.
+ */
+size_t pa_decode_shared_prefix_groups_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                                     int32_t max_context_len, int32_t partition_size);
+
 size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                               int32_t head_dim, int32_t max_context_len, int32_t shared_len,
                                               int32_t partition_size);

@@ -10,7 +10,8 @@ from ._binding import (  # noqa: F401
     KERNELS, LIB_PATH, REUSE, PA_BF16, PA_ERR_ARG, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_UNSUPPORTED,
     PA_ERR_WORKSPACE, PA_F32, PA_OK, PaError, copy_blocks, decode, decode_append, decode_partition,
     decode_multi, decode_multi_partition_size, decode_multi_workspace_size,
-    decode_partition_size, decode_reduce, decode_shared_prefix, decode_workspace_size, kv_append, lib,
+    decode_partition_size, decode_reduce, decode_shared_prefix, decode_shared_prefix_groups,
+    decode_workspace_size, kv_append, lib,
     shared_prefix_len, shared_prefix_workspace_size,
     make_workspace, probe_stream_read, status_string,
 )

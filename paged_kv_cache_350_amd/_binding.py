@@ -59,6 +59,11 @@ _SIGNATURES = {
                                  _vp, _c_size, _vp, _vp, _vp], _c_int),
     "pa_decode_shared_prefix_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                                                _c_size),
+    "pa_decode_shared_prefix_groups": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
+                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int,
+                                        _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp, _vp],
+                                       _c_int),
+    "pa_decode_shared_prefix_groups_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
     "pa_decode_reduce": ([_vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int],
                          _c_int),
     "pa_copy_blocks": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _vp], _c_int),
@@ -379,6 +384,42 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                        block_tables.shape[1], int(max_context_len), nb, _elem_dtype(q),
                                        int(shared_len), int(partition_size), ws_ptr, ws_bytes, kn, vn, sm)
     _check("pa_decode_shared_prefix", st)
+    return out
+
+
+def decode_shared_prefix_groups(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                max_context_len: int, group_start: torch.Tensor, group_shared_len: torch.Tensor,
+                                seq_shared_len: torch.Tensor, max_group_size: int, max_shared_len: int,
+                                partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None, k_new=None, v_new=None,
+                                slot_mapping=None) -> torch.Tensor:
+    """Decode a batch of groups of sequences, each group sharing its own
+    prefix pages (see pa_decode_shared_prefix_groups); the group arrays are
+    int32 device tensors."""
+    nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len)
+    G = int(group_shared_len.shape[0])
+    _dev_tensor("group_start", group_start, dtype=torch.int32, ndim=1)
+    _dev_tensor("group_shared_len", group_shared_len, dtype=torch.int32, ndim=1)
+    _dev_tensor("seq_shared_len", seq_shared_len, dtype=torch.int32, ndim=1)
+    if group_start.shape[0] != G + 1 or seq_shared_len.shape[0] != B:
+        raise ValueError("group_start must have num_groups + 1 entries, seq_shared_len num_seqs")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dtype=q.dtype, ndim=3)
+    if workspace is None:
+        n = lib().pa_decode_shared_prefix_groups_workspace_size(B, hq, d, int(max_context_len),
+                                                                int(partition_size))
+        workspace = torch.empty(max(n, 16) // 4, dtype=torch.float32, device=q.device)
+    kn, vn, sm = _append_args(k_new, v_new, slot_mapping, B, hkv, d, q.dtype)
+    st = lib().pa_decode_shared_prefix_groups(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+        bs, hkv, float(scale), out.data_ptr(), _stream(q), B, hq, d, block_tables.shape[1],
+        int(max_context_len), nb, _elem_dtype(q), G, group_start.data_ptr(), group_shared_len.data_ptr(),
+        seq_shared_len.data_ptr(), int(max_group_size), int(max_shared_len), int(partition_size),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), kn, vn, sm)
+    _check("pa_decode_shared_prefix_groups", st)
     return out
 
 

@@ -133,9 +133,11 @@ void decode_mfma_kernel(DecodeParams p) {
         return;
     }
     // positions below first_token are read by a shared-prefix launch
+    const int first = p.seq_first ? p.seq_first[b] : p.first_token;
+    const int shift = p.seq_first ? (first % p.partition != 0 ? 1 : 0) : p.slot_shift;
     const int pstart = part * p.partition;
-    if (pstart + p.partition <= p.first_token) return;
-    const int start = max(pstart, p.first_token);
+    if (pstart + p.partition <= first) return;
+    const int start = max(pstart, first);
     const int end = min(pstart + p.partition, L);
 
     // Q^T as the B operand: lane (hl, j) holds head hl, dims 32 s + 8 j .. + 8.
@@ -373,7 +375,7 @@ void decode_mfma_kernel(DecodeParams p) {
             }
         }
         if (p.split) {
-            const size_t rr = (head0 + h) * wsp + part + p.slot_shift;
+            const size_t rr = (head0 + h) * wsp + part + shift;
             p.ws[rr * D + d] = num;
             if (d == 0) {
                 p.ws[rows * D + rr] = M;

@@ -136,7 +136,9 @@ void decode_multi_kernel(DecodeParams p) {
     constexpr uint32_t kStepBytes = 4u * BS * 16;
     constexpr uint32_t kTileStep = 16u * BS * 2;
 
-    const int* row = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+    // a group of sequences sharing a prefix reads it through its first
+    // member's table row
+    const int* row = p.block_tables + (size_t)(p.table_rows_from_queries ? qr.row0 : b) * p.max_blocks_per_seq;
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache);
     const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.v_cache);
     const size_t tile_elems = (size_t)D * BS;

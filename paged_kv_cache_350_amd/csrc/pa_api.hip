@@ -266,6 +266,8 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.uniform_len = 0;
     p.ws_parts = 0;
     p.slot_shift = 0;
+    p.seq_first = nullptr;
+    p.table_rows_from_queries = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -293,6 +295,7 @@ pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out
     r.num_groups = 0;
     r.max_query_len = 0;
     r.slot_shift = plan.p.slot_shift;
+    r.seq_first = plan.p.seq_first;
     r.ws = plan.p.ws;
     r.context_lens = context_lens;
     r.out = out;
@@ -536,6 +539,7 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
     plan.p.max_parts = parts_for(max_context_len, partition);
     plan.p.ws_parts = 0;
     plan.p.slot_shift = 0;
+    plan.p.seq_first = nullptr;
     return launch_reduce(plan, context_lens, out, stream);
 }
 
@@ -628,6 +632,109 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     plan.p.first_token = shared_len;
     plan.p.ws_parts = sh.row;
     plan.p.slot_shift = sh.shift;
+    plan.p.k_new = k_new;
+    plan.p.v_new = v_new;
+    plan.p.append_mask = k_new ? slot_mapping : nullptr;
+    st = launch_plan(plan, stream);
+    if (st != PA_OK) return st;
+    return launch_reduce(plan, context_lens, out, stream);
+}
+
+size_t pa_decode_shared_prefix_groups_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                                     int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+    if (partition_size == 0) partition_size = kSharedPrefixPartition;
+    if (partition_size < kChunk || partition_size % kChunk != 0) return 0;
+    // the split path's row plus one slot: a group whose shared length ends
+    // inside a partition reads that partition in two parts
+    return pa_impl::ws_rows(num_seqs, num_heads, parts_for(max_context_len, partition_size) + 1) *
+           (size_t)(head_dim + 2) * sizeof(float);
+}
+
+pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t block_size, int32_t num_kv_heads, float scale,
+                                         void* out, hipStream_t stream,
+                                         int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int64_t num_blocks, pa_dtype dtype, int32_t num_groups,
+                                         const int32_t* group_start, const int32_t* group_shared_len,
+                                         const int32_t* seq_shared_len, int32_t max_group_size,
+                                         int32_t max_shared_len, int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, const void* k_new, const void* v_new,
+                                         const int64_t* slot_mapping) {
+    if (!valid_dtype(dtype)) return PA_ERR_ARG;
+    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (partition_size == 0) partition_size = kSharedPrefixPartition;
+    if (partition_size < 0) return PA_ERR_ARG;
+    if (num_groups < 0 || max_group_size < 1 || max_shared_len < 0) return PA_ERR_ARG;
+    if (max_group_size > kMaxQueryLen) return PA_ERR_UNSUPPORTED;   // query rows of one group
+    Plan plan;
+    pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                             scale, out, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                             max_context_len, num_blocks, dtype, partition_size, PA_KERNEL_MFMA,
+                             PA_KV_SHARED, workspace, workspace_bytes,
+                             /*need_out=*/true, /*force_split=*/true, &plan);
+    if (st != PA_OK) return st;
+    if (max_shared_len > max_context_len) return PA_ERR_ARG;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
+    if (num_seqs == 0) return PA_OK;
+    if (!seq_shared_len || (num_groups > 0 && (!group_start || !group_shared_len))) return PA_ERR_NULL;
+    const size_t need = pa_decode_shared_prefix_groups_workspace_size(num_seqs, num_heads, head_dim,
+                                                                      max_context_len, plan.partition);
+    if (!workspace) return PA_ERR_WORKSPACE;
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    const int32_t P = plan.partition;
+    const int32_t row = parts_for(max_context_len, P) + 1;
+
+    // Each group's shared positions: one multi-query launch whose virtual
+    // sequence g has query rows group_start[g] .. group_start[g + 1] - 1 (the
+    // group's decode queries, each seeing all group_shared_len[g]
+    // positions), reads the pages through its first member's table row and
+    // writes the partials of partitions 0 .. ceil(group_shared_len[g] / P) - 1
+    // to those slots of its members' rows.
+    if (num_groups > 0 && max_shared_len > 0) {
+        DecodeParams m{};
+        m.q = q;
+        m.k_cache = k_cache;
+        m.v_cache = v_cache;
+        m.block_tables = block_tables;
+        m.context_lens = group_shared_len;    // a group's context is its shared prefix
+        m.out = out;
+        m.ws = plan.p.ws;
+        m.scale_log2 = plan.p.scale_log2;
+        m.num_seqs = num_groups;
+        m.num_heads = num_heads;
+        m.num_kv_heads = num_kv_heads;
+        m.group = plan.p.group;
+        m.head_dim = head_dim;
+        m.block_size = block_size;
+        m.max_blocks_per_seq = max_blocks_per_seq;
+        m.max_context_len = max_shared_len;
+        m.num_blocks = num_blocks;
+        m.partition = P;
+        m.max_parts = parts_for(max_shared_len, P);
+        m.ws_parts = row;
+        m.split = 1;
+        m.waves = 4;
+        m.query_start = group_start;
+        m.num_tokens = num_seqs;
+        m.max_query_len = max_group_size;
+        m.stream_kv = 0;                      // ordinary loads: the pages are shared
+        m.all_visible = 1;
+        m.table_rows_from_queries = 1;
+        const int32_t tiles = multi_col_tiles(m.group, max_group_size);
+        m.col_groups = multi_col_groups(m.group, max_group_size);
+        if ((uint64_t)num_groups * num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid)
+            return PA_ERR_UNSUPPORTED;
+        st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
+        if (st != PA_OK) return st;
+    }
+    // The rest of every context from its own shared length on, partitions
+    // shifted past its prefix slots, then the merge.
+    plan.p.seq_first = seq_shared_len;
+    plan.p.ws_parts = row;
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
@@ -761,6 +868,7 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
     r.num_groups = num_seqs;
     r.max_query_len = max_query_len;
     r.slot_shift = 0;
+    r.seq_first = nullptr;
     return hip_status(pa_impl::launch_decode_reduce(r, dtype, stream));
 }
 

@@ -50,6 +50,11 @@ struct DecodeParams {
     int32_t uniform_len;   // > 0: every sequence's context length (context_lens is not read)
     int32_t ws_parts;      // > 0: partial slots per workspace row (else max_parts)
     int32_t slot_shift;    // split: partition p writes workspace slot p + slot_shift
+    // shared-prefix groups: sequence b's own first position (its group's
+    // shared length; replaces first_token, and its slot shift is 1 when it
+    // ends inside a partition), or null
+    const int32_t* seq_first;
+    int32_t table_rows_from_queries;  // multi-query: sequence b reads the table row of its first query row
 };
 
 struct ReduceParams {
@@ -70,6 +75,7 @@ struct ReduceParams {
     // a row merges slots 0 .. ceil(L / partition) + slot_shift - 1 (a
     // shared prefix's partials come first, read in partitions of their own)
     int32_t slot_shift;
+    const int32_t* seq_first;   // or per sequence: 1 when its shared length ends inside a partition
 };
 
 // Workspace layout for the split path (all fp32):

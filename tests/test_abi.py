@@ -328,3 +328,40 @@ def test_shared_prefix_workspace_size():
     # per-sequence partitions 4 and 5 -> 7 slots per row
     assert pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 0) == \
         pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 2048) == 100 * 32 * 7 * 130 * 4
+
+
+def _groups(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, bs=16, hkv=8, scale=0.1, out=FAKE,
+             stream=None, B=4, hq=32, d=128, maxb=16, maxctx=256, nb=100, dtype=1, G=2, gs=FAKE, gl=FAKE,
+             sl=FAKE, maxg=3, maxs=128, part=64, ws=FAKE, wsb=1 << 30, kn=None, vn=None, sm=None)
+    a.update(kw)
+    return L.pa_decode_shared_prefix_groups(
+        a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bs"], a["hkv"], a["scale"], a["out"], a["stream"], a["B"],
+        a["hq"], a["d"], a["maxb"], a["maxctx"], a["nb"], a["dtype"], a["G"], a["gs"], a["gl"], a["sl"],
+        a["maxg"], a["maxs"], a["part"], a["ws"], a["wsb"], a["kn"], a["vn"], a["sm"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), pa.PA_ERR_UNSUPPORTED),
+    (dict(G=-1), pa.PA_ERR_ARG),
+    (dict(maxg=0), pa.PA_ERR_ARG),
+    (dict(maxg=1025), pa.PA_ERR_UNSUPPORTED),
+    (dict(maxs=-1), pa.PA_ERR_ARG),
+    (dict(maxs=512), pa.PA_ERR_ARG),                  # beyond max_context_len
+    (dict(part=48), pa.PA_ERR_ARG),
+    (dict(sl=None), pa.PA_ERR_NULL),
+    (dict(gs=None), pa.PA_ERR_NULL),
+    (dict(gl=None), pa.PA_ERR_NULL),
+    (dict(kn=FAKE), pa.PA_ERR_NULL),
+    (dict(ws=None, wsb=0), pa.PA_ERR_WORKSPACE),
+    (dict(wsb=4 * 32 * 4 * 130 * 4), pa.PA_ERR_WORKSPACE),   # the split path's size: a slot short
+    (dict(B=0), pa.PA_OK),
+])
+def test_decode_shared_prefix_groups_validates(L, kw, status):
+    assert _groups(L, **kw) == status
+
+
+def test_shared_prefix_groups_workspace_size(L):
+    assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 256, 64) == 4 * 32 * 5 * 130 * 4
+    assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 10512, 0) == 4 * 32 * 7 * 130 * 4
+    assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 256, 48) == 0

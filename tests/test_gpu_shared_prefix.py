@@ -207,3 +207,74 @@ def test_largest_batch():
         out = _run(pa, w, t, S, P)
         torch.cuda.synchronize()
         check_close(out_f64(out)[seqs], ref, "bf16", f"shared 1024 seqs P={P}")
+
+
+def _grouped_batch(seed, hq, hkv, d, bs, groups, loner_len=300):
+    """Sequences in groups [(size, shared_tokens)], then one sequence in no
+    group; each group's rows point their leading entries at its first row's
+    pages."""
+    rng = np.random.default_rng(seed)
+    lens, shared = [], []
+    for size, S in groups:
+        for _ in range(size):
+            lens.append(S + 2 + int(rng.integers(0, 300)))
+            shared.append(S)
+    lens.append(loner_len)
+    shared.append(0)
+    w = W.custom("groups", seed, "bf16", lens, hq, hkv, d, bs)
+    t = W.make_tensors(w, "cuda")
+    tables = w.block_tables.copy()
+    start, starts = 0, [0]
+    for size, S in groups:
+        tables[start:start + size, :S // bs] = tables[start, :S // bs]
+        start += size
+        starts.append(start)
+    w.block_tables = tables
+    t["block_tables"].copy_(torch.from_numpy(tables))
+    arrays = dict(group_start=torch.tensor(starts, dtype=torch.int32, device="cuda"),
+                  group_shared_len=torch.tensor([S for _, S in groups], dtype=torch.int32, device="cuda"),
+                  seq_shared_len=torch.tensor(shared, dtype=torch.int32, device="cuda"),
+                  max_group_size=max(size for size, _ in groups), max_shared_len=max(S for _, S in groups))
+    return w, t, arrays
+
+
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32)], ids=lambda s: "-".join(map(str, s)))
+def test_prefix_groups_match_oracle(shape):
+    """Groups of 10, 5, 1 and 14 sequences sharing 320, 96, 640 and 480
+    tokens (ending on and inside partitions), and one sequence in no group."""
+    pa = require_gpu()
+    hq, hkv, d, bs = shape
+    w, t, arr = _grouped_batch(48, hq, hkv, d, bs, [(10, 320), (5, 96), (1, 640), (14, 480)])
+    say("prefix groups", shape, w.summary())
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    for P in (64, 256, 0):
+        out = pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                             t["context_lens"], w.scale, w.max_context_len, partition_size=P, **arr)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"groups {shape} P={P}")
+
+
+def test_prefix_groups_fused_append():
+    pa = require_gpu()
+    w, t, arr = _grouped_batch(49, 32, 8, 128, 16, [(6, 256), (7, 160)])
+    say("prefix groups, fused append", w.summary())
+    B = w.num_seqs
+    k_new = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=t["k_new"].dtype, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    mask = np.full(B, -1, dtype=np.int64)
+    for i, b in enumerate(w.append_seq.tolist()):
+        k_new[b] = t["k_new"][i]
+        v_new[b] = t["v_new"][i]
+        mask[b] = w.append_slots[i]
+    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
+    rk, rv = oracle.kv_append(storage_np(k_new), storage_np(v_new), mask, kc0, vc0, w.block_size)
+    ref = oracle.decode(storage_np(t["q"]), rk, rv, w.block_tables, w.context_lens, w.scale, w.block_size,
+                        "bf16")
+    kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+    out = pa.decode_shared_prefix_groups(t["q"], kc, vc, t["block_tables"], t["context_lens"], w.scale,
+                                         w.max_context_len, partition_size=96, k_new=k_new, v_new=v_new,
+                                         slot_mapping=torch.from_numpy(mask).cuda(), **arr)
+    torch.cuda.synchronize()
+    assert np.array_equal(storage_np(kc).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(storage_np(vc).view(np.uint16), rv.view(np.uint16))
+    check_close(out_f64(out), ref, "bf16", "groups fused")
