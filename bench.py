@@ -264,7 +264,7 @@ def capacity_bench(a) -> int:
     reserve = {"tiny": 64, "llama3_8b": 4096, "llama3_70b": 8192, "prefix_share": 10512,
                "beam_fork": 32774, "long_context": 32768}
     usage = {}
-    for name in W.NAMED:
+    for name in reserve:
         w = W.by_name(name)
         if name == "prefix_share":
             u = C.measure_usage(w.context_lens, w.block_size, reserve[name], prompt=10000)
@@ -535,12 +535,31 @@ def main(argv=None) -> int:
         # host bookkeeping, as a block manager would know it: the leading
         # block-table entries every sequence shares, in whole pages
         shared_len = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)
+        groups = w.extra.get("groups")
+        if groups:
+            # several prompts: each group's own shared length, per group and per sequence
+            gsl = [pa.shared_prefix_len(w.block_tables[g0:g0 + gn], w.context_lens[g0:g0 + gn], w.block_size)
+                   for g0, gn in groups]
+            seq_sl = np.zeros(w.num_seqs, dtype=np.int32)
+            for (g0, gn), S in zip(groups, gsl):
+                seq_sl[g0:g0 + gn] = S
+            garr = dict(group_start=torch.tensor([g0 for g0, _ in groups] + [sum(groups[-1])], dtype=torch.int32,
+                                                 device="cuda"),
+                        group_shared_len=torch.tensor(gsl, dtype=torch.int32, device="cuda"),
+                        seq_shared_len=torch.from_numpy(seq_sl).cuda(),
+                        max_group_size=max(gn for _, gn in groups), max_shared_len=max(gsl))
+            shared_len = gsl
     else:
         P = pa.decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, ps_req, reuse)
         shared_len = None
+        groups = None
     split = P > 0
     out = torch.empty_like(t["q"])
-    if prefix:
+    if prefix and groups:
+        nws = pa.lib().pa_decode_shared_prefix_groups_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                                     w.max_context_len, P)
+        ws = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
+    elif prefix:
         nws = pa.shared_prefix_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
                                               w.max_context_len, shared_len, P)
         ws = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
@@ -548,7 +567,7 @@ def main(argv=None) -> int:
         ws = pa.make_workspace(t["q"], w.num_kv_heads, w.max_context_len, P, reuse) if split else None
     kernel_name = "decode_mfma" if (a.kernel == "mfma" or (a.kernel == "auto" and w.dtype == "bf16")) \
         else "decode_valu"
-    main_name = "decode_shared_prefix" if prefix else kernel_name + ("_partition" if split else "_single")
+    main_name = ("decode_shared_prefix_groups" if groups else "decode_shared_prefix") if prefix else kernel_name + ("_partition" if split else "_single")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -559,7 +578,13 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[1].record(stream)
         app = dict(k_new=step_k, v_new=step_v, slot_mapping=step_slots) if fused else {}
-        if prefix:
+        if prefix and groups:
+            pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                           t["context_lens"], w.scale, w.max_context_len, partition_size=P,
+                                           out=out, workspace=ws, **garr, **app)
+            if ev is not None:
+                ev[2].record(stream)
+        elif prefix:
             # prefix launch + partition kernel + merge: one call, timed as a whole
             pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                                     w.scale, w.max_context_len, shared_len, P, out=out, workspace=ws, **app)

@@ -278,3 +278,29 @@ def test_prefix_groups_fused_append():
     assert np.array_equal(storage_np(kc).view(np.uint16), rk.view(np.uint16))
     assert np.array_equal(storage_np(vc).view(np.uint16), rv.view(np.uint16))
     check_close(out_f64(out), ref, "bf16", "groups fused")
+
+
+def test_prefix_groups_workload_full_size():
+    """Four 4,096-token prompts, each forked to 25 sequences with suffixes:
+    the grouped call with each group's shared length from its tables; sampled
+    sequences from every group against the oracle."""
+    pa = require_gpu()
+    w = W.by_name("prefix_groups")
+    say("prefix groups full", w.summary())
+    t = W.make_tensors(w, "cuda")
+    groups = w.extra["groups"]
+    seqs = sorted({a for a, _ in groups} | {a + n - 1 for a, n in groups} | {37, 61})
+    ref = step_and_reference(pa, w, t, seqs)
+    gsl = [pa.shared_prefix_len(w.block_tables[a:a + n], w.context_lens[a:a + n], w.block_size) for a, n in groups]
+    assert gsl == [4096] * 4
+    seq_sl = np.zeros(w.num_seqs, dtype=np.int32)
+    for (a, n), S in zip(groups, gsl):
+        seq_sl[a:a + n] = S
+    arr = dict(group_start=torch.tensor([a for a, _ in groups] + [w.num_seqs], dtype=torch.int32, device="cuda"),
+               group_shared_len=torch.tensor(gsl, dtype=torch.int32, device="cuda"),
+               seq_shared_len=torch.from_numpy(seq_sl).cuda(), max_group_size=25, max_shared_len=4096)
+    out = pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                         w.scale, w.max_context_len, **arr)
+    torch.cuda.synchronize()
+    stats = check_close(out_f64(out)[seqs], ref, "bf16", "prefix groups full")
+    say("  ", stats)

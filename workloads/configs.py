@@ -337,6 +337,58 @@ def prefix_share(seed: int = 3, num_seqs: int = 100, prefix: int = 10000,
     return w
 
 
+def prefix_groups(seed: int = 5, num_groups: int = 4, group_size: int = 25, prompt: int = 4096,
+                  suffix_max: int = 512, manager=None) -> Workload:
+    """Several tenants' prompts at once: ``num_groups`` prompts of ``prompt``
+    tokens, each forked to ``group_size`` sequences (consecutive ids) that
+    append their own suffixes of U{0..suffix_max} tokens.  32 q / 8 kv heads,
+    head_dim 128, block 32, bf16.  extra["groups"] lists (first sequence,
+    size) per group."""
+    rng = np.random.default_rng(seed)
+    bs = 32
+    num_seqs = num_groups * group_size
+    suffix = rng.integers(0, suffix_max, size=num_seqs, endpoint=True)
+    lens = prompt + suffix
+    need = num_groups * -(-prompt // bs)
+    for L in lens:
+        need += -(-int(L) // bs) - (prompt // bs)
+    num_blocks = int(math.ceil(1.1 * need))
+    perm = rng.permutation(num_blocks)
+    mgr = _manager(manager, num_blocks, bs, perm)
+    prompt_tables, groups = [], []
+    for gi in range(num_groups):
+        pid = PROMPT_SEQ - gi
+        mgr.allocate(pid, prompt)
+        prompt_tables.append(list(mgr.tables[pid]))
+        for b in range(gi * group_size, (gi + 1) * group_size):
+            mgr.fork(pid, b)
+        mgr.free_sequence(pid)
+        groups.append((gi * group_size, group_size))
+    resident = _resident_mask(num_blocks, bs, prompt_tables, [prompt] * num_groups)
+    slots, owner = [], []
+    for b in range(num_seqs):
+        for _ in range(int(suffix[b])):
+            slots.append(mgr.append_token(b))
+            owner.append(b)
+    copies = mgr.take_copies()
+    pad_page = int(mgr.free[-1])
+    tables = _tables_from(mgr, list(range(num_seqs)), pad_page)
+    w = Workload(
+        name="prefix_groups" if (num_groups, group_size, prompt, suffix_max) == (4, 25, 4096, 512) else
+        f"prefix_groups_g{num_groups}x{group_size}_p{prompt}_s{suffix_max}",
+        seed=seed, dtype="bf16", num_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=bs, num_blocks=num_blocks, context_lens=lens.astype(np.int32),
+        block_tables=tables, pad_page=pad_page, resident=resident,
+        copy_pairs=np.asarray(copies, dtype=np.int64).reshape(-1, 2),
+        append_slots=np.asarray(slots, dtype=np.int64),
+        append_seq=np.asarray(owner, dtype=np.int32),
+        description=f"{num_groups} prompts of {prompt} tokens x {group_size} sequences each + U{{0..{suffix_max}}} "
+                    f"suffix, 32/8 heads, D 128, bs 32, bf16")
+    w.extra["shared_pages"] = [p for t in prompt_tables for p in t]
+    w.extra["groups"] = groups
+    return w
+
+
 def beam_fork(seed: int = 3, beams: int = 8, prompt: int = 32768, shared_gen: int = 5,
               manager=None) -> Workload:
     """Beam search over one long prompt: the prompt plus ``shared_gen``
@@ -467,6 +519,7 @@ NAMED = {
     "prefix_share": prefix_share,
     "beam_fork": beam_fork,
     "long_context": long_context,
+    "prefix_groups": prefix_groups,
 }
 
 
