@@ -471,8 +471,8 @@ def main(argv=None) -> int:
     a = _args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not "
-                                   "part of this build (see the design notes on sharding)",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the library has no multi-GPU "
+                                   "path (how it would shard is described in the design notes)",
                           "n_gpus": a.gpus}), flush=True)
         return 2
 

@@ -511,7 +511,8 @@ def custom(name: str, seed: int, dtype: str, lens, num_heads: int, num_kv_heads:
                               f"bs {block_size}, {dtype}")
 
 
-# Named workloads, in the order the task lists them.
+# Named workloads: the tiny case, the 8B- and 70B-shaped layers, prefix sharing,
+# beams, long context, then several prompts at once.
 NAMED = {
     "tiny": tiny,
     "llama3_8b": llama3_8b,
