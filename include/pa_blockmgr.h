@@ -180,6 +180,22 @@ pa_status pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int32_t n, 
  */
 int64_t pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n);
 
+/*
+ * The group arrays pa_decode_shared_prefix_groups takes, for a batch in the
+ * order seq_ids[0 .. n): the batch splits into maximal runs of consecutive
+ * sequences whose first pages are one and the same page, one group each.
+ * A run of two or more gets the shared length pa_bm_shared_prefix gives for
+ * it; a single sequence, or a run sharing no whole page, gets 0 (the decode
+ * reads it per sequence).  group_start (host, n + 1 entries) receives the
+ * groups' first positions and then n, group_shared_len (host, n entries)
+ * their shared lengths and seq_shared_len (host, n entries) each
+ * sequence's group's shared length.  Returns the number of groups, or -1
+ * for a NULL manager or output, n < 0, or an unknown id.  [Internals,
+ * "Copy-on-Write and Prefix Sharing"]
+ */
+int32_t pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                            int32_t* group_start, int32_t* group_shared_len, int32_t* seq_shared_len);
+
 pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks_per_seq, int32_t pad_page, int32_t* tables,
                              int32_t* context_lens);

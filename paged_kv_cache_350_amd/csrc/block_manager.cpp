@@ -526,6 +526,32 @@ int64_t pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, 
     return by_pages < by_len ? by_pages : by_len;
 }
 
+int32_t pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                            int32_t* group_start, int32_t* group_shared_len, int32_t* seq_shared_len) {
+    if (!bm || n < 0) return -1;
+    if (!group_start || (n > 0 && (!seq_ids || !group_shared_len || !seq_shared_len))) return -1;
+    std::vector<int32_t> first((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+        const auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end()) return -1;
+        first[(size_t)i] = it->second.pages.empty() ? -1 : it->second.pages[0];
+    }
+    // maximal runs of consecutive sequences that start on the same page
+    int32_t groups = 0;
+    for (int32_t a = 0; a < n;) {
+        int32_t e = a + 1;
+        while (e < n && first[(size_t)a] >= 0 && first[(size_t)e] == first[(size_t)a]) ++e;
+        const int64_t shared = e - a >= 2 ? pa_bm_shared_prefix(bm, seq_ids + a, e - a) : 0;
+        group_start[groups] = a;
+        group_shared_len[groups] = (int32_t)shared;
+        for (int32_t i = a; i < e; ++i) seq_shared_len[i] = (int32_t)shared;
+        ++groups;
+        a = e;
+    }
+    group_start[groups] = n;
+    return groups;
+}
+
 pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks_per_seq, int32_t pad_page, int32_t* tables,
                              int32_t* context_lens) {

@@ -175,3 +175,86 @@ def test_beams_driven_by_native_manager_through_the_shared_prefix_path():
         check_close(out_f64(out), ref, "bf16", f"beam step {step}")
     assert np.array_equal(storage_np(kc).view(np.uint16), hk.view(np.uint16))
     assert np.array_equal(storage_np(vc).view(np.uint16), hv.view(np.uint16))
+
+
+def test_prompt_groups_driven_by_native_manager():
+    """Two prompts (150 and 96 tokens) forked to 5 and 4 sequences, with a
+    sequence on its own between them.  Every step the manager appends a token
+    to each, its copy pairs go to pa_copy_blocks, and
+    pa_decode_shared_prefix_groups appends the rows and decodes with the group
+    arrays the manager reports (pa_bm_prefix_groups).  The oracle's pool runs
+    in lockstep; outputs against the oracle decode every step, caches bit for
+    bit at the end."""
+    pa = require_gpu()
+    bs, hq, hkv, d, nb, maxb, steps = 16, 32, 8, 128, 240, 16, 5
+    rng = np.random.default_rng(51)
+    order = rng.permutation(nb)
+    m = pa.NativeBlockManager(nb, bs, free_order=order)
+    pool = oracle.PrefixCachingPool(nb, bs, free_order=order.tolist())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(52)
+
+    def rows(n):
+        return (torch.randn(n, hkv, d, generator=g, device="cuda").to(torch.bfloat16),
+                torch.randn(n, hkv, d, generator=g, device="cuda").to(torch.bfloat16))
+
+    x = W.chunk_elems("bf16")
+    nan = float("nan")
+    kc = torch.full((nb, hkv, d // x, bs, x), nan, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((nb, hkv, d, bs), nan, dtype=torch.bfloat16, device="cuda")
+    hk, hv = storage_np(kc), storage_np(vc)
+
+    def prefill(seq, n):
+        nonlocal hk, hv
+        m.allocate(seq, 0)
+        pool.allocate(seq, 0)
+        slots, _ = m.append(np.full(n, seq, dtype=np.int64))
+        pslots = [pool.append_token(seq) for _ in range(n)]
+        assert slots.tolist() == pslots
+        k, v = rows(n)
+        pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
+        hk, hv = oracle.kv_append(storage_np(k), storage_np(v), pslots, hk, hv, bs)
+
+    prefill(100, 150)
+    prefill(200, 96)
+    for c in (1, 2, 3, 4, 5):
+        m.fork(100, c)
+        pool.fork(100, c)
+    prefill(6, 70)
+    for c in (7, 8, 9, 10):
+        m.fork(200, c)
+        pool.fork(200, c)
+    batch = np.array([1, 2, 3, 4, 5, 6, 7, 8, 9, 10], dtype=np.int64)
+    tables, lens = m.block_tables(batch, maxb, pad_page=nb - 1)
+    tables, lens = tables.copy(), lens.copy()
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    for step in range(steps):
+        slots, copies = m.append(batch, tables, lens)
+        before = len(pool.copies)
+        pslots = [pool.append_token(int(b)) for b in batch]
+        assert slots.tolist() == pslots
+        gs, gl, sl = m.prefix_groups(batch)
+        assert gs.tolist() == [0, 5, 6, 10] and gl.tolist() == [144, 0, 96]
+        say("groups step", step, "copies", len(copies))
+        if len(copies):
+            pa.copy_blocks(kc, vc, torch.from_numpy(np.ascontiguousarray(copies)).cuda())
+            hk, hv = oracle.copy_blocks(hk, hv, np.array(pool.copies[before:], dtype=np.int64))
+        k, v = rows(len(batch))
+        q = torch.randn(len(batch), hq, d, generator=g, device="cuda").to(torch.bfloat16)
+        out = pa.decode_shared_prefix_groups(
+            q, kc, vc, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), scale, int(lens.max()),
+            group_start=torch.from_numpy(gs).cuda(), group_shared_len=torch.from_numpy(gl).cuda(),
+            seq_shared_len=torch.from_numpy(sl).cuda(), max_group_size=int(np.diff(gs).max()),
+            max_shared_len=int(gl.max()), partition_size=64, k_new=k, v_new=v,
+            slot_mapping=torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        hk, hv = oracle.kv_append(storage_np(k), storage_np(v), pslots, hk, hv, bs)
+        ptables = np.full((len(batch), maxb), nb - 1, dtype=np.int32)
+        for i, b in enumerate(batch.tolist()):
+            ptables[i, :len(pool.pages[b])] = pool.pages[b]
+        plens = np.array([pool.length[b] for b in batch.tolist()], dtype=np.int32)
+        assert np.array_equal(ptables, tables) and np.array_equal(plens, lens)
+        ref = oracle.decode(storage_np(q), hk, hv, ptables, plens, scale, bs, "bf16")
+        check_close(out_f64(out), ref, "bf16", f"groups step {step}")
+    assert np.array_equal(storage_np(kc).view(np.uint16), hk.view(np.uint16))
+    assert np.array_equal(storage_np(vc).view(np.uint16), hv.view(np.uint16))
