@@ -3,9 +3,11 @@
  *
  * A C ABI over hand-written HIP kernels.  Every tensor argument is a plain
  * device pointer owned by the caller; sizes are plain integers.  The library
- * allocates no memory, keeps no mutable global state, never synchronises and
- * never throws: every call validates its arguments on the host, then enqueues
- * its kernels asynchronously on `stream` (NULL = the null stream) and returns.
+ * allocates no memory, never synchronises and never throws: every call
+ * validates its arguments on the host, then enqueues its kernels
+ * asynchronously on `stream` (NULL = the null stream) and returns.  Its only
+ * global state is pa_decode_noalloc's static scratch array and the cached
+ * per-device address of it.
  *
  * Pages cited (title, then section):
  *   [Glossary]  "What is PagedAttention? Definition & Virtual Memory
@@ -67,8 +69,12 @@ typedef enum pa_status {
     PA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
     PA_ERR_OUT_OF_PAGES = -6, /* block manager: the page pool is exhausted */
     PA_ERR_NOT_FOUND = -7,   /* block manager: no sequence with that id */
-    PA_ERR_HOST_MEMORY = -8  /* block manager: host allocation failed */
+    PA_ERR_HOST_MEMORY = -8, /* block manager: host allocation failed */
+    PA_ERR_SCRATCH = -9      /* pa_decode_noalloc: request exceeds the static scratch */
 } pa_status;
+
+/* Bytes of device scratch pa_decode_noalloc holds per GPU (32 MiB). */
+#define PA_STATIC_SCRATCH_BYTES (32u * 1024u * 1024u)
 
 typedef enum pa_dtype {
     PA_F32 = 0,
@@ -175,6 +181,35 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
                     pa_kernel kernel, pa_kv_reuse reuse, void* workspace,
                     size_t workspace_bytes);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes pa_decode's arguments without the workspace;
+ * when the split path runs, the partials go to a device array of
+ * PA_STATIC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends.  The call itself allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine); its first call on
+ * a device looks up that device's copy of the array once.
+ *
+ * Result, partition choice and status codes are those of pa_decode with a
+ * workspace of pa_decode_workspace_size() bytes, bit for bit, plus
+ * PA_ERR_SCRATCH (nothing launched) when that size exceeds
+ * PA_STATIC_SCRATCH_BYTES; a single pass needs no scratch at all.  No
+ * scratch content needs clearing between calls: a call writes every
+ * partial it later reads.
+ *
+ * Calls that overlap on one GPU race: they share that GPU's array, so a
+ * caller serialises them (one stream, or events between streams).
+ */
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t block_size, int32_t num_kv_heads, float scale,
+                            void* out, hipStream_t stream,
+                            int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                            pa_kernel kernel, pa_kv_reuse reuse);
 
 /*
  * pa_decode_append -- the usual decode step in one pass: every sequence

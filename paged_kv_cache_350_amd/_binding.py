@@ -19,6 +19,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4, -5
+PA_ERR_SCRATCH = -9
+STATIC_SCRATCH_BYTES = 32 * 1024 * 1024      # PA_STATIC_SCRATCH_BYTES in include/pa.h
 PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 REUSE = {"auto": 0, "stream": 1, "shared": 2}
@@ -48,6 +50,9 @@ _SIGNATURES = {
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                    _c_int, _vp, _c_size], _c_int),
+    "pa_decode_noalloc": ([_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
+                           _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                           _c_int], _c_int),
     "pa_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _vp, _vp,
                           _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                           _c_int, _vp, _c_size], _c_int),
@@ -238,6 +243,27 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          int(max_context_len), nb, _elem_dtype(q), int(partition_size),
                          KERNELS[kernel], REUSE[reuse], ws_ptr, ws_bytes)
     _check("pa_decode", st)
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                   max_context_len: int, out: torch.Tensor, partition_size: int = 0,
+                   kernel: str = "auto", reuse: str = "auto") -> torch.Tensor:
+    """pa_decode without a workspace argument: the split path's partials go to
+    the library's static per-GPU scratch (pa_decode_noalloc).  ``out`` must be
+    given, so the call allocates nothing; calls on one GPU must not overlap."""
+    nb, hkv, d, bs, B, hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len)
+    _dev_tensor("out", out, dtype=q.dtype, ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    st = lib().pa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 block_tables.data_ptr(), context_lens.data_ptr(), bs, hkv, float(scale),
+                                 out.data_ptr(), _stream(q), B, hq, d, block_tables.shape[1],
+                                 int(max_context_len), nb, _elem_dtype(q), int(partition_size),
+                                 KERNELS[kernel], REUSE[reuse])
+    _check("pa_decode_noalloc", st)
     return out
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pa_internal.h"
 
 using pa_impl::DecodeParams;
@@ -184,7 +186,7 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
                     int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
                     pa_dtype dtype, int32_t partition_size, pa_kernel kernel, pa_kv_reuse reuse,
                     void* workspace, size_t workspace_bytes, bool need_out, bool force_split,
-                    Plan* plan) {
+                    Plan* plan, bool check_workspace = true) {
     if (!valid_dtype(dtype)) return PA_ERR_ARG;
     if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
         return PA_ERR_ARG;
@@ -218,7 +220,7 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     const int32_t parts = partition > 0 ? parts_for(max_context_len, partition) : 1;
     if ((uint64_t)num_seqs * (uint64_t)num_kv_heads * (uint64_t)parts >= kMaxGrid)
         return PA_ERR_UNSUPPORTED;
-    if (partition > 0) {
+    if (partition > 0 && check_workspace) {
         const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, partition);
         if (need > 0) {
             if (!workspace) return PA_ERR_WORKSPACE;
@@ -363,11 +365,13 @@ const char* pa_status_string(pa_status status) {
         case PA_ERR_OUT_OF_PAGES: return "out of physical pages: the page pool is exhausted";
         case PA_ERR_NOT_FOUND: return "no sequence with that id";
         case PA_ERR_HOST_MEMORY: return "host memory allocation failed";
+        case PA_ERR_SCRATCH: return "the split path needs more than the library's static scratch "
+                                    "(PA_STATIC_SCRATCH_BYTES); pass a workspace to pa_decode instead";
     }
     return "unknown status";
 }
 
-int32_t pa_version(void) { return 330; }
+int32_t pa_version(void) { return 331; }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size, pa_kv_reuse reuse) {
@@ -439,6 +443,88 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                              partition_size, kernel, reuse, workspace, workspace_bytes,
                              /*need_out=*/true, /*force_split=*/false, &plan);
     if (st != PA_OK || num_seqs == 0) return st;
+    st = launch_plan(plan, stream);
+    if (st != PA_OK || plan.partition == 0) return st;
+    return launch_reduce(plan, context_lens, out, stream);
+}
+
+}  // extern "C"
+
+// ---- pa_decode_noalloc: the split path's partials in a static device array
+//
+// One array per GPU, in device memory the code object brings with it, so a
+// call makes no allocation.  In host code `scratch` names a host-side shadow,
+// not device memory: only the address hipGetSymbolAddress returns for the
+// device that runs the call may reach a kernel.  That address is looked up
+// once per device, with the device current, and kept.
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the device `stream` belongs to (the
+// current device for the null stream); the lookup runs with that device
+// current and restores the caller's current device afterwards.
+pa_status scratch_on_stream_device(hipStream_t stream, void** ptr) {
+    int dev = -1;
+    if (stream != nullptr) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(stream, &sd) != hipSuccess) return PA_ERR_HIP;
+        dev = (int)sd;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return PA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return PA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return PA_ERR_HIP;
+        void* found = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&found, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return PA_ERR_HIP;
+        if (e != hipSuccess || found == nullptr) return PA_ERR_HIP;
+        g_scratch_ptr[dev] = found;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t block_size, int32_t num_kv_heads, float scale,
+                            void* out, hipStream_t stream,
+                            int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                            pa_kernel kernel, pa_kv_reuse reuse) {
+    Plan plan;
+    pa_status st = make_plan(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                             num_kv_heads, scale, out, num_seqs, num_heads, head_dim,
+                             max_blocks_per_seq, max_context_len, num_blocks, dtype,
+                             partition_size, kernel, reuse, nullptr, 0,
+                             /*need_out=*/true, /*force_split=*/false, &plan,
+                             /*check_workspace=*/false);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (plan.partition > 0) {
+        const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, plan.partition);
+        if (need > (size_t)PA_STATIC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+        void* ws = nullptr;
+        st = scratch_on_stream_device(stream, &ws);
+        if (st != PA_OK) return st;
+        plan.p.ws = static_cast<float*>(ws);
+    }
     st = launch_plan(plan, stream);
     if (st != PA_OK || plan.partition == 0) return st;
     return launch_reduce(plan, context_lens, out, stream);

@@ -51,7 +51,7 @@ def test_status_strings(L):
         assert pa.status_string(code)
     assert pa.status_string(0) == "ok"
     assert pa.status_string(-99) == "unknown status"
-    assert L.pa_version() == 330
+    assert L.pa_version() == 331
 
 
 def test_partition_policy_and_workspace_size(L):
