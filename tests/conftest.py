@@ -21,3 +21,12 @@ def _name_gpu_case(request):
     if request.node.get_closest_marker("gpu") is not None:
         print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
     yield
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the parity lines the GPU tests recorded (worst rows against the oracle)."""
+    util = sys.modules.get("gpu_util")
+    if util is not None and getattr(util, "REPORT", None):
+        terminalreporter.write_sep("-", "parity against the float64 oracle")
+        for line in util.REPORT:
+            terminalreporter.write_line(line)

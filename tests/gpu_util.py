@@ -10,10 +10,17 @@ import torch
 import oracle
 
 # Attention-output tolerances: fp32 caches max-abs 1e-5; bf16 caches max-abs
-# 2e-2 and relative L2 (over all compared outputs) 5e-3.
+# 2e-2 and relative L2 (over all compared outputs) 5e-3.  The relative-L2
+# bound is also applied to every (sequence, head) row on its own, so an error
+# confined to one row can no longer hide under the norm of the whole batch.
+# Measured at full size: the one bf16 rounding of the output gives a relative
+# L2 of about 1.7e-3 (vector-ALU kernel, worst row 2.2e-3); the matrix-core
+# kernel rounds the softmax weights to bf16 for P.V as well, 2.2e-3 (worst
+# row 3.5e-3).
 F32_MAX_ABS = 1e-5
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
+BF16_ROW_REL_L2 = 5e-3
 
 
 def require_gpu():
@@ -27,6 +34,18 @@ def require_gpu():
 def say(*msg):
     print("[gpu-case]", *msg, flush=True)
     sys.stdout.flush()
+
+
+# Parity lines printed in pytest's terminal summary (see conftest.py), so the
+# worst rows of the full-size comparisons show even in a quiet run.
+REPORT = []
+
+
+def report(what: str, stats: dict):
+    line = f"{what}: " + ", ".join(f"{k} {v:.3g}" if isinstance(v, float) else f"{k} {v}"
+                                   for k, v in stats.items())
+    REPORT.append(line)
+    say(line)
 
 
 def storage_np(t: torch.Tensor) -> np.ndarray:
@@ -51,6 +70,23 @@ def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
     return bool(torch.equal(a.view(iv), b.view(iv)))
 
 
+def row_stats(got: np.ndarray, ref: np.ndarray) -> dict:
+    """Worst (sequence, head) row of an attention output [rows, heads, D]:
+    its relative L2 error and its max-abs error over max|ref|, each with the
+    (row, head) where it occurs.  A row whose reference is all zeros (an
+    empty context) counts its error against 1."""
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    heads = got.shape[1] if got.ndim == 3 else 1
+    ref_norm = np.linalg.norm(r, axis=1)
+    ref_max = np.abs(r).max(axis=1)
+    rel = np.linalg.norm(g - r, axis=1) / np.where(ref_norm > 0, ref_norm, 1.0)
+    mx = np.abs(g - r).max(axis=1) / np.where(ref_max > 0, ref_max, 1.0)
+    i, k = int(rel.argmax()), int(mx.argmax())
+    return {"worst_row_rel_l2": float(rel[i]), "worst_row_rel_l2_at": list(divmod(i, heads)),
+            "worst_row_maxabs_over_maxref": float(mx[k]), "worst_row_maxabs_at": list(divmod(k, heads))}
+
+
 def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", f32_max_abs: float = F32_MAX_ABS):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
@@ -61,7 +97,13 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", f3
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
     assert err.max() <= BF16_MAX_ABS, f"{what}: max-abs {err.max():.3g} > {BF16_MAX_ABS}"
     assert rel <= BF16_REL_L2, f"{what}: rel-L2 {rel:.3g} > {BF16_REL_L2}"
-    return {"max_abs": float(err.max()), "rel_l2": rel}
+    stats = {"max_abs": float(err.max()), "rel_l2": rel}
+    if got.ndim >= 2:
+        rows = row_stats(got, ref)
+        assert rows["worst_row_rel_l2"] <= BF16_ROW_REL_L2, \
+            f"{what}: row {rows['worst_row_rel_l2_at']} rel-L2 {rows['worst_row_rel_l2']:.3g} > {BF16_ROW_REL_L2}"
+        stats.update(rows)
+    return stats
 
 
 def sub_pool(w, t, seqs, k_cache=None, v_cache=None):

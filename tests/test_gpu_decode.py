@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import bits_equal, check_close, out_f64, require_gpu, run_step_updates, say, step_and_reference
+from gpu_util import (bits_equal, check_close, out_f64, report, require_gpu, run_step_updates, say,
+                      step_and_reference)
 
 pytestmark = pytest.mark.gpu
 
@@ -127,14 +128,14 @@ def _sample(w, n, seed):
                                   "long_context"])
 def test_named_workload_full_size(name):
     """Full-size workload in the launch configuration the benchmark times
-    (library-default partitions, the load path a caller would pick), sampled
-    sequences against the oracle; the other load path and the vector-ALU
+    (library-default partitions, the load path a caller would pick), every
+    sequence against the oracle; the other load path and the vector-ALU
     kernel as further checks."""
     pa = require_gpu()
     w = W.by_name(name)
     say("full", name, w.summary())
     t = W.make_tensors(w, "cuda")
-    seqs = _sample(w, 8, 11)
+    seqs = list(range(w.num_seqs))
     ref = step_and_reference(pa, w, t, seqs)
     nat = natural_reuse(w)
     other = "shared" if nat == "stream" else "stream"
@@ -143,7 +144,7 @@ def test_named_workload_full_size(name):
         torch.cuda.synchronize()
         got = out_f64(out)[seqs]
         stats = check_close(got, ref, w.dtype, f"{name} {kernel} {reuse}")
-        say("  ", kernel, reuse, stats)
+        report(f"pa_decode {name} {kernel} {reuse} ({len(seqs)} seqs)", stats)
         assert np.isfinite(out_f64(out)).all()
 
 

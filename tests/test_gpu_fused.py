@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import bits_equal, check_close, out_f64, reference_after_step, require_gpu, say, storage_np
+from gpu_util import bits_equal, check_close, out_f64, reference_after_step, report, require_gpu, say, storage_np
 
 pytestmark = pytest.mark.gpu
 
@@ -147,17 +147,15 @@ def test_fused_mask_and_empty_contexts():
                                   "long_context"])
 def test_fused_named_workload_full_size(name):
     """The decode step as the benchmark runs it: set-up appends every token
-    but each sequence's newest, then one pa_decode_append with the load path
-    a caller would pick; sampled sequences against the oracle, appended
-    slots checked bit for bit."""
+    but each sequence's newest, then one pa_decode_append with the library's
+    default partition and the load path a caller would pick; every sequence
+    of the batch against the oracle (whole batch and each (sequence, head)
+    row on its own), appended slots checked bit for bit."""
     pa = require_gpu()
     w = W.by_name(name)
     say("fused full", name, w.summary())
     t = W.make_tensors(w, "cuda")
-    rng = np.random.default_rng(19)
-    order = np.argsort(w.context_lens)
-    seqs = sorted({int(order[0]), int(order[-1])} |
-                  set(int(s) for s in rng.choice(w.num_seqs, size=min(6, w.num_seqs), replace=False)))
+    seqs = list(range(w.num_seqs))
     ref = reference_after_step(w, t, seqs)         # every row of the step appended, by the oracle
     if len(w.copy_pairs):
         pa.copy_blocks(t["k_cache"], t["v_cache"], t["copy_pairs"])
@@ -172,14 +170,14 @@ def test_fused_named_workload_full_size(name):
     # every appended slot holds its row, bit for bit
     bs, x = w.block_size, w.x
     kc, vc = t["k_cache"], t["v_cache"]
-    for b in np.flatnonzero(mask >= 0)[:16]:
+    for b in np.flatnonzero(mask >= 0):
         page, off = divmod(int(mask[b]), bs)
         got_k = kc[page, :, :, off, :].reshape(w.num_kv_heads, w.head_dim)
         got_v = vc[page, :, :, off]
         assert bits_equal(got_k.contiguous(), k_new[b].contiguous())
         assert bits_equal(got_v.contiguous(), v_new[b].contiguous())
     stats = check_close(out_f64(out)[seqs], ref, w.dtype, f"fused {name}")
-    say("  ", stats)
+    report(f"bench step {name} ({len(seqs)} of {w.num_seqs} seqs, pa_decode_append, {reuse})", stats)
 
 
 def test_fused_append_skips_a_page_outside_the_pool():
