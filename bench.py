@@ -14,10 +14,15 @@ kv heads, head_dim 128, block 16, bf16, context lengths uniform in
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 Prints one JSON line.  `value` is KV bytes read per step (every context
-token's K and V row once per kv head) divided by the wall time per step.
-`roofline` measures the dominant kernel alone with HIP events on the stream
-the library launches on.  `cpu_baseline` times the float64 oracle on the
-host, on a bounded sample of the same batch.
+token's K and V row once per kv head; for workloads whose sequences share
+pages, every distinct page slot once -- the bytes a step must bring from HBM)
+divided by the wall time per step.  `roofline` times the dominant kernel
+alone: 200 back-to-back launches between one pair of HIP events on the
+stream the library launches on.  `step_timing` gives the median, p10 and p90
+of single steps, warm (back to back) and cold (L2 and the Infinity Cache
+evicted before each step).  `cpu_baseline` times the float64 oracle on the
+host cores (one worker process per core), on a bounded sample of the same
+batch.
 """
 
 from __future__ import annotations
@@ -59,7 +64,8 @@ def _args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--mode", default="decode", choices=["decode", "copy_probe", "copy_calib",
-                                                         "blockmgr", "capacity", "prefix", "multi"],
+                                                         "blockmgr", "capacity", "prefix", "multi",
+                                                         "append_bulk", "read_calib"],
                     help="copy_probe: time pa_copy_blocks on an eager fork of a 32,768-token "
                          "prompt to 7 beams (7,168 pages of 32 tokens, K and V); copy_calib: "
                          "the same number of page copies with 7,168 distinct sources (a plain "
@@ -70,18 +76,24 @@ def _args(argv=None):
                          "contiguous pre-allocation, measured with the native allocator (no GPU); "
                          "prefix: prefix caching on a multi-tenant request stream, native manager "
                          "vs the oracle (no GPU); multi: multi-query attention on the "
-                         "speculative-verification batch (5 queries per sequence)")
+                         "speculative-verification batch (5 queries per sequence); append_bulk: "
+                         "pa_kv_append at prefill sizes; read_calib: streaming reads of a known "
+                         "size with and without the non-temporal bit (to scale traffic counters)")
     ap.add_argument("--requests", type=int, default=2000, help="prefix mode: requests in the stream")
     ap.add_argument("--oracle-requests", type=int, default=400,
                     help="prefix mode: leading requests the oracle replays (CPU baseline sample)")
     return ap.parse_args(argv)
 
 
-def _src_digest(*names):
+def _src_digest():
+    """Digest of every HIP source and header of the library (a counter summary
+    taken on other sources no longer describes the kernels that run)."""
+    csrc = os.path.join(ROOT, "paged_kv_cache_350_amd", "csrc")
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_350_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(n.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -106,47 +118,93 @@ def _host(t):
     return t.numpy()
 
 
-def cpu_baseline(w, t, target_s):
-    """Oracle (float64, host) over whole sequences of the batch until about
-    `target_s` seconds of CPU work; BLAS limited to one thread."""
-    import oracle
+# ---- CPU baseline: the float64 oracle, process-parallel over the host cores
+#
+# Workers are spawned interpreters (fresh processes that never touch the
+# GPU); the cache pages the batch reads are handed over once in shared host
+# memory, and every task is one whole sequence.
+
+_CPU = {}
+
+
+def _cpu_worker_init(shm_name, kshape, vshape, kdtype, q, tables, lens, scale, bs, dtype):
+    from multiprocessing import shared_memory
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:          # pragma: no cover - threadpoolctl missing
-        limiter = None
+        threadpool_limits(limits=1)
+    except Exception:           # pragma: no cover - threadpoolctl missing
+        pass
+    shm = shared_memory.SharedMemory(name=shm_name)    # the parent owns (and unlinks) it
+    nk = int(np.prod(kshape)) * np.dtype(kdtype).itemsize
+    _CPU.update(shm=shm, q=q, tables=tables, lens=lens, scale=scale, bs=bs, dtype=dtype,
+                kc=np.ndarray(kshape, dtype=kdtype, buffer=shm.buf[:nk]),
+                vc=np.ndarray(vshape, dtype=kdtype, buffer=shm.buf[nk:]))
+
+
+def _cpu_worker_run(b):
+    import oracle
+    c = _CPU
+    oracle.decode(c["q"], c["kc"], c["vc"], c["tables"], c["lens"], c["scale"], c["bs"], c["dtype"], seqs=[b])
+    return b
+
+
+def cpu_baseline(w, t, target_s):
+    """Oracle (float64, host) over whole sequences of the batch, one process
+    per host core (one BLAS thread each), about `target_s` seconds of wall
+    time: the batch's sequences are queued round after round."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
     import torch
     bs = w.block_size
+    seqs = [b for b in range(w.num_seqs) if int(w.context_lens[b]) > 0]
+    pages = sorted({int(p) for b in seqs for p in w.block_tables[b, :-(-int(w.context_lens[b]) // bs)]})
+    where = np.zeros(w.num_blocks, dtype=np.int64)
+    where[pages] = np.arange(len(pages))
+    idx = torch.tensor(pages, dtype=torch.long, device=t["k_cache"].device)
+    kc = _host(t["k_cache"].index_select(0, idx))
+    vc = _host(t["v_cache"].index_select(0, idx))
+    tables = np.zeros_like(w.block_tables)
+    for b in seqs:
+        n = -(-int(w.context_lens[b]) // bs)
+        tables[b, :n] = where[w.block_tables[b, :n]]
     q = _host(t["q"])
-    kc_dev, vc_dev = t["k_cache"], t["v_cache"]
-    done, nbytes = 0, 0
-    elapsed = 0.0
-    order = list(range(w.num_seqs))
-    rounds = 0
-    while elapsed < target_s and rounds < 50:
-        for b in order:
-            L = int(w.context_lens[b])
-            n = -(-L // bs)
-            pages = w.block_tables[b, :n].astype(np.int64)
-            idx = torch.from_numpy(pages).to(kc_dev.device)
-            kc = _host(kc_dev.index_select(0, idx))
-            vc = _host(vc_dev.index_select(0, idx))
-            table = np.arange(n, dtype=np.int32)[None]
+    batch_bytes = int(sum(int(w.context_lens[b]) for b in seqs)) * w.kv_bytes_per_token()
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    if any("rocprof" in v.lower() for k, v in os.environ.items() if k in ("LD_PRELOAD", "HSA_TOOLS_LIB")):
+        # under a profiler every new process would load its tool library
+        # (and open the GPU): no worker processes then
+        return None
+    shm = shared_memory.SharedMemory(create=True, size=kc.nbytes + vc.nbytes)
+    try:
+        np.ndarray(kc.shape, dtype=kc.dtype, buffer=shm.buf[:kc.nbytes])[...] = kc
+        np.ndarray(vc.shape, dtype=vc.dtype, buffer=shm.buf[kc.nbytes:])[...] = vc
+        kshape, vshape, kdtype = kc.shape, vc.shape, kc.dtype
+        del kc, vc
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(cores, initializer=_cpu_worker_init,
+                      initargs=(shm.name, kshape, vshape, kdtype, q, tables, w.context_lens, w.scale, bs,
+                                w.dtype)) as pool:
+            # a worker that cannot start would leave map() waiting forever:
+            # every round has a deadline
+            pool.map_async(_cpu_worker_run, seqs, chunksize=1).get(timeout=120)   # warm-up (imports, page-in)
             t0 = time.perf_counter()
-            oracle.decode(q[b:b + 1], kc, vc, table, w.context_lens[b:b + 1], w.scale, bs, w.dtype)
-            elapsed += time.perf_counter() - t0
-            done += 1
-            nbytes += L * w.kv_bytes_per_token()
-            if elapsed >= target_s:
-                break
-        rounds += 1
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
+            pool.map_async(_cpu_worker_run, seqs, chunksize=1).get(timeout=120)
+            first = time.perf_counter() - t0
+            rounds = max(1, int(round(target_s / max(first, 1e-3))))
+            t0 = time.perf_counter()
+            pool.map_async(_cpu_worker_run, seqs * rounds, chunksize=1).get(timeout=10 * target_s + 120)
+            wall = time.perf_counter() - t0
+    finally:
+        shm.close()
+        shm.unlink()
+    done = rounds * len(seqs)
     return {
-        "value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s",
-        "seqs_per_s": round(done / elapsed, 3), "cores": 1, "kind": "oracle",
-        "sample": f"{done} whole sequences of the {w.name} batch ({nbytes / 1e6:.1f} MB of KV), "
-                  f"float64 numpy oracle, one BLAS thread, {elapsed:.1f} s of CPU time",
+        "value": round(rounds * batch_bytes / wall / 1e9, 4), "unit": "GB/s",
+        "seqs_per_s": round(done / wall, 3), "cores": cores, "kind": "oracle",
+        "sample": f"{rounds} round(s) of the whole {w.name} batch ({done} sequences, "
+                  f"{rounds * batch_bytes / 1e6:.1f} MB of KV), float64 numpy oracle, {cores} worker "
+                  f"processes with one BLAS thread each, {wall:.1f} s wall",
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
 
@@ -199,6 +257,70 @@ def copy_probe(a, torch, pa, W) -> int:
                       "bytes_written": moved // 2, "avg_us": round(us, 2),
                       "gbps_read_plus_write": round(moved / (us * 1e-6) / 1e9, 1),
                       "steps": a.steps}), flush=True)
+    return 0
+
+
+def append_bulk(a, torch, pa, W) -> int:
+    """pa_kv_append at prefill sizes: the 32,768-token prompt of the beam
+    workload written into 1,024 pages of 32 tokens (page order permuted), and
+    the prefix workload's suffix prefill (every suffix token but each
+    sequence's newest).  Bytes moved = rows read + the same bytes written."""
+    res = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+
+    def time_append(name, k, v, slots, kc, vc):
+        fn = lambda: pa.kv_append(k, v, slots, kc, vc)        # noqa: E731
+        for _ in range(max(a.warmup, 1)):
+            fn()
+        ms = _loop_ms(torch, torch.cuda.current_stream(), fn, max(a.steps, 20))
+        moved = 2 * (k.numel() + v.numel()) * k.element_size()
+        res[name] = {"tokens": int(k.shape[0]), "bytes_read_plus_written": moved, "avg_us": round(ms * 1e3, 2),
+                     "gbps_read_plus_write": round(moved / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    # beam prompt: 32,768 tokens, block 32, 8 kv heads, D 128, bf16
+    T, bs, hkv, d = 32768, 32, 8, 128
+    pages = T // bs
+    nb = pages + pages // 10
+    order = torch.from_numpy(np.random.default_rng(5).permutation(nb)[:pages].astype(np.int64)).cuda()
+    slots = (order.repeat_interleave(bs) * bs + torch.arange(bs, device="cuda").repeat(pages)).contiguous()
+    k = torch.randn(T, hkv, d, generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn(T, hkv, d, generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.zeros(nb, hkv, d // 8, bs, 8, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(nb, hkv, d, bs, dtype=torch.bfloat16, device="cuda")
+    time_append("beam_prompt_32768", k, v, slots, kc, vc)
+    del k, v, kc, vc
+
+    # prefix workload: the suffix prefill after the copy-on-write fork
+    w = W.prefix_share()
+    t = W.make_tensors(w, "cuda")
+    newest = {}
+    for i, b in enumerate(w.append_seq.tolist()):
+        newest[b] = i
+    older = torch.tensor([i for i in range(len(w.append_seq)) if i not in set(newest.values())],
+                         dtype=torch.long, device="cuda")
+    time_append("prefix_suffix_prefill", t["k_new"].index_select(0, older).contiguous(),
+                t["v_new"].index_select(0, older).contiguous(),
+                t["slot_mapping"].index_select(0, older).contiguous(), t["k_cache"], t["v_cache"])
+    print(json.dumps({"mode": "append_bulk", "digest": _src_digest(), "steps": max(a.steps, 20),
+                      "results": res}), flush=True)
+    return 0
+
+
+def read_calib(a, torch, pa) -> int:
+    """Streaming reads of a known size (1 GiB per dispatch), with and without
+    the non-temporal bit: what FETCH_SIZE reads for them scales the counter
+    for kernels whose loads are streaming (the decode kernels) or ordinary."""
+    nbytes = 1 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for nt in (True, False):
+        for _ in range(max(a.steps, 1)):
+            pa.probe_stream_read(x, sink, nontemporal=nt)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "read_calib", "bytes_per_dispatch": nbytes, "dispatches_each": max(a.steps, 1)}),
+          flush=True)
     return 0
 
 
@@ -389,18 +511,12 @@ def multi_bench(a, torch, pa, W) -> int:
     fused = a.step == "fused"
     app = dict(k_new=t["k_new"], v_new=t["v_new"]) if fused else {}
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         if not fused:
             pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
-        if ev is not None:
-            ev[1].record(stream)
         pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                         t["query_start"], w.scale, w.max_context_len, w.max_query_len, out=out,
                         partition_size=P if P > 0 else -1, workspace=ws, reuse=reuse, **app)
-        if ev is not None:
-            ev[2].record(stream)
 
     for _ in range(a.warmup):
         step()
@@ -412,17 +528,18 @@ def multi_bench(a, torch, pa, W) -> int:
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    nbd = min(a.steps, 100)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nbd)]
-    for k in range(nbd):
-        step(events[k])
-    torch.cuda.synchronize()
-    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    multi_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    # each launch alone, back to back, one event pair around the loop
+    nloop = max(a.steps, 200)
+    append_ms = _loop_ms(torch, stream, lambda: pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"],
+                                                            t["k_cache"], t["v_cache"]), nloop)
+    multi_ms = _loop_ms(torch, stream, lambda: pa.decode_multi(
+        t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], t["query_start"], w.scale,
+        w.max_context_len, w.max_query_len, out=out, partition_size=P if P > 0 else -1, workspace=ws,
+        reuse=reuse, **app), nloop)
     kv_bytes = w.algorithmic_kv_bytes()       # every context token once per kv head (one column group)
     ms_per_step = wall * 1e3 / a.steps
     achieved = kv_bytes / (multi_ms * 1e-3) / 1e9
-    digest = _src_digest("decode_multi.hip", "decode_reduce.hip", "pa_device.h", "pa_internal.h")
+    digest = _src_digest()
 
     # CPU baseline: the oracle on whole sequences, about cpu_seconds of work
     cpu = None
@@ -496,6 +613,10 @@ def main(argv=None) -> int:
         return copy_probe(a, torch, pa, W)
     if a.mode == "multi":
         return multi_bench(a, torch, pa, W)
+    if a.mode == "append_bulk":
+        return append_bulk(a, torch, pa, W)
+    if a.mode == "read_calib":
+        return read_calib(a, torch, pa)
     w = W.by_name(a.workload)
     ps_req = w.partition_size if a.partition_size is None else a.partition_size
     t = W.make_tensors(w, "cuda")
@@ -569,89 +690,108 @@ def main(argv=None) -> int:
         else "decode_valu"
     main_name = ("decode_shared_prefix_groups" if groups else "decode_shared_prefix") if prefix else kernel_name + ("_partition" if split else "_single")
     stream = torch.cuda.current_stream()
+    app = dict(k_new=step_k, v_new=step_v, slot_mapping=step_slots) if fused else {}
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        if not fused:
-            pa.kv_append(step_k, step_v, step_slots, t["k_cache"], t["v_cache"])
-        if ev is not None:
-            ev[1].record(stream)
-        app = dict(k_new=step_k, v_new=step_v, slot_mapping=step_slots) if fused else {}
+    def run_partition():
+        pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                            w.scale, w.max_context_len, P, ws, kernel=a.kernel, reuse=reuse, **app)
+
+    def run_reduce():
+        pa.decode_reduce(ws, t["context_lens"], out, w.max_context_len, P)
+
+    def run_append():
+        pa.kv_append(step_k, step_v, step_slots, t["k_cache"], t["v_cache"])
+
+    def run_decode():
         if prefix and groups:
             pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                            t["context_lens"], w.scale, w.max_context_len, partition_size=P,
                                            out=out, workspace=ws, **garr, **app)
-            if ev is not None:
-                ev[2].record(stream)
         elif prefix:
-            # prefix launch + partition kernel + merge: one call, timed as a whole
             pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                                     w.scale, w.max_context_len, shared_len, P, out=out, workspace=ws, **app)
-            if ev is not None:
-                ev[2].record(stream)
         elif split:
-            pa.decode_partition(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                t["context_lens"], w.scale, w.max_context_len, P, ws, kernel=a.kernel,
-                                reuse=reuse, **app)
-            if ev is not None:
-                ev[2].record(stream)
-            pa.decode_reduce(ws, t["context_lens"], out, w.max_context_len, P)
+            run_partition()
+            run_reduce()
+        elif fused:
+            pa.decode_append(step_k, step_v, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                             t["context_lens"], w.scale, w.max_context_len, slot_mapping=step_slots,
+                             out=out, partition_size=-1, kernel=a.kernel, reuse=reuse)
         else:
-            if fused:
-                pa.decode_append(step_k, step_v, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                 t["context_lens"], w.scale, w.max_context_len, slot_mapping=step_slots,
-                                 out=out, partition_size=-1, kernel=a.kernel, reuse=reuse)
-            else:
-                pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                          w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel,
-                          reuse=reuse)
-            if ev is not None:
-                ev[2].record(stream)
-        if ev is not None:
-            ev[3].record(stream)
+            pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                      w.scale, w.max_context_len, out=out, partition_size=-1, kernel=a.kernel, reuse=reuse)
+
+    def step():
+        if not fused:
+            run_append()
+        run_decode()
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: warmup done, timing {a.steps} steps", file=sys.stderr, flush=True)
 
-    # timed region: exactly `steps` steps, synchronised on both sides
+    # timed region: exactly `steps` steps, synchronised on both sides; one
+    # event pair on the library's stream around the same back-to-back steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for _ in range(a.steps):
         step()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_event_ms = e0.elapsed_time(e1) / a.steps
 
-    # per-kernel breakdown in a separate pass (events between the launches)
-    nbd = min(a.steps, 100)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nbd)]
-    torch.cuda.synchronize()
-    for k in range(nbd):
-        step(events[k])
-    torch.cuda.synchronize()
+    # The dominant kernel alone, back to back, one event pair around the loop:
+    # the partition kernel of a split step; otherwise the decode call (one
+    # kernel, or for a single pass of 12-wave workgroups over many pairs with
+    # the append, the append launch plus the decode kernel; the shared-prefix
+    # call is its three launches).
+    nloop = max(a.steps, 200)
+    main_ms = _loop_ms(torch, stream, run_partition if (split and not prefix) else run_decode, nloop)
+    reduce_ms = _loop_ms(torch, stream, run_reduce, nloop) if split and not prefix else None
+    append_ms = _loop_ms(torch, stream, run_append, nloop) if not fused else None
 
-    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    main_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    decode_ms = float(np.mean([e[1].elapsed_time(e[3]) for e in events]))
-    kv_bytes = w.algorithmic_kv_bytes()
+    # per-step distributions, warm (back to back) and cold (caches evicted
+    # by a write and a read of 1 GiB each before every step, outside the events)
+    nsamp = 200
+    warm = _step_samples(torch, stream, step, nsamp)
+    evict = _Evictor(torch, pa, 1 << 30)
+    cold = _step_samples(torch, stream, step, nsamp, before=evict)
+    del evict
+
+    shared = bool(w.extra.get("shared_pages"))
+    logical = w.algorithmic_kv_bytes()
+    unique = w.unique_kv_bytes() if shared else logical
+    kv_bytes = unique          # bytes a step must bring from HBM at least once
     ms_per_step = wall * 1e3 / a.steps
     gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
-    digest = _src_digest("decode_mfma.hip" if kernel_name == "decode_mfma" else "decode_valu.hip",
-                         "pa_device.h", "pa_internal.h")
+    digest = _src_digest()
     achieved = kv_bytes / (main_ms * 1e-3) / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": _traffic(kernel_name, w.name, digest),
+        "traffic": _traffic(main_name, w.name, digest),
         "kernel": main_name,
         "avg_launch_us": round(main_ms * 1e3, 2),
         "algorithmic_bytes_per_launch": kv_bytes,
+        "bytes_basis": "unique" if shared else "every context token once per kv head",
         "source_digest": digest,
     }
+    if shared:
+        roofline["logical_bytes_per_launch"] = logical
+        roofline["logical_gbps"] = round(logical / (main_ms * 1e-3) / 1e9, 1)
+
+    def dist(ms):
+        med = float(np.median(ms))
+        return {"median_us": round(med * 1e3, 2), "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2), "mean_us": round(float(np.mean(ms)) * 1e3, 2),
+                "gbps_median": round(kv_bytes / (med * 1e-3) / 1e9, 1),
+                "frac_median": round(kv_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
     rec = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -674,17 +814,21 @@ def main(argv=None) -> int:
             "max_context_len": w.max_context_len, "num_blocks": w.num_blocks,
             "partition_size": P, "kernel": main_name if prefix else kernel_name, "reuse": reuse,
             "seed": w.seed, "shared_len": shared_len,
-            "kv_bytes_per_step": kv_bytes, "appended_tokens_per_step": int((slots >= 0).sum()),
-            "step": a.step,
+            "kv_bytes_per_step": kv_bytes, "logical_kv_bytes_per_step": logical,
+            "appended_tokens_per_step": int((slots >= 0).sum()), "step": a.step,
         },
+        "step_event_us": round(step_event_ms * 1e3, 2),
         "kernels_avg_us": {
-            "kv_append": None if fused else round(append_ms * 1e3, 2),
+            "kv_append": round(append_ms * 1e3, 2) if append_ms is not None else None,
             main_name: round(main_ms * 1e3, 2),
-            "decode_reduce": round(reduce_ms * 1e3, 2) if split and not prefix else None,
-            "decode_total": round(decode_ms * 1e3, 2),
+            "decode_reduce": round(reduce_ms * 1e3, 2) if reduce_ms is not None else None,
         },
+        "step_timing": {"warm": dist(warm), "cold": dist(cold), "samples": nsamp,
+                        "cold_eviction": "1 GiB write + 1 GiB read before each step, outside the events"},
         "roofline": roofline,
     }
+    if shared:
+        rec["logical_kv_gbps"] = round(logical / (ms_per_step * 1e-3) / 1e9, 1)
     # achievable read bandwidth on this device: a plain streaming read of
     # 2 GiB, and of exactly the bytes one decode step reads
     rec["stream_read_reference_gbps"] = {
@@ -700,6 +844,53 @@ def main(argv=None) -> int:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _loop_ms(torch, stream, fn, n):
+    """Average ms per call of `n` back-to-back calls of `fn`, from one event
+    pair on `stream` around them."""
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _step_samples(torch, stream, fn, n, before=None):
+    """Milliseconds of each of `n` calls of `fn`, each between its own event
+    pair on `stream`; `before` (if given) runs ahead of each pair."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for s0, s1 in evs:
+        if before is not None:
+            before()
+        s0.record(stream)
+        fn()
+        s1.record(stream)
+    torch.cuda.synchronize()
+    return [s0.elapsed_time(s1) for s0, s1 in evs]
+
+
+class _Evictor:
+    """Evicts L2 and the Infinity Cache: writes one buffer of `nbytes` and
+    reads another (ordinary cached loads), so the caches end up holding
+    neither the step's pages nor dirty lines."""
+
+    def __init__(self, torch, pa, nbytes):
+        self.pa = pa
+        self.w = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.r = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.k = 0
+
+    def __call__(self):
+        self.k ^= 1
+        self.w.fill_(self.k)
+        self.pa.probe_stream_read(self.r, self.sink, nontemporal=False)
 
 
 if __name__ == "__main__":
