@@ -56,6 +56,49 @@ def test_append_bit_exact(dtype, bs, d):
 
 
 @pytest.mark.parametrize("dtype,bs,d", SHAPES)
+def test_bulk_append_bit_exact(dtype, bs, d):
+    """A prefill-sized append (the LDS-staged kernel, 1,500 tokens: 23 full
+    token groups and a ragged one): runs of consecutive slots that start and
+    end mid-page, padding, out-of-range slots and a stretch of tokens
+    scattered over pages, so both store orders run; whole caches against
+    the oracle, bit for bit."""
+    pa = require_gpu()
+    say("bulk append", dtype, bs, d)
+    nb, hkv, T = 211, 4, 1500
+    x = W.chunk_elems(dtype)
+    kc, vc = _random_cache((nb, hkv, d // x, bs, x), (nb, hkv, d, bs), dtype, 11)
+    rng = np.random.default_rng(12)
+    pages = rng.permutation(nb)
+    slots = np.full(T, -1, dtype=np.int64)
+    pos, p = 0, 0
+    for run in (5, 300, 77, 640, 129):                  # prefill runs, each from a page offset onward
+        start = int(rng.integers(0, bs))
+        taken = []
+        while len(taken) < run:
+            taken.extend(int(pages[p]) * bs + o for o in range(start, bs))
+            start, p = 0, p + 1
+        slots[pos:pos + run] = taken[:run]
+        pos += run + 3                                  # three padding tokens between runs
+    free = np.array([int(q) * bs + o for q in pages[p:] for o in range(bs)], dtype=np.int64)
+    slots[pos:] = rng.choice(free, size=T - pos, replace=False)     # scattered tail
+    slots[[10, 400, 1490]] = [nb * bs, nb * bs + 99, -5]            # out of range / padding: skipped
+    assert len(set(slots[slots >= 0].tolist())) == int((slots >= 0).sum())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    td = W.torch_dtype(dtype)
+    k = torch.randn(T, hkv, d, generator=g, device="cuda").to(td)
+    v = torch.randn(T, hkv, d, generator=g, device="cuda").to(td)
+    k_before, v_before = storage_np(kc), storage_np(vc)
+    pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    ref_slots = np.where(slots >= nb * bs, -1, slots)
+    rk, rv = oracle.kv_append(storage_np(k), storage_np(v), ref_slots, k_before, v_before, bs)
+    view = np.uint16 if dtype == "bf16" else np.uint32
+    assert np.array_equal(storage_np(kc).view(view), rk.view(view))
+    assert np.array_equal(storage_np(vc).view(view), rv.view(view))
+
+
+@pytest.mark.parametrize("dtype,bs,d", SHAPES)
 def test_copy_blocks_bit_exact(dtype, bs, d):
     pa = require_gpu()
     say("copy_blocks", dtype, bs, d)
