@@ -128,11 +128,12 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim
 // partitions of Pp tokens, whose partials take workspace slots 0 .. np - 1
 // of every row; the per-sequence launch reads from shared_len on in
 // partitions of P, partition p >= q0 = shared_len / P writing slot p + shift
-// with shift = np - q0, so each row's partials stay contiguous and the merge
-// takes slots 0 .. ceil(L / P) + shift - 1.  Pp = P: prefix partitions of
-// 1024 or 512 tokens under P = 2048 measured no faster (100 sequences over
-// 9,984 shared tokens: 94.5 and 113.8 us against 95.3; 8 beams: 39.7 and
-// 44.2 against 38.2).
+// with shift = np - q0 (negative when Pp > P), so each row's partials stay
+// contiguous and the merge takes slots 0 .. ceil(L / P) + shift - 1.  The
+// per-wave-loads multi-query launch keeps Pp = P: prefix partitions of 1024
+// or 512 tokens under P = 2048 measured no faster with it (100 sequences
+// over 9,984 shared tokens: 94.5 and 113.8 us against 95.3; 8 beams: 39.7
+// and 44.2 against 38.2); the LDS-staged launch sizes Pp for itself.
 struct PrefixShape {
     int32_t Pp;
     int32_t np;
@@ -140,7 +141,25 @@ struct PrefixShape {
     int32_t row;     // slots per workspace row
     int32_t tiles;   // 16-column tiles per prefix workgroup
     int32_t col_groups;
+    bool wide;       // the LDS-staged prefix kernel (128 columns per workgroup)
 };
+
+// Many query columns per kv head (a prompt forked to many sequences): the
+// LDS-staged prefix kernel, whose workgroups stage each chunk of shared
+// pages once for 128 columns.  Its partitions are multiples of its 64-token
+// chunk, sized so that the launch has about kPrefixWideFill workgroups (two
+// per compute unit: each holds 64 KiB of LDS).
+constexpr int32_t kPrefixWideMinCols = 64;
+constexpr int64_t kPrefixWideFill = 512;
+
+int32_t prefix_wide_partition(int64_t units_per_part, int32_t shared_len) {
+    const int32_t chunk = pa_impl::decode_prefix_chunk();
+    const int64_t parts = (kPrefixWideFill + units_per_part - 1) / units_per_part;
+    int64_t Pp = (shared_len + parts - 1) / parts;
+    Pp = (Pp + chunk - 1) / chunk * chunk;
+    if (Pp < 4 * chunk) Pp = 4 * chunk;
+    return (int32_t)Pp;
+}
 
 int32_t multi_col_tiles(int32_t group, int32_t max_query_len);
 int32_t multi_col_groups(int32_t group, int32_t max_query_len);
@@ -162,6 +181,12 @@ PrefixShape prefix_shape(int32_t num_seqs, int32_t group, int32_t num_kv_heads, 
         sh.tiles = 1;
     sh.col_groups = (int32_t)(((int64_t)group * num_seqs + 16 * sh.tiles - 1) / (16 * sh.tiles));
     sh.Pp = P;
+    sh.wide = (int64_t)group * num_seqs >= kPrefixWideMinCols;
+    if (sh.wide) {
+        const int32_t cols = pa_impl::decode_prefix_columns();
+        sh.col_groups = (int32_t)(((int64_t)group * num_seqs + cols - 1) / cols);
+        sh.Pp = prefix_wide_partition((int64_t)num_kv_heads * sh.col_groups, shared_len);
+    }
     sh.np = shared_len > 0 ? (shared_len + sh.Pp - 1) / sh.Pp : 0;
     sh.shift = sh.np - shared_len / P;
     sh.row = parts_for(max_context_len, P) + sh.shift;
@@ -660,7 +685,8 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
                              scale, out, num_seqs, num_heads, head_dim, max_blocks_per_seq,
                              max_context_len, num_blocks, dtype, partition_size, PA_KERNEL_MFMA,
                              PA_KV_SHARED, workspace, workspace_bytes,
-                             /*need_out=*/true, /*force_split=*/true, &plan);
+                             /*need_out=*/true, /*force_split=*/true, &plan,
+                             /*check_workspace=*/false);      // its own row length, checked below
     if (st != PA_OK) return st;
     if (shared_len < 0 || shared_len % block_size != 0 || shared_len > max_context_len) return PA_ERR_ARG;
     if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
@@ -670,6 +696,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     const PrefixShape sh = prefix_shape(num_seqs, plan.p.group, num_kv_heads, max_context_len, shared_len, P);
     const size_t need = pa_impl::ws_rows(num_seqs, num_heads, sh.row) * (size_t)(head_dim + 2) * sizeof(float);
     if (!workspace) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ARG;
     if (workspace_bytes < need) return PA_ERR_WORKSPACE;
 
     // Prefix positions: one multi-query launch over sequence 0's table row
@@ -707,8 +734,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.stream_kv = 0;                      // ordinary loads: the pages are shared
         m.all_visible = 1;
         m.uniform_len = shared_len;
-        if ((uint64_t)num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid) return PA_ERR_UNSUPPORTED;
-        st = hip_status(pa_impl::launch_decode_multi(m, sh.tiles, stream));
+        if ((uint64_t)num_kv_heads * m.col_groups * (m.max_parts + 8) >= kMaxGrid) return PA_ERR_UNSUPPORTED;
+        st = hip_status(sh.wide ? pa_impl::launch_decode_prefix(m, stream)
+                                : pa_impl::launch_decode_multi(m, sh.tiles, stream));
         if (st != PA_OK) return st;
     }
     // The rest of every context, sequence by sequence, from shared_len on

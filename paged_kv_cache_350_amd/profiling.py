@@ -6,6 +6,8 @@ Two summaries:
   ``rocprofv3 --kernel-trace --stats --output-format csv`` run
   (``*_kernel_stats.csv``), for the kernels whose names contain the given
   substrings.
+* ``counters`` -- the median per dispatch of every counter of one or more
+  ``--pmc`` runs for one kernel (busy cycles, cache hits, instruction counts).
 * ``traffic`` -- HBM bytes per launch of one kernel from two counter runs
   (``--pmc FETCH_SIZE``, then ``--pmc WRITE_SIZE``; both report KiB per
   dispatch), each scaled by what the same counter reads for a plain copy of
@@ -92,6 +94,42 @@ def traffic(fetch_dir: str, write_dir: str, calib_fetch_dir: str, calib_write_di
     }
 
 
+def counters(run_dirs: List[str], kernel: str) -> Dict[str, float]:
+    """Median per dispatch of every counter collected for kernels matching
+    ``kernel`` over one or more ``--pmc`` runs (one pass each)."""
+    out: Dict[str, float] = {}
+    for d in run_dirs:
+        path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+        per: Dict[str, List[float]] = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if not per:
+            raise ValueError(f"no counters for kernel {kernel!r} in {path}")
+        for name, vals in per.items():
+            out[name] = statistics.median(vals)
+    return out
+
+
+def _counters_main(a) -> int:
+    vals = counters(a.run_dir, a.kernel)
+    lines = [f"# {a.title}", "", "Commands (one counter pass each):", ""]
+    lines += ["    " + c for c in a.command]
+    lines += ["", f"Kernel: `{a.kernel}` (median over its dispatches)", "", "| counter | value |", "|---|---|"]
+    for name in sorted(vals):
+        v = vals[name]
+        lines.append(f"| {name} | {v:.6g} |")
+    if a.note:
+        lines += ["", a.note]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
 def _stats_main(a) -> int:
     rows = kernel_stats(a.run_dir, a.kernel)
     lines = [f"# {a.title}", "", "Command:", "", "    " + a.command, "",
@@ -146,8 +184,15 @@ def main(argv=None) -> int:
     t.add_argument("--source-digest", required=True)
     t.add_argument("--command", action="append", required=True)
     t.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("run_dir", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--title", default="rocprofv3 counters")
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--note", default="")
+    c.add_argument("--out")
     a = ap.parse_args(argv)
-    return _stats_main(a) if a.cmd == "stats" else _traffic_main(a)
+    return {"stats": _stats_main, "traffic": _traffic_main, "counters": _counters_main}[a.cmd](a)
 
 
 if __name__ == "__main__":

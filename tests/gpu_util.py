@@ -147,7 +147,7 @@ def run_step_updates(pa, w, t):
         pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
 
 
-def reference_after_step(w, t, seqs):
+def reference_after_step(w, t, seqs, scale=None):
     """The float64 oracle decode of ``seqs`` after the step's copy-on-write
     copies and appends, computed on the host before the device runs them.
     The pages those sequences read (plus the sources copied into them) are
@@ -176,11 +176,12 @@ def reference_after_step(w, t, seqs):
         n = -(-int(w.context_lens[b]) // bs)
         tables[i, :n] = [where[int(p)] for p in w.block_tables[b, :n]]
     q = storage_np(t["q"])[seqs]
-    return oracle.decode(q, kc, vc, tables, w.context_lens[seqs], w.scale, bs, w.dtype)
+    return oracle.decode(q, kc, vc, tables, w.context_lens[seqs], w.scale if scale is None else scale, bs, w.dtype)
 
 
-def step_and_reference(pa, w, t, seqs):
-    """reference_after_step, then the step's copies and appends on the GPU."""
-    ref = reference_after_step(w, t, seqs)
+def step_and_reference(pa, w, t, seqs, scale=None):
+    """reference_after_step (with the workload's scale, or ``scale``), then
+    the step's copies and appends on the GPU."""
+    ref = reference_after_step(w, t, seqs, scale)
     run_step_updates(pa, w, t)
     return ref

@@ -77,6 +77,25 @@ def test_shared_prefix_matches_oracle(shape):
         assert bits_equal(_run(pa, w, t, S - bs, P), again), f"repeat {shape} P={P}"
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_shared_prefix_negative_and_zero_scale(scale):
+    """The wide prefix launch folds the scale's sign into the queries and
+    scales the column max: a negative scale and a zero scale (uniform
+    weights over every position) against the oracle, shared length ending
+    inside a 64-token chunk."""
+    pa = require_gpu()
+    w, t = _shared_batch("shared_scale", 45, 32, 8, 128, 32, shared_tokens=672, nseq=20)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 32)
+    assert S == 672 and 4 * w.num_seqs >= 64
+    say("shared prefix scale", scale, w.summary())
+    ref = step_and_reference(pa, w, t, range(w.num_seqs), scale=np.float32(scale))
+    for P in (64, 256):
+        out = pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                      float(np.float32(scale)), w.max_context_len, S, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"shared scale {scale} P={P}")
+
+
 def test_zero_shared_length_is_the_split_path():
     """shared_len 0 launches no prefix work: bit-identical to pa_decode's
     split path on the matrix-core kernel with shared-page loads (only the
