@@ -60,6 +60,9 @@ def _args(argv=None):
                     help="K/V load path (auto: shared when the workload's sequences share pages)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the library default (0 default, -1 single pass)")
+    ap.add_argument("--samples", type=int, default=200,
+                    help="single steps timed warm and cold, and back-to-back launches of the dominant kernel "
+                         "(at least --steps); fewer keep a profiled run short")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
@@ -529,7 +532,7 @@ def multi_bench(a, torch, pa, W) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # each launch alone, back to back, one event pair around the loop
-    nloop = max(a.steps, 200)
+    nloop = max(a.steps, a.samples)
     append_ms = _loop_ms(torch, stream, lambda: pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"],
                                                             t["k_cache"], t["v_cache"]), nloop)
     multi_ms = _loop_ms(torch, stream, lambda: pa.decode_multi(
@@ -749,14 +752,14 @@ def main(argv=None) -> int:
     # kernel, or for a single pass of 12-wave workgroups over many pairs with
     # the append, the append launch plus the decode kernel; the shared-prefix
     # call is its three launches).
-    nloop = max(a.steps, 200)
+    nloop = max(a.steps, a.samples)
     main_ms = _loop_ms(torch, stream, run_partition if (split and not prefix) else run_decode, nloop)
     reduce_ms = _loop_ms(torch, stream, run_reduce, nloop) if split and not prefix else None
     append_ms = _loop_ms(torch, stream, run_append, nloop) if not fused else None
 
     # per-step distributions, warm (back to back) and cold (caches evicted
     # by a write and a read of 1 GiB each before every step, outside the events)
-    nsamp = 200
+    nsamp = max(a.samples, 1)
     warm = _step_samples(torch, stream, step, nsamp)
     evict = _Evictor(torch, pa, 1 << 30)
     cold = _step_samples(torch, stream, step, nsamp, before=evict)

@@ -19,7 +19,8 @@ Two summaries:
         --command "..." --out profiles/NAME.md
     python -m paged_kv_cache_350_amd.profiling traffic --fetch DIR --write DIR \\
         --calib-fetch DIR --calib-write DIR --kernel decode_mfma --calib-kernel copy_blocks \\
-        --calib-bytes N --algorithmic-bytes N --source-digest HEX --out profiles/NAME.json
+        --calib-bytes N [--calib-fetch-kernel stream_read_kernel<true> --calib-fetch-bytes N] \\
+        --algorithmic-bytes N --source-digest HEX --out profiles/NAME.json
 """
 
 from __future__ import annotations
@@ -72,22 +73,28 @@ def counter_per_dispatch(run_dir: str, kernel: str, counter: str) -> List[float]
 
 
 def traffic(fetch_dir: str, write_dir: str, calib_fetch_dir: str, calib_write_dir: str,
-            kernel: str, calib_kernel: str, calib_bytes: int) -> Dict[str, object]:
-    """HBM bytes per launch of ``kernel``, calibrated against a copy moving
-    ``calib_bytes`` bytes each way per dispatch."""
-    f_k = statistics.median(counter_per_dispatch(fetch_dir, kernel, "FETCH_SIZE"))
-    w_k = statistics.median(counter_per_dispatch(write_dir, kernel, "WRITE_SIZE"))
-    f_c = statistics.median(counter_per_dispatch(calib_fetch_dir, calib_kernel, "FETCH_SIZE"))
+            kernel: str, calib_kernel: str, calib_bytes: int, calib_fetch_kernel: str = "",
+            calib_fetch_bytes: int = 0) -> Dict[str, object]:
+    """HBM bytes per launch of ``kernel``: FETCH_SIZE scaled by what it reads
+    for a plain read of ``calib_fetch_bytes`` per dispatch (kernel
+    ``calib_fetch_kernel``; default: the copy below), WRITE_SIZE by what it
+    reads for a copy writing ``calib_bytes`` per dispatch (``calib_kernel``)."""
+    fk = calib_fetch_kernel or calib_kernel
+    fb = calib_fetch_bytes or calib_bytes
+    kernels = kernel.split("+")           # several kernels of one call: the sum of their medians
+    f_k = sum(statistics.median(counter_per_dispatch(fetch_dir, k, "FETCH_SIZE")) for k in kernels)
+    w_k = sum(statistics.median(counter_per_dispatch(write_dir, k, "WRITE_SIZE")) for k in kernels)
+    f_c = statistics.median(counter_per_dispatch(calib_fetch_dir, fk, "FETCH_SIZE"))
     w_c = statistics.median(counter_per_dispatch(calib_write_dir, calib_kernel, "WRITE_SIZE"))
-    f_scale = calib_bytes / (f_c * 1024.0)
+    f_scale = fb / (f_c * 1024.0)
     w_scale = calib_bytes / (w_c * 1024.0)
     read = f_k * 1024.0 * f_scale
     written = w_k * 1024.0 * w_scale
     return {
         "kernel": kernel,
         "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
-        "calib_kernel": calib_kernel, "calib_bytes_each_way": calib_bytes,
-        "calib_fetch_kib": f_c, "calib_write_kib": w_c,
+        "calib_fetch_kernel": fk, "calib_fetch_bytes": fb, "calib_fetch_kib": f_c,
+        "calib_write_kernel": calib_kernel, "calib_write_bytes": calib_bytes, "calib_write_kib": w_c,
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
         "hbm_read_bytes_per_launch": int(read), "hbm_write_bytes_per_launch": int(written),
         "hbm_bytes_per_launch": int(read + written),
@@ -149,7 +156,7 @@ def _stats_main(a) -> int:
 
 def _traffic_main(a) -> int:
     rec = traffic(a.fetch, a.write, a.calib_fetch, a.calib_write, a.kernel, a.calib_kernel,
-                  a.calib_bytes)
+                  a.calib_bytes, a.calib_fetch_kernel, a.calib_fetch_bytes)
     rec["algorithmic_bytes_per_launch"] = a.algorithmic_bytes
     rec["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / a.algorithmic_bytes, 4)
     rec["workload"] = a.workload
@@ -179,6 +186,8 @@ def main(argv=None) -> int:
     t.add_argument("--kernel", required=True)
     t.add_argument("--calib-kernel", required=True)
     t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--calib-fetch-kernel", default="")
+    t.add_argument("--calib-fetch-bytes", type=int, default=0)
     t.add_argument("--algorithmic-bytes", type=int, required=True)
     t.add_argument("--workload", required=True)
     t.add_argument("--source-digest", required=True)
