@@ -176,12 +176,18 @@ void decode_mfma_kernel(DecodeParams p) {
     // Fused append (pa_decode_append): the workgroup that reads position
     // L - 1 stores kv head g's new K and V rows into that slot, and the wave
     // that reads it (the one whose last chunk holds L - 1) stores them
-    // itself.  Its loads of the new row go out with its first loads; the
-    // stores follow its first chunk's K/V loads, and it waits for them only
-    // before its last chunk's loads, so no wave waits on the row's latency.
-    // The first chunk never holds the appended page unless it is also the
-    // last; then the row is stored and waited for before any K/V load.  No
-    // other workgroup reads that page: without sharing it belongs to this
+    // itself.  Its loads of the new row go out with its first loads and the
+    // stores follow its first chunk's K/V loads.
+    //  * Streaming path: the wave never waits for its stores.  It loads its
+    //    last chunk as usual -- the slot of L - 1 may still hold what was
+    //    there before -- and puts the new row into that chunk's operand
+    //    registers itself, lane to lane (ds_bpermute), before any MFMA reads
+    //    them; then it writes the row back inside whole 64-byte blocks.
+    //    (8B-shaped step 95.4 -> 94.0 us against storing the row alone and
+    //    waiting for it before the last chunk's loads.)
+    //  * Shared-page path: it waits for its stores before its last chunk's
+    //    loads (before any load when its only chunk holds L - 1).
+    // No other workgroup reads that page: without sharing it belongs to this
     // (sequence, kv head) alone, and a sequence only appends into a page it
     // owns (copy-on-write happens before).  A page id outside the pool
     // writes nothing, as pa_kv_append skips an out-of-range slot.
@@ -191,26 +197,35 @@ void decode_mfma_kernel(DecodeParams p) {
     typedef const __attribute__((address_space(4))) int* const_row_t;
     typedef const __attribute__((address_space(4))) int64_t* const_mask_t;
     const const_row_t rowc = (const_row_t)row;
-    bool append_wave = false;                                // wave-uniform
-    if (p.k_new != nullptr && end == L && w == (nchunks - 1) % kWaves) {
+    // The wave that reads L - 1 (wave-uniform).  The streaming path reads
+    // the mask, the page id and the new row only with that last chunk's
+    // loads, so nothing delays the wave before then (it runs the longest of
+    // its workgroup's waves: the last chunk makes its share the largest).
+    const bool append_cand = p.k_new != nullptr && end == L && w == (nchunks - 1) % kWaves;
+    bool append_wave = false;                                // shared-page path, decided here
+    if (!SPLIT && append_cand) {
         const bool masked_out = p.append_mask != nullptr && ((const_mask_t)p.append_mask)[b] < 0;
         append_wave = !masked_out && (uint32_t)rowc[(L - 1) / BS] < (uint64_t)p.num_blocks;
     }
-    const bool store_first = append_wave && nchunks - 1 < kWaves;       // its only chunk holds L - 1
+    const bool store_first = !SPLIT && append_wave && nchunks - 1 < kWaves;   // its only chunk holds L - 1
     // lane c < D / 8 holds K bytes 16 c .. 16 c + 15 of the new row; lane
     // l holds V dims l and l + 64 (D = 128) or l (D = 64)
     u32x4_t new_k = u32x4_t{0u, 0u, 0u, 0u};
     uint16_t new_v[D / kWave];
-    uint16_t* new_kdst = nullptr;
-    uint16_t* new_vdst = nullptr;
-    if (append_wave) {
-        const int pos = L - 1;
-        const size_t tile = ((size_t)rowc[pos / BS] * kv_heads + g) * tile_elems;
+    for (int i = 0; i < D / kWave; ++i) new_v[i] = 0;
+    auto load_new_row = [&]() {
         const size_t src = ((size_t)b * kv_heads + g) * D;
         const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + src;
         const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + src;
         if (lane < D / 8) new_k = ld16(kn + 8 * lane);
         for (int i = 0; i < D / kWave; ++i) new_v[i] = vn[lane + kWave * i];
+    };
+    uint16_t* new_kdst = nullptr;
+    uint16_t* new_vdst = nullptr;
+    if (append_wave) {
+        const int pos = L - 1;
+        const size_t tile = ((size_t)rowc[pos / BS] * kv_heads + g) * tile_elems;
+        load_new_row();
         new_kdst = const_cast<uint16_t*>(kc) + tile + ((size_t)lane * BS + pos % BS) * 8;
         new_vdst = const_cast<uint16_t*>(vc) + tile + pos % BS;
     }
@@ -244,24 +259,39 @@ void decode_mfma_kernel(DecodeParams p) {
         const int valid = min(kChunk, end - cstart);
 
         // ---- pages of the chunk (wave-uniform); the next chunk's ids go in flight
-        const int pg0 = clamp_page(__builtin_amdgcn_readfirstlane(next0));
-        const int pg1 = clamp_page(__builtin_amdgcn_readfirstlane(next1));
+        const int raw0 = __builtin_amdgcn_readfirstlane(next0);
+        const int raw1 = __builtin_amdgcn_readfirstlane(next1);
+        const int pg0 = clamp_page(raw0);
+        const int pg1 = clamp_page(raw1);
         if (ci + kWaves < nchunks) chunk_pages(ci + kWaves, next0, next1);
-        // the appended row is in this (last) chunk: this wave's own stores of
-        // it complete before the chunk's loads are issued
-        if (append_wave && !store_first && ci == nchunks - 1) __builtin_amdgcn_s_waitcnt(0);
+        // shared-page path: the appended row is in this (last) chunk, and
+        // this wave's own stores of it complete before the chunk's loads
+        if (!SPLIT && append_wave && !store_first && ci == nchunks - 1) __builtin_amdgcn_s_waitcnt(0);
 
         // ---- loads: K of both row tiles, V of every 16-dim tile
         u32x4_t kraw[2][KSTEPS];
         u32x4_t vop[DC];                 // V^T operand, 8 bf16 per lane
         if constexpr (SPLIT) {
+            // the appending wave's last chunk: its mask entry (a vector load,
+            // so that no branch waits for it) and the new row go out with its
+            // K/V loads; the page id of L - 1 is the chunk's own, loaded a chunk
+            // ahead
+            const bool last_cand = append_cand && ci == nchunks - 1;        // wave-uniform
+            u32x2_t mask_v = u32x2_t{0u, 0u};
+            if (last_cand) {
+                if (p.append_mask != nullptr)
+                    mask_v = __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(p.append_mask + b, 8), 0, 0, 0);
+                load_new_row();
+            }
             __amdgpu_buffer_rsrc_t krs[2], vrs[2];
             for (int t = 0; t < 2; ++t) {
                 const int page = t ? pg1 : pg0;
                 const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
                 const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
                 // a half with no valid token gets an empty range: loads return 0
-                const bool live = t == 0 || valid > kHalf;
+                // (at block 32 the appending chunk reads its page's second
+                // half anyway: it writes the page's rows back whole, below)
+                const bool live = t == 0 || valid > kHalf || (BS == 32 && last_cand);
                 krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
                 vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
             }
@@ -274,6 +304,61 @@ void decode_mfma_kernel(DecodeParams p) {
             __builtin_amdgcn_sched_barrier(0);
             for (int dc = 0; dc < DC; ++dc)
                 vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
+            if (last_cand) {
+                // The new row into this chunk's registers.  Position L - 1 is
+                // chunk token p0: K row r0 of half t0 (lane (r0, j) holds its
+                // 16-byte column 4 s + j, held by lane 4 s + j of new_k); V
+                // slot 4 j0 + i0 of half t0 (dword 2 t0 + i0 / 2, half i0 % 2,
+                // of the lanes with j = j0; lane (r, j0) takes dim 16 dc + r,
+                // held by lane (16 dc + r) % 64, element (16 dc + r) / 64).
+                const int p0 = L - 1 - cstart;
+                const int t0 = p0 / kHalf;
+                const int r0 = p0 % kHalf;
+                const int j0 = (p0 % kHalf) / 4;
+                const int i0 = p0 % 4;
+                const int q0 = 2 * t0 + i0 / 2;
+                const uint32_t sh = 16u * (uint32_t)(i0 % 2);
+                // the same in every lane: the sequence appends (mask entry >= 0)
+                // into a page inside the pool
+                const bool app = (int32_t)mask_v[1] >= 0 &&
+                                 (uint32_t)(t0 ? raw1 : raw0) < (uint64_t)p.num_blocks;
+                for (int s = 0; s < KSTEPS; ++s) {
+                    u32x4_t v;
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * s + j), (int)new_k[e]);
+                    for (int t = 0; t < 2; ++t)
+                        if (t == t0) kraw[t][s] = app && r == r0 ? v : kraw[t][s];
+                }
+                for (int dc = 0; dc < DC; ++dc) {
+                    const int d = 16 * dc + r;
+                    const uint32_t nv = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (d % kWave), (int)new_v[(16 * dc) / kWave]);
+                    for (int q = 0; q < 4; ++q)
+                        if (q == q0) {
+                            const uint32_t patched = (vop[dc][q] & ~(0xffffu << sh)) | ((nv & 0xffffu) << sh);
+                            vop[dc][q] = app && j == j0 ? patched : vop[dc][q];
+                        }
+                }
+                // The row goes to the cache inside whole 64-byte blocks: the
+                // four tokens of its K columns, and every dim row of its V
+                // half-page (block 16: the page's whole V tile; block 32: both
+                // halves of each 64-byte dim row), the other tokens' bytes as
+                // just loaded -- the same bits -- rather than as 2-byte pieces
+                // of 128 V dim rows.
+                const int pg_t0 = t0 ? pg1 : pg0;
+                const int toff0 = BS == 32 ? kHalf * t0 : 0;
+                uint16_t* kw = const_cast<uint16_t*>(kc) + ((size_t)pg_t0 * kv_heads + g) * tile_elems;
+                if (app && (r & ~3) == (r0 & ~3))
+                    for (int s = 0; s < KSTEPS; ++s)
+                        st16(kw + ((size_t)(4 * s + j) * BS + toff0 + r) * 8, kraw[t0][s]);
+                for (int t = 0; t < 2 && app; ++t) {
+                    if (BS == 16 && t != t0) continue;           // block 16: the other half is another page
+                    const int toff = BS == 32 ? kHalf * t : 0;
+                    uint16_t* vw = const_cast<uint16_t*>(vc) + ((size_t)(BS == 32 ? pg0 : pg_t0) * kv_heads + g) * tile_elems;
+                    for (int dc = 0; dc < DC; ++dc)
+                        *reinterpret_cast<u32x2_t*>(vw + (size_t)(16 * dc + r) * BS + toff + 4 * j) =
+                            u32x2_t{vop[dc][2 * t], vop[dc][2 * t + 1]};
+                }
+            }
         } else {
             const int kpage = (BS == 16 && tk >= kHalf) ? pg1 : pg0;
             const uint16_t* kb = kc + ((size_t)kpage * kv_heads + g) * tile_elems +
@@ -286,8 +371,9 @@ void decode_mfma_kernel(DecodeParams p) {
             for (int dc = 0; dc < DC; ++dc) vop[dc] = ld16(vb + (size_t)dc * 16 * BS);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the appending wave stores the new row behind its first chunk's loads
-        if (append_wave && !store_first && ci == w) store_new_row();
+        // shared-page path: the appending wave stores the new row behind its
+        // first chunk's loads
+        if (!SPLIT && append_wave && !store_first && ci == w) store_new_row();
 
         // ---- S = K . Q^T
         f32x4_t st[2];

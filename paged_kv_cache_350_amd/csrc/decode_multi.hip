@@ -33,8 +33,6 @@ namespace pa_impl {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr int kChunk = 32;            // tokens per MFMA step (k of the P.V product)
 constexpr int kHalf = 16;             // tokens per row tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
@@ -60,9 +58,11 @@ __device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off
 // t is the 16-token half t of the chunk).
 __device__ __forceinline__ int slot_token(int t, int i, int j) { return kHalf * t + 4 * j + i; }
 
-template <int D, int BS, int NT, int POLICY>
-__global__ __launch_bounds__(kThreads)
+template <int D, int BS, int NT, int POLICY, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave)
 void decode_multi_kernel(DecodeParams p) {
+    constexpr int kWaves = WAVES;
+    constexpr int kThreads = kWaves * kWave;
     constexpr int KSTEPS = D / 32;   // Q.K^T k-steps
     constexpr int DC = D / 16;       // 16-dim output tiles of P.V
     constexpr int COLS = 16 * NT;    // (query token, head) columns per workgroup
@@ -396,30 +396,39 @@ void decode_multi_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int BS, int NT, int POLICY>
+template <int D, int BS, int NT, int POLICY, int WAVES>
 hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
-    const size_t smem = sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * 16 * D);
+    const size_t smem = sizeof(float) * (2 * WAVES * 16 + (size_t)WAVES * 16 * D);
     const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * p.col_groups * p.max_parts;
-    hipLaunchKernelGGL((decode_multi_kernel<D, BS, NT, POLICY>), dim3((unsigned)nwg), dim3(kThreads), smem,
+    hipLaunchKernelGGL((decode_multi_kernel<D, BS, NT, POLICY, WAVES>), dim3((unsigned)nwg), dim3(WAVES * kWave), smem,
                        stream, p);
     return hipGetLastError();
 }
 
-template <int NT, int POLICY>
+template <int NT, int POLICY, int WAVES>
 hipError_t launch_tiles(const DecodeParams& p, hipStream_t stream) {
     if (p.head_dim == 64)
-        return p.block_size == 16 ? launch_shape<64, 16, NT, POLICY>(p, stream)
-                                  : launch_shape<64, 32, NT, POLICY>(p, stream);
-    return p.block_size == 16 ? launch_shape<128, 16, NT, POLICY>(p, stream)
-                              : launch_shape<128, 32, NT, POLICY>(p, stream);
+        return p.block_size == 16 ? launch_shape<64, 16, NT, POLICY, WAVES>(p, stream)
+                                  : launch_shape<64, 32, NT, POLICY, WAVES>(p, stream);
+    return p.block_size == 16 ? launch_shape<128, 16, NT, POLICY, WAVES>(p, stream)
+                              : launch_shape<128, 32, NT, POLICY, WAVES>(p, stream);
 }
 
 }  // namespace
 
+// Streaming loads come in two workgroup sizes (p.waves): 4 waves, or 8 (one
+// workgroup fills a compute unit at this kernel's two waves per SIMD) for a
+// single pass whose workgroups take the sequences longest first.  Shared-page
+// loads always use 4.
 hipError_t launch_decode_multi(const DecodeParams& p, int col_tiles, hipStream_t stream) {
-    if (p.stream_kv)
-        return col_tiles == 1 ? launch_tiles<1, kPolicyStream>(p, stream) : launch_tiles<2, kPolicyStream>(p, stream);
-    return col_tiles == 1 ? launch_tiles<1, kPolicyReuse>(p, stream) : launch_tiles<2, kPolicyReuse>(p, stream);
+    if (p.stream_kv) {
+        if (p.waves == 8)
+            return col_tiles == 1 ? launch_tiles<1, kPolicyStream, 8>(p, stream)
+                                  : launch_tiles<2, kPolicyStream, 8>(p, stream);
+        return col_tiles == 1 ? launch_tiles<1, kPolicyStream, 4>(p, stream)
+                              : launch_tiles<2, kPolicyStream, 4>(p, stream);
+    }
+    return col_tiles == 1 ? launch_tiles<1, kPolicyReuse, 4>(p, stream) : launch_tiles<2, kPolicyReuse, 4>(p, stream);
 }
 
 }  // namespace pa_impl
