@@ -971,6 +971,12 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
         p.max_parts = 1;
         p.split = 0;
     }
+    // 4-wave workgroups.  8 (one per compute unit at this kernel's two waves
+    // per SIMD) measured faster without the fused append (speculative
+    // verification, 64 sequences x 5 queries: 104.6 against 108.2 us) and
+    // slower with it (116.9 against 114.9); pa_decode_multi_append must stay
+    // bit-identical to pa_kv_append + pa_decode_multi, so both keep 4.
+    p.waves = 4;
     st = hip_status(pa_impl::launch_decode_multi(p, tiles, stream));
     if (st != PA_OK || partition == 0) return st;
 

@@ -175,6 +175,29 @@ def test_fused_append_equals_append_then_multi(shape):
         check_close(out_f64(out_b), ref, "bf16", f"fused {shape} P={P}")
 
 
+def test_fused_append_many_new_rows():
+    """More new rows per workgroup than one wave's LDS slice holds (17 to
+    32: the workgroup copies them to LDS before its loop) and more than that
+    (stored first): bit-identical to pa_kv_append + pa_decode_multi and
+    within tolerance of the oracle."""
+    pa = require_gpu()
+    w = W.multi_custom("many_new", 50, [20, 45, 300, 700, 33], [20, 33, 17, 40, 32], 32, 8, 128, 16)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    for P in (-1, 64):
+        a = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        b = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("fused multi append, many new rows, partition", P)
+        out_a = run_gpu(pa, w, a, partition_size=P)
+        out_b = pa.decode_multi(b["q"], b["k_cache"], b["v_cache"], b["block_tables"], b["context_lens"],
+                                b["query_start"], w.scale, w.max_context_len, w.max_query_len, partition_size=P,
+                                k_new=b["k_new"], v_new=b["v_new"])
+        torch.cuda.synchronize()
+        assert bits_equal(out_a, out_b), P
+        assert bits_equal(a["k_cache"], b["k_cache"]) and bits_equal(a["v_cache"], b["v_cache"]), P
+        check_close(out_f64(out_b), ref, "bf16", f"many new rows P={P}")
+
+
 def test_fused_append_skips_pages_outside_the_pool():
     """A block-table entry outside the pool at a new token's position: that
     row is not written anywhere (as pa_kv_append skips an out-of-range slot);
