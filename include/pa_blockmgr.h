@@ -182,19 +182,25 @@ int64_t pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, 
 
 /*
  * The group arrays pa_decode_shared_prefix_groups takes, for a batch in the
- * order seq_ids[0 .. n): the batch splits into maximal runs of consecutive
- * sequences whose first pages are one and the same page, one group each.
- * A run of two or more gets the shared length pa_bm_shared_prefix gives for
- * it; a single sequence, or a run sharing no whole page, gets 0 (the decode
- * reads it per sequence).  group_start (host, n + 1 entries) receives the
- * groups' first positions and then n, group_shared_len (host, n entries)
- * their shared lengths and seq_shared_len (host, n entries) each
- * sequence's group's shared length.  Returns the number of groups, or -1
- * for a NULL manager or output, n < 0, or an unknown id.  [Internals,
- * "Copy-on-Write and Prefix Sharing"]
+ * order seq_ids[0 .. n): each maximal run of two or more consecutive
+ * sequences whose first pages are one and the same page, and that share at
+ * least one whole page, is a group with the shared length
+ * pa_bm_shared_prefix gives for it; the sequences between two such runs
+ * (single sequences, runs sharing no whole page) form one group each of
+ * shared length 0, read per sequence by the decode.  group_start (host,
+ * n + 1 entries) receives the groups' first positions and then n,
+ * group_shared_len (host, n entries) their shared lengths and
+ * seq_shared_len (host, n entries) each sequence's group's shared length.
+ * max_group_size and max_shared_len (host, may be NULL) receive the bounds
+ * the decode call takes: the largest size of a group with a shared length
+ * (1 when there is none; shared-nothing groups need no bound) and the
+ * largest shared length.  Returns the number of groups, or -1 for a NULL
+ * manager or output, n < 0, or an unknown id.  [Internals, "Copy-on-Write
+ * and Prefix Sharing"]
  */
 int32_t pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
-                            int32_t* group_start, int32_t* group_shared_len, int32_t* seq_shared_len);
+                            int32_t* group_start, int32_t* group_shared_len, int32_t* seq_shared_len,
+                            int32_t* max_group_size, int32_t* max_shared_len);
 
 pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks_per_seq, int32_t pad_page, int32_t* tables,

@@ -35,7 +35,7 @@ _SIGNATURES = {
     "pa_bm_append": ([_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp], _i32),
     "pa_bm_block_tables": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
     "pa_bm_shared_prefix": ([_vp, _vp, _i32], _i64),
-    "pa_bm_prefix_groups": ([_vp, _vp, _i32, _vp, _vp, _vp], _i32),
+    "pa_bm_prefix_groups": ([_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
 }
 
 PA_ERR_OUT_OF_PAGES, PA_ERR_NOT_FOUND, PA_ERR_HOST_MEMORY = -6, -7, -8
@@ -245,19 +245,22 @@ class NativeBlockManager:
             raise KeyError("unknown sequence id")
         return n
 
-    def prefix_groups(self, seqs: Sequence[int]) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-        """(group_start [G + 1], group_shared_len [G], seq_shared_len [n]),
-        int32 host arrays for pa_decode_shared_prefix_groups on a batch of
-        these sequences in this order."""
+    def prefix_groups(self, seqs: Sequence[int]) -> Tuple[np.ndarray, np.ndarray, np.ndarray, int, int]:
+        """(group_start [G + 1], group_shared_len [G], seq_shared_len [n],
+        max_group_size, max_shared_len): int32 host arrays and the two host
+        bounds for pa_decode_shared_prefix_groups on a batch of these
+        sequences in this order."""
         ids = np.ascontiguousarray(np.asarray(list(seqs), dtype=np.int64))
         n = int(ids.shape[0])
         gs = np.zeros(n + 1, dtype=np.int32)
         gl = np.zeros(max(n, 1), dtype=np.int32)
         sl = np.zeros(max(n, 1), dtype=np.int32)
-        g = int(_lib().pa_bm_prefix_groups(self._h, _ptr(ids) if n else None, n, _ptr(gs), _ptr(gl), _ptr(sl)))
+        bounds = np.zeros(2, dtype=np.int32)
+        g = int(_lib().pa_bm_prefix_groups(self._h, _ptr(ids) if n else None, n, _ptr(gs), _ptr(gl), _ptr(sl),
+                                           _ptr(bounds[:1]), _ptr(bounds[1:])))
         if g < 0:
             raise KeyError("unknown sequence id")
-        return gs[:g + 1], gl[:g], sl[:n]
+        return gs[:g + 1], gl[:g], sl[:n], int(bounds[0]), int(bounds[1])
 
     def block_tables(self, seqs: Sequence[int], max_blocks_per_seq: int,
                      pad_page: int = 0) -> Tuple[np.ndarray, np.ndarray]:

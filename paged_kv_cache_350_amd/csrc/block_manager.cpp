@@ -26,6 +26,7 @@
 // word.  A cached page stays cached while it is held and after it returns
 // to the free list; it is evicted when the free list hands it out again, so
 // the least recently released cached page goes first.
+#include <algorithm>
 #include <stdint.h>
 
 #include <memory>
@@ -527,7 +528,8 @@ int64_t pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, 
 }
 
 int32_t pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
-                            int32_t* group_start, int32_t* group_shared_len, int32_t* seq_shared_len) {
+                            int32_t* group_start, int32_t* group_shared_len, int32_t* seq_shared_len,
+                            int32_t* max_group_size, int32_t* max_shared_len) {
     if (!bm || n < 0) return -1;
     if (!group_start || (n > 0 && (!seq_ids || !group_shared_len || !seq_shared_len))) return -1;
     std::vector<int32_t> first((size_t)n);
@@ -536,19 +538,38 @@ int32_t pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seq_ids, 
         if (it == bm->seqs.end()) return -1;
         first[(size_t)i] = it->second.pages.empty() ? -1 : it->second.pages[0];
     }
-    // maximal runs of consecutive sequences that start on the same page
-    int32_t groups = 0;
+    // maximal runs of consecutive sequences that start on the same page and
+    // share at least one whole page; everything between two such runs is one
+    // group that shares nothing (the decode reads it per sequence)
+    int32_t groups = 0, max_size = 1, max_shared = 0;
+    auto open_group = [&](int32_t a, int32_t e, int32_t shared) {
+        group_start[groups] = a;
+        group_shared_len[groups] = shared;
+        for (int32_t i = a; i < e; ++i) seq_shared_len[i] = shared;
+        ++groups;
+        if (shared > 0) {
+            max_size = std::max(max_size, e - a);
+            max_shared = std::max(max_shared, shared);
+        }
+    };
+    int32_t loose = -1;                                      // first sequence of the current sharing-nothing run
     for (int32_t a = 0; a < n;) {
         int32_t e = a + 1;
         while (e < n && first[(size_t)a] >= 0 && first[(size_t)e] == first[(size_t)a]) ++e;
         const int64_t shared = e - a >= 2 ? pa_bm_shared_prefix(bm, seq_ids + a, e - a) : 0;
-        group_start[groups] = a;
-        group_shared_len[groups] = (int32_t)shared;
-        for (int32_t i = a; i < e; ++i) seq_shared_len[i] = (int32_t)shared;
-        ++groups;
+        if (shared > 0) {
+            if (loose >= 0) open_group(loose, a, 0);
+            loose = -1;
+            open_group(a, e, (int32_t)shared);
+        } else if (loose < 0) {
+            loose = a;
+        }
         a = e;
     }
+    if (loose >= 0) open_group(loose, n, 0);
     group_start[groups] = n;
+    if (max_group_size) *max_group_size = max_size;
+    if (max_shared_len) *max_shared_len = max_shared;
     return groups;
 }
 

@@ -233,8 +233,9 @@ def test_prompt_groups_driven_by_native_manager():
         before = len(pool.copies)
         pslots = [pool.append_token(int(b)) for b in batch]
         assert slots.tolist() == pslots
-        gs, gl, sl = m.prefix_groups(batch)
+        gs, gl, sl, max_group, max_shared = m.prefix_groups(batch)
         assert gs.tolist() == [0, 5, 6, 10] and gl.tolist() == [144, 0, 96]
+        assert (max_group, max_shared) == (5, 144)
         say("groups step", step, "copies", len(copies))
         if len(copies):
             pa.copy_blocks(kc, vc, torch.from_numpy(np.ascontiguousarray(copies)).cuda())
@@ -244,8 +245,8 @@ def test_prompt_groups_driven_by_native_manager():
         out = pa.decode_shared_prefix_groups(
             q, kc, vc, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), scale, int(lens.max()),
             group_start=torch.from_numpy(gs).cuda(), group_shared_len=torch.from_numpy(gl).cuda(),
-            seq_shared_len=torch.from_numpy(sl).cuda(), max_group_size=int(np.diff(gs).max()),
-            max_shared_len=int(gl.max()), partition_size=64, k_new=k, v_new=v,
+            seq_shared_len=torch.from_numpy(sl).cuda(), max_group_size=max_group,
+            max_shared_len=max_shared, partition_size=64, k_new=k, v_new=v,
             slot_mapping=torch.from_numpy(slots).cuda())
         torch.cuda.synchronize()
         hk, hv = oracle.kv_append(storage_np(k), storage_np(v), pslots, hk, hv, bs)

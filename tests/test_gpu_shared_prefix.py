@@ -231,7 +231,9 @@ def test_largest_batch():
 def _grouped_batch(seed, hq, hkv, d, bs, groups, loner_len=300):
     """Sequences in groups [(size, shared_tokens)], then one sequence in no
     group; each group's rows point their leading entries at its first row's
-    pages."""
+    pages.  A group with 0 shared tokens shares nothing (several sequences
+    read one by one, as the block manager reports sequences between two
+    sharing runs); max_group_size bounds only the groups that share."""
     rng = np.random.default_rng(seed)
     lens, shared = [], []
     for size, S in groups:
@@ -253,18 +255,23 @@ def _grouped_batch(seed, hq, hkv, d, bs, groups, loner_len=300):
     arrays = dict(group_start=torch.tensor(starts, dtype=torch.int32, device="cuda"),
                   group_shared_len=torch.tensor([S for _, S in groups], dtype=torch.int32, device="cuda"),
                   seq_shared_len=torch.tensor(shared, dtype=torch.int32, device="cuda"),
-                  max_group_size=max(size for size, _ in groups), max_shared_len=max(S for _, S in groups))
+                  max_group_size=max([size for size, S in groups if S > 0] + [1]),
+                  max_shared_len=max(S for _, S in groups))
     return w, t, arrays
 
 
 @pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32)], ids=lambda s: "-".join(map(str, s)))
 def test_prefix_groups_match_oracle(shape):
-    """Groups of 10, 5, 1 and 14 sequences sharing 320, 96, 640 and 480
-    tokens (ending on and inside partitions), and one sequence in no group."""
+    """Groups of 10, 5, 1 and 14 sequences, three sequences sharing nothing
+    between the second and third, and one sequence in no group.  At block 16
+    the shared lengths 336 and 208 end in the middle of a 32-token chunk and
+    of a partition; at block 32, 320 and 480 end on or inside partitions."""
     pa = require_gpu()
     hq, hkv, d, bs = shape
-    w, t, arr = _grouped_batch(48, hq, hkv, d, bs, [(10, 320), (5, 96), (1, 640), (14, 480)])
-    say("prefix groups", shape, w.summary())
+    groups = ([(10, 336), (5, 96), (3, 0), (1, 640), (14, 208)] if bs == 16 else
+              [(10, 320), (5, 96), (3, 0), (1, 640), (14, 480)])
+    w, t, arr = _grouped_batch(48, hq, hkv, d, bs, groups)
+    say("prefix groups", shape, groups, w.summary())
     ref = step_and_reference(pa, w, t, range(w.num_seqs))
     for P in (64, 256, 0):
         out = pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],

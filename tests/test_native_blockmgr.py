@@ -328,7 +328,9 @@ def test_shared_prefix_agrees_with_the_tables(seed):
 
 def test_prefix_groups_of_a_batch():
     """Two forked prompts, a loner between them, then a single fork: each
-    maximal run starting on one page is a group; singletons share nothing."""
+    maximal run starting on one page and sharing a whole page is a group;
+    the sequences between two such runs share nothing, one group for the
+    lot; the bounds cover only the groups that share."""
     m = pa.NativeBlockManager(256, 16)
     m.allocate(100, 200)                     # prompt A: 12 full pages + 8 tokens
     m.allocate(200, 64)                      # prompt B: 4 full pages
@@ -337,19 +339,25 @@ def test_prefix_groups_of_a_batch():
     for c in (5, 6):
         m.fork(200, c)
     m.allocate(4, 30)                        # on its own
+    m.allocate(8, 17)                        # on its own
     m.fork(200, 7)
     for s in (1, 2, 3, 5, 6, 7):
         m.append_token(s)                    # copy-on-write of A's tail page; B's is full
     batch = [1, 2, 3, 4, 5, 6, 7]
-    gs, gl, sl = m.prefix_groups(batch)
+    gs, gl, sl, max_group, max_shared = m.prefix_groups(batch)
     assert gs.tolist() == [0, 3, 4, 7]
     assert gl.tolist() == [192, 0, 64]
     assert sl.tolist() == [192, 192, 192, 0, 64, 64, 64]
+    assert (max_group, max_shared) == (3, 192)
     for (a, e), S in zip(zip(gs[:-1], gs[1:]), gl):
         if e - a >= 2:
             assert S == m.shared_prefix(batch[a:e])
-    assert [x.tolist() for x in m.prefix_groups([4])] == [[0, 1], [0], [0]]
-    assert [x.tolist() for x in m.prefix_groups([])] == [[0], [], []]
+    # two loners together, and a lone member of a forked prompt: one group sharing nothing
+    gs, gl, sl, max_group, max_shared = m.prefix_groups([4, 8, 1, 5, 6, 7])
+    assert gs.tolist() == [0, 3, 6] and gl.tolist() == [0, 64] and sl.tolist() == [0, 0, 0, 64, 64, 64]
+    assert (max_group, max_shared) == (3, 64)
+    assert [x.tolist() if hasattr(x, "tolist") else x for x in m.prefix_groups([4])] == [[0, 1], [0], [0], 1, 0]
+    assert [x.tolist() if hasattr(x, "tolist") else x for x in m.prefix_groups([])] == [[0], [], [], 1, 0]
     with pytest.raises(KeyError):
         m.prefix_groups([1, 99])
     m.close()
