@@ -40,6 +40,15 @@
  * Supported shapes: head_dim in {64, 128}; block_size in {16, 32};
  * num_heads a multiple of num_kv_heads with num_heads / num_kv_heads <= 16.
  *
+ * Beyond the interface the library was specified with -- pa_kv_append(k, v,
+ * slot_mapping, k_cache, v_cache), pa_decode(q, k_cache, v_cache,
+ * block_tables, context_lens, block_size, num_kv_heads, scale, out, stream)
+ * and pa_copy_blocks -- every added argument comes after those: sizes, the
+ * pool size num_blocks (pa_decode and pa_copy_blocks clamp or skip ids
+ * outside it), the dtype, the partition size, the kernel family and load
+ * path (pa_decode, and num_kv_heads and reuse in pa_decode_workspace_size,
+ * on which the default partition depends) and the workspace.
+ *
  * Preconditions the library cannot check without reading device memory
  * (violating them gives unspecified output, never an out-of-bounds access):
  * table entries used by a sequence lie in [0, num_blocks); context_lens[b]
