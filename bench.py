@@ -55,7 +55,7 @@ def _args(argv=None):
                     help="fused: the append runs inside the decode kernel (pa_decode_append); "
                          "separate: pa_kv_append, then pa_decode; prefix: pa_decode_shared_prefix "
                          "(append fused) with the longest prefix the block tables share "
-                         "(whole pages; partition 2048 unless --partition-size is given)")
+                         "(whole pages; the library's default partition unless --partition-size is given)")
     ap.add_argument("--reuse", default="auto", choices=["auto", "stream", "shared"],
                     help="K/V load path (auto: shared when the workload's sequences share pages)")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -655,7 +655,7 @@ def main(argv=None) -> int:
     prefix = a.step == "prefix"
     if prefix:
         reuse = "shared"
-        P = ps_req if ps_req and ps_req > 0 else 2048      # the library's default for this call
+        P = ps_req if ps_req else 0      # 0: the library's default for this call
         # host bookkeeping, as a block manager would know it: the leading
         # block-table entries every sequence shares, in whole pages
         shared_len = pa.shared_prefix_len(w.block_tables, w.context_lens, w.block_size)

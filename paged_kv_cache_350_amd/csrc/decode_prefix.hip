@@ -136,31 +136,44 @@ void decode_prefix_kernel(DecodeParams p) {
     const size_t tile_elems = (size_t)D * BS;
     const size_t kv_heads = (size_t)p.num_kv_heads;
 
-    // ---- staging: this thread's K and V units of a chunk (page pi of the
-    // chunk is wave-uniform for every unit index k); pages past the
-    // partition's end give zeros (their table entries may be anything)
+    // ---- staging: this thread's K and V units of a chunk.  Unit k lies in
+    // page unit_page(k) of the chunk (wave-uniform) at 16-byte unit
+    // unit_rem(k) of its tile.  The chunk's page ids are scalar loads issued
+    // together (an index past the partition's end reads the last live
+    // entry), then every unit is one buffer load whose range is empty for a
+    // page past the end, so it returns zeros: no branch and no wait between
+    // the loads.
+    constexpr int KUPP = KCH * BS;            // 16-byte K units per page tile
+    constexpr int VUPP = D * BS / 8;          // 16-byte V units per page tile
+    constexpr uint32_t kTileBytes = (uint32_t)D * BS * 2;
+    auto unit_page = [&](int k, int upp) {
+        return __builtin_amdgcn_readfirstlane((kThreads * k + tid) / upp);
+    };
+    auto unit_rem = [&](int k, int upp) { return (kThreads * k + tid) % upp; };
+    auto page_rsrc = [&](const uint16_t* cache, int pg, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(cache + ((size_t)pg * kv_heads + g) * tile_elems), 0,
+            live ? (int)kTileBytes : 0, kBufferFlags);
+    };
     u32x4_t sk[KPER], sv[VPER];
     auto load_chunk = [&](int ci) {
         const int cstart = start + ci * kTok;
         const int live_pages = (min(kTok, end - cstart) + BS - 1) / BS;
+        int kpg[KPER], vpg[VPER];
         for (int k = 0; k < KPER; ++k) {
-            const int uu = tid + kThreads * k;
-            const int pi = uu / (KCH * BS);                  // uniform in k
-            const int rem = uu % (KCH * BS);
-            int pg = pi < live_pages ? rowc[cstart / BS + pi] : 0;
-            pg = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
-            const uint16_t* src = kc + ((size_t)pg * kv_heads + g) * tile_elems + (size_t)rem * 8;
-            sk[k] = pi < live_pages ? ld16(src) : u32x4_t{0u, 0u, 0u, 0u};
+            const int pg = rowc[cstart / BS + min(unit_page(k, KUPP), live_pages - 1)];
+            kpg[k] = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
         }
         for (int k = 0; k < VPER; ++k) {
-            const int uu = tid + kThreads * k;
-            const int pi = uu / (D * BS / 8);
-            const int rem = uu % (D * BS / 8);
-            int pg = pi < live_pages ? rowc[cstart / BS + pi] : 0;
-            pg = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
-            const uint16_t* src = vc + ((size_t)pg * kv_heads + g) * tile_elems + (size_t)rem * 8;
-            sv[k] = pi < live_pages ? ld16(src) : u32x4_t{0u, 0u, 0u, 0u};
+            const int pg = rowc[cstart / BS + min(unit_page(k, VUPP), live_pages - 1)];
+            vpg[k] = (uint32_t)pg >= (uint64_t)p.num_blocks ? 0 : pg;
         }
+        for (int k = 0; k < KPER; ++k)
+            sk[k] = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(kc, kpg[k], unit_page(k, KUPP) < live_pages),
+                                                          unit_rem(k, KUPP) * 16, 0, kPolicyReuse);
+        for (int k = 0; k < VPER; ++k)
+            sv[k] = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(vc, vpg[k], unit_page(k, VUPP) < live_pages),
+                                                          unit_rem(k, VUPP) * 16, 0, kPolicyReuse);
     };
     auto store_chunk = [&](int buf) {
         unsigned char* kb = lds + buf * (KBUF + VBUF);
