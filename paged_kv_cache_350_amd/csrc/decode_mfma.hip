@@ -110,14 +110,15 @@ void decode_mfma_kernel(DecodeParams p) {
     const int j = lane / 16;         // lane group
     const int r = lane % 16;         // A-operand row of this lane
 
+    const int part0 = SPLIT ? 0 : p.first_part;              // slots below it are not launched
     const WorkItem wi = decode_work_item(blockIdx.x, (uint32_t)p.num_seqs,
-                                         (uint32_t)(p.num_kv_heads * p.max_parts));
+                                         (uint32_t)(p.num_kv_heads * (p.max_parts - part0)));
     __shared__ __align__(16) int s_lens[kSortMax];
     __shared__ int s_pick;
     const int b = p.order_by_length ? seq_by_length<kThreads>(p.context_lens, p.num_seqs, wi.b, s_lens, &s_pick)
                                     : wi.b;                  // launch-uniform choice
     const int g = wi.q % p.num_kv_heads;
-    const int slot = wi.q / p.num_kv_heads;
+    const int slot = wi.q / p.num_kv_heads + part0;
     const int G = p.group;
 
     int L = p.context_lens[b];
@@ -476,7 +477,8 @@ void decode_mfma_kernel(DecodeParams p) {
 template <int D, int BS, bool SPLIT, int WAVES>
 hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
     const size_t smem = sizeof(float) * (2 * WAVES * 16 + (size_t)WAVES * p.group * D);
-    const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * p.max_parts;
+    const uint64_t nwg = (uint64_t)p.num_seqs * p.num_kv_heads * (p.max_parts - (SPLIT ? 0 : p.first_part));
+    if (nwg == 0) return hipSuccess;                          // every position lies in the prefix
     hipLaunchKernelGGL((decode_mfma_kernel<D, BS, SPLIT, WAVES>), dim3((unsigned)nwg), dim3(WAVES * kWave), smem,
                        stream, p);
     return hipGetLastError();

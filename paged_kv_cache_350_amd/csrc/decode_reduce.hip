@@ -21,8 +21,8 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
-constexpr int kUnroll = 4;
-constexpr int kPre = 8;          // partitions whose rows are loaded up front
+constexpr int kUnroll = 8;
+constexpr int kPre = 16;         // partitions whose rows are loaded up front
 
 template <int N>
 struct FloatN;

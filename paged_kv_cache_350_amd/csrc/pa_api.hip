@@ -295,6 +295,7 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.slot_shift = 0;
     p.seq_first = nullptr;
     p.table_rows_from_queries = 0;
+    p.first_part = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -752,6 +753,8 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     plan.p.first_token = shared_len;
     plan.p.ws_parts = sh.row;
     plan.p.slot_shift = sh.shift;
+    // the partitions wholly inside the prefix are not launched
+    plan.p.first_part = plan.p.stream_kv ? 0 : shared_len / P;
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;

@@ -55,6 +55,10 @@ struct DecodeParams {
     // ends inside a partition), or null
     const int32_t* seq_first;
     int32_t table_rows_from_queries;  // multi-query: sequence b reads the table row of its first query row
+    // decode_mfma, shared-page loads (partition p in slot p): partitions
+    // below this one lie below first_token for every sequence; the grid
+    // starts at it (0: every partition)
+    int32_t first_part;
 };
 
 struct ReduceParams {
