@@ -88,8 +88,9 @@ __device__ __forceinline__ int slot_token(int t, int i, int j) {
     return SPLIT ? kHalf * t + 4 * j + i : 8 * j + 4 * t + i;
 }
 
+// (6-wave workgroups are held to three waves per SIMD, so two share a compute unit)
 template <int D, int BS, bool SPLIT, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave)
+__global__ __launch_bounds__(WAVES * kWave, WAVES == kPairWaves ? 3 : 1)
 void decode_mfma_kernel(DecodeParams p) {
     constexpr int kWaves = WAVES;
     constexpr int kThreads = kWaves * kWave;
@@ -495,13 +496,15 @@ hipError_t launch_path(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// Streaming loads come in two workgroup sizes: 4 waves (three workgroups
-// share a compute unit, so one's set-up and merge overlap the others'
-// streaming) and 12 waves (one workgroup fills a compute unit, three times
-// the bytes in flight for one (sequence, kv head, partition), which drains
-// long and ragged work units faster).  Shared-page loads always use 4.
+// Streaming loads come in three workgroup sizes: 4 waves (several
+// workgroups share a compute unit, so one's set-up and merge overlap the
+// others' streaming), 12 waves (one workgroup fills a compute unit, three
+// times the bytes in flight for one (sequence, kv head, partition), which
+// drains long and ragged work units faster) and 6 waves (two per compute
+// unit, for a longest-first single pass).  Shared-page loads always use 4.
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
     if (!p.stream_kv) return launch_path<false, 4>(p, stream);
+    if (p.waves == kPairWaves) return launch_path<true, kPairWaves>(p, stream);
     return p.waves == kWideWaves ? launch_path<true, kWideWaves>(p, stream) : launch_path<true, 4>(p, stream);
 }
 
