@@ -10,13 +10,14 @@
 // contraction for the matrix cores.
 //
 // A workgroup takes one kv head, one partition of the shared positions and
-// 128 query columns; each of its four waves owns 32 of the columns (two
-// 16-column MFMA tiles) for the whole partition.  The partition's K/V rows go
-// through LDS in chunks of 64 tokens, double-buffered: all 256 threads load
-// chunk i + 1 from the pages (16-byte loads, contiguous inside each page
-// tile) while the waves compute chunk i from LDS, so each page is read from
-// memory once per 128 columns instead of once per 32 (the per-wave-loads
-// kernel) or once per sequence (the per-sequence path).
+// 128 or 256 query columns; each of its four or eight waves owns 32 of the
+// columns (two 16-column MFMA tiles) for the whole partition.  The
+// partition's K/V rows go through LDS in chunks of 64 tokens,
+// double-buffered: all the workgroup's threads load chunk i + 1 from the
+// pages (16-byte loads, contiguous inside each page tile) while the waves
+// compute chunk i from LDS, so each page is read from memory once per 128 or
+// 256 columns instead of once per 32 (the per-wave-loads kernel) or once per
+// sequence (the per-sequence path).
 //
 //   S = K.Q^T   v_mfma_f32_16x16x32_bf16, A = K rows (16 tokens), B = Q^T
 //   P.V         v_mfma_f32_16x16x32_bf16, A = V^T (16 dims), B = P^T
@@ -42,10 +43,7 @@ namespace pa_impl {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr int kTok = 64;              // tokens per LDS chunk
-constexpr int kCols = 32 * kWaves;    // query columns per workgroup
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256 between rescales
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -54,9 +52,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-template <int D, int BS>
-__global__ __launch_bounds__(kThreads, 2)      // two waves per SIMD: two workgroups per compute unit
+// WAVES = 4 (two workgroups per compute unit) or 8 (one); either way two
+// waves per SIMD
+template <int D, int BS, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave, 2)
 void decode_prefix_kernel(DecodeParams p) {
+    constexpr int kWaves = WAVES;
+    constexpr int kThreads = kWaves * kWave;
+    constexpr int kCols = 32 * kWaves;        // query columns per workgroup
     constexpr int KSTEPS = D / 32;            // Q.K^T k-steps
     constexpr int DC = D / 16;                // 16-dim output tiles of P.V
     constexpr int KCH = D / 8;                // 16-byte chunks of a K row
@@ -323,25 +326,33 @@ void decode_prefix_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int BS>
+template <int D, int BS, int WAVES>
 hipError_t launch_shape(const DecodeParams& p, hipStream_t stream) {
     constexpr size_t kBuf = (size_t)(D / 8) * kTok * 16 + (size_t)D * kTok * 2;
     const uint64_t units = (uint64_t)p.num_seqs * p.num_kv_heads * p.max_parts;
     const uint64_t nwg = (units + kXcds - 1) / kXcds * kXcds * (uint64_t)p.col_groups;
-    hipLaunchKernelGGL((decode_prefix_kernel<D, BS>), dim3((unsigned)nwg), dim3(kThreads), 2 * kBuf, stream, p);
+    hipLaunchKernelGGL((decode_prefix_kernel<D, BS, WAVES>), dim3((unsigned)nwg), dim3(WAVES * kWave), 2 * kBuf,
+                       stream, p);
     return hipGetLastError();
+}
+
+template <int WAVES>
+hipError_t launch_waves(const DecodeParams& p, hipStream_t stream) {
+    if (p.head_dim == 64)
+        return p.block_size == 16 ? launch_shape<64, 16, WAVES>(p, stream) : launch_shape<64, 32, WAVES>(p, stream);
+    return p.block_size == 16 ? launch_shape<128, 16, WAVES>(p, stream) : launch_shape<128, 32, WAVES>(p, stream);
 }
 
 }  // namespace
 
-// Columns per workgroup of the launch below (the host sizes col_groups with it).
-int decode_prefix_columns() { return kCols; }
+// Query columns per workgroup of a launch with `waves` waves (4 or 8; the
+// host sizes col_groups with it), and the chunk its partitions are whole
+// multiples of.
+int decode_prefix_columns(int waves) { return 32 * waves; }
 int decode_prefix_chunk() { return kTok; }
 
 hipError_t launch_decode_prefix(const DecodeParams& p, hipStream_t stream) {
-    if (p.head_dim == 64)
-        return p.block_size == 16 ? launch_shape<64, 16>(p, stream) : launch_shape<64, 32>(p, stream);
-    return p.block_size == 16 ? launch_shape<128, 16>(p, stream) : launch_shape<128, 32>(p, stream);
+    return p.waves == 8 ? launch_waves<8>(p, stream) : launch_waves<4>(p, stream);
 }
 
 }  // namespace pa_impl
