@@ -82,10 +82,11 @@ __device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, kPolicyStream);
 }
 
-// Chunk-relative token of score slot 4 t + i held by lane group j.
-template <bool SPLIT>
+// Chunk-relative token of score slot 4 t + i held by lane group j: split
+// halves, or interleaved.
+template <bool IL>
 __device__ __forceinline__ int slot_token(int t, int i, int j) {
-    return SPLIT ? kHalf * t + 4 * j + i : 8 * j + 4 * t + i;
+    return IL ? 8 * j + 4 * t + i : kHalf * t + 4 * j + i;
 }
 
 // (6-wave workgroups are held to three waves per SIMD, so two share a compute unit)
@@ -98,6 +99,9 @@ void decode_mfma_kernel(DecodeParams p) {
     constexpr int DC = D / 16;       // 16-dim output tiles of P.V
     constexpr uint32_t kTileBytes = (uint32_t)D * BS * 2;
     static_assert(BS == 16 || BS == 32, "block size");
+    // token order inside a chunk: split halves on the streaming path at
+    // block 16, interleaved otherwise
+    constexpr bool IL = !SPLIT || BS == 32;
 
     extern __shared__ float smem[];
     float* sm_m = smem;                          // [kWaves][16]
@@ -152,15 +156,16 @@ void decode_mfma_kernel(DecodeParams p) {
         for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(ld16(qrow + 32 * s + 8 * j));
     }
 
-    // split path: per-lane byte offsets inside a half's K / V tile (loop
-    // invariant); the k-step / dim-tile strides are scalar offsets.
-    const uint32_t kofs = (uint32_t)((j * BS + r) * 16);
-    const uint32_t vofs = (uint32_t)((r * BS + 4 * j) * 2);
-    constexpr uint32_t kStepBytes = 4u * BS * 16;     // K chunk 4 s + j -> 4 (s + 1) + j
-    constexpr uint32_t kTileStep = 16u * BS * 2;      // V dim 16 dc + r -> 16 (dc + 1) + r
-    // interleaved path: this lane's K row (tile 0) and V token group
+    // interleaved order: this lane's K row (tile 0) and V token group
     const int tk = 8 * (r / 4) + (r % 4);
     const int tv = 8 * j;
+    // streaming path: per-lane byte offsets inside a K / V page tile (a
+    // half's at block 16; loop invariant); the tile, k-step and dim-tile
+    // strides are scalar offsets.
+    const uint32_t kofs = (uint32_t)((j * BS + (IL ? tk : r)) * 16);
+    const uint32_t vofs = (uint32_t)((r * BS + (IL ? tv : 4 * j)) * 2);
+    constexpr uint32_t kStepBytes = 4u * BS * 16;     // K chunk 4 s + j -> 4 (s + 1) + j
+    constexpr uint32_t kTileStep = 16u * BS * 2;      // V dim 16 dc + r -> 16 (dc + 1) + r
 
     const int* row = p.block_tables + (size_t)b * p.max_blocks_per_seq;
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.k_cache);
@@ -285,45 +290,57 @@ void decode_mfma_kernel(DecodeParams p) {
                     mask_v = __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(p.append_mask + b, 8), 0, 0, 0);
                 load_new_row();
             }
-            __amdgpu_buffer_rsrc_t krs[2], vrs[2];
-            for (int t = 0; t < 2; ++t) {
-                const int page = t ? pg1 : pg0;
-                const int toff = BS == 32 ? kHalf * t : 0;      // token offset in the page
-                const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
-                // a half with no valid token gets an empty range: loads return 0
-                // (at block 32 the appending chunk reads its page's second
-                // half anyway: it writes the page's rows back whole, below)
-                const bool live = t == 0 || valid > kHalf || (BS == 32 && last_cand);
-                krs[t] = make_rsrc(kc + tile + toff * 8, live ? kTileBytes - toff * 16 : 0);
-                vrs[t] = make_rsrc(vc + tile + toff, live ? kTileBytes - toff * 2 : 0);
+            if constexpr (IL) {
+                // block 32: the chunk is one page; row tile t's K rows sit 4 t
+                // tokens (64 bytes) in, each V operand is one 16-byte load (8
+                // tokens of a dim).  Every load covers whole 64-byte blocks of
+                // the page; tokens past the context are masked below.
+                const size_t tile = ((size_t)pg0 * kv_heads + g) * tile_elems;
+                const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + tile, kTileBytes);
+                const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + tile, kTileBytes);
+                for (int t = 0; t < 2; ++t)
+                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs, kofs, 64u * t + s * kStepBytes);
+                for (int dc = 0; dc < DC; ++dc) vop[dc] = bload16(vrs, vofs, dc * kTileStep);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                __amdgpu_buffer_rsrc_t krs[2], vrs[2];
+                for (int t = 0; t < 2; ++t) {
+                    const size_t tile = ((size_t)(t ? pg1 : pg0) * kv_heads + g) * tile_elems;
+                    // a half (page) with no valid token gets an empty range: loads return 0
+                    const bool live = t == 0 || valid > kHalf;
+                    krs[t] = make_rsrc(kc + tile, live ? kTileBytes : 0);
+                    vrs[t] = make_rsrc(vc + tile, live ? kTileBytes : 0);
+                }
+                for (int t = 0; t < 2; ++t)
+                    for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
+                u32x2_t vh[2][DC];
+                for (int t = 0; t < 2; ++t)
+                    for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
+                // every load of the chunk is in flight before the first MFMA waits on one
+                __builtin_amdgcn_sched_barrier(0);
+                for (int dc = 0; dc < DC; ++dc)
+                    vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
             }
-            for (int t = 0; t < 2; ++t)
-                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16(krs[t], kofs, s * kStepBytes);
-            u32x2_t vh[2][DC];
-            for (int t = 0; t < 2; ++t)
-                for (int dc = 0; dc < DC; ++dc) vh[t][dc] = bload8(vrs[t], vofs, dc * kTileStep);
-            // every load of the chunk is in flight before the first MFMA waits on one
-            __builtin_amdgcn_sched_barrier(0);
-            for (int dc = 0; dc < DC; ++dc)
-                vop[dc] = u32x4_t{vh[0][dc][0], vh[0][dc][1], vh[1][dc][0], vh[1][dc][1]};
             if (last_cand) {
                 // The new row into this chunk's registers.  Position L - 1 is
-                // chunk token p0: K row r0 of half t0 (lane (r0, j) holds its
+                // chunk token p0: K row r0 of tile t0 (lane (r0, j) holds its
                 // 16-byte column 4 s + j, held by lane 4 s + j of new_k); V
-                // slot 4 j0 + i0 of half t0 (dword 2 t0 + i0 / 2, half i0 % 2,
-                // of the lanes with j = j0; lane (r, j0) takes dim 16 dc + r,
-                // held by lane (16 dc + r) % 64, element (16 dc + r) / 64).
+                // element e0 of the lanes with j = j0 (dword q0 = e0 / 2, half
+                // e0 % 2; lane (r, j0) takes dim 16 dc + r, held by lane
+                // (16 dc + r) % 64, element (16 dc + r) / 64).  Split halves:
+                // p0 = 16 t0 + r0, r0 = 4 j0 + i0, e0 = 4 t0 + i0; interleaved:
+                // p0 = 8 (r0 / 4) + 4 t0 + r0 % 4, e0 = p0 % 8, j0 = p0 / 8.
                 const int p0 = L - 1 - cstart;
-                const int t0 = p0 / kHalf;
-                const int r0 = p0 % kHalf;
-                const int j0 = (p0 % kHalf) / 4;
-                const int i0 = p0 % 4;
-                const int q0 = 2 * t0 + i0 / 2;
-                const uint32_t sh = 16u * (uint32_t)(i0 % 2);
+                const int t0 = IL ? (p0 / 4) % 2 : p0 / kHalf;
+                const int r0 = IL ? 4 * (p0 / 8) + p0 % 4 : p0 % kHalf;
+                const int j0 = IL ? p0 / 8 : (p0 % kHalf) / 4;
+                const int e0 = IL ? p0 % 8 : 4 * t0 + p0 % 4;
+                const int q0 = e0 / 2;
+                const uint32_t sh = 16u * (uint32_t)(e0 % 2);
                 // the same in every lane: the sequence appends (mask entry >= 0)
                 // into a page inside the pool
                 const bool app = (int32_t)mask_v[1] >= 0 &&
-                                 (uint32_t)(t0 ? raw1 : raw0) < (uint64_t)p.num_blocks;
+                                 (uint32_t)(t0 && !IL ? raw1 : raw0) < (uint64_t)p.num_blocks;
                 for (int s = 0; s < KSTEPS; ++s) {
                     u32x4_t v;
                     for (int e = 0; e < 4; ++e)
@@ -341,24 +358,26 @@ void decode_mfma_kernel(DecodeParams p) {
                         }
                 }
                 // The row goes to the cache inside whole 64-byte blocks: the
-                // four tokens of its K columns, and every dim row of its V
-                // half-page (block 16: the page's whole V tile; block 32: both
-                // halves of each 64-byte dim row), the other tokens' bytes as
-                // just loaded -- the same bits -- rather than as 2-byte pieces
-                // of 128 V dim rows.
-                const int pg_t0 = t0 ? pg1 : pg0;
-                const int toff0 = BS == 32 ? kHalf * t0 : 0;
+                // four tokens of its K columns (rows r with r / 4 = r0 / 4 of
+                // tile t0), and every dim row of its page's V tile, the other
+                // tokens' bytes as just loaded -- the same bits -- rather than
+                // as 2-byte pieces of 128 V dim rows.
+                const int pg_t0 = t0 && !IL ? pg1 : pg0;
                 uint16_t* kw = const_cast<uint16_t*>(kc) + ((size_t)pg_t0 * kv_heads + g) * tile_elems;
+                uint16_t* vw = const_cast<uint16_t*>(vc) + ((size_t)pg_t0 * kv_heads + g) * tile_elems;
+                const int krow = IL ? tk + 4 * t0 : r;           // page token of this lane's tile-t0 row
                 if (app && (r & ~3) == (r0 & ~3))
                     for (int s = 0; s < KSTEPS; ++s)
-                        st16(kw + ((size_t)(4 * s + j) * BS + toff0 + r) * 8, kraw[t0][s]);
-                for (int t = 0; t < 2 && app; ++t) {
-                    if (BS == 16 && t != t0) continue;           // block 16: the other half is another page
-                    const int toff = BS == 32 ? kHalf * t : 0;
-                    uint16_t* vw = const_cast<uint16_t*>(vc) + ((size_t)(BS == 32 ? pg0 : pg_t0) * kv_heads + g) * tile_elems;
-                    for (int dc = 0; dc < DC; ++dc)
-                        *reinterpret_cast<u32x2_t*>(vw + (size_t)(16 * dc + r) * BS + toff + 4 * j) =
-                            u32x2_t{vop[dc][2 * t], vop[dc][2 * t + 1]};
+                        st16(kw + ((size_t)(4 * s + j) * BS + krow) * 8, t0 ? kraw[1][s] : kraw[0][s]);
+                if (app) {
+                    for (int dc = 0; dc < DC; ++dc) {
+                        if constexpr (IL) {
+                            st16(vw + (size_t)(16 * dc + r) * BS + tv, vop[dc]);
+                        } else {
+                            *reinterpret_cast<u32x2_t*>(vw + (size_t)(16 * dc + r) * BS + 4 * j) =
+                                u32x2_t{vop[dc][2 * t0], vop[dc][2 * t0 + 1]};
+                        }
+                    }
                 }
             }
         } else {
@@ -392,7 +411,7 @@ void decode_mfma_kernel(DecodeParams p) {
         if (valid < kChunk) {
             for (int t = 0; t < 2; ++t)
                 for (int i = 0; i < 4; ++i)
-                    sc[4 * t + i] = (slot_token<SPLIT>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
+                    sc[4 * t + i] = (slot_token<IL>(t, i, j) < valid) ? sc[4 * t + i] : neg_inf();
         }
         float mx = sc[0];
         for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
@@ -423,7 +442,7 @@ void decode_mfma_kernel(DecodeParams p) {
         if (valid < kChunk) {
             // zero the value slots past the context: dword q holds slots 2 q, 2 q + 1
             for (int q = 0; q < 4; ++q) {
-                const int tok = slot_token<SPLIT>(q / 2, 2 * (q % 2), j);
+                const int tok = slot_token<IL>(q / 2, 2 * (q % 2), j);
                 const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
                 const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
                 for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);

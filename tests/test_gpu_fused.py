@@ -143,8 +143,13 @@ def test_fused_mask_and_empty_contexts():
             check_close(got, ref, "bf16", f"mask {kernel} P={ps}")
 
 
+# the 8B-shaped batch on 32-token pages: the streaming path's interleaved
+# token order (one page per chunk) under the longest-first single pass
+_BUILDERS = {"llama3_8b_bs32": lambda: W.llama3_8b(block_size=32)}
+
+
 @pytest.mark.parametrize("name", ["llama3_8b", "llama3_70b", "prefix_share", "beam_fork",
-                                  "long_context"])
+                                  "long_context", "llama3_8b_bs32"])
 def test_fused_named_workload_full_size(name):
     """The decode step as the benchmark runs it: set-up appends every token
     but each sequence's newest, then one pa_decode_append with the library's
@@ -152,7 +157,7 @@ def test_fused_named_workload_full_size(name):
     of the batch against the oracle (whole batch and each (sequence, head)
     row on its own), appended slots checked bit for bit."""
     pa = require_gpu()
-    w = W.by_name(name)
+    w = _BUILDERS[name]() if name in _BUILDERS else W.by_name(name)
     say("fused full", name, w.summary())
     t = W.make_tensors(w, "cuda")
     seqs = list(range(w.num_seqs))
