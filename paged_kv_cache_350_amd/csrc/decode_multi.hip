@@ -54,9 +54,14 @@ __device__ __forceinline__ u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, POLICY);
 }
 
-// Chunk-relative token of score slot 4 t + i held by lane group j (row tile
-// t is the 16-token half t of the chunk).
-__device__ __forceinline__ int slot_token(int t, int i, int j) { return kHalf * t + 4 * j + i; }
+// Chunk-relative token of score slot 4 t + i held by lane group j: row tile
+// t is the 16-token half t of the chunk (block 16: page t), or, at block 32
+// (one page per chunk), the interleaved order in which lane group j holds
+// tokens 8 j .. 8 j + 7.
+template <bool IL>
+__device__ __forceinline__ int slot_token(int t, int i, int j) {
+    return IL ? 8 * j + 4 * t + i : kHalf * t + 4 * j + i;
+}
 
 template <int D, int BS, int NT, int POLICY, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave)
@@ -68,6 +73,7 @@ void decode_multi_kernel(DecodeParams p) {
     constexpr int COLS = 16 * NT;    // (query token, head) columns per workgroup
     constexpr uint32_t kTileBytes = (uint32_t)D * BS * 2;
     static_assert(BS == 16 || BS == 32, "block size");
+    constexpr bool IL = BS == 32;    // interleaved token order (one page per chunk)
 
     extern __shared__ float smem[];
     float* sm_m = smem;                          // [kWaves][16]
@@ -131,8 +137,11 @@ void decode_multi_kernel(DecodeParams p) {
         for (int s = 0; s < KSTEPS; ++s) qf[nt][s] = as_bf16x8(ld16(qp + 32 * s + 8 * j));
     }
 
-    const uint32_t kofs = (uint32_t)((j * BS + r) * 16);
-    const uint32_t vofs = (uint32_t)((r * BS + 4 * j) * 2);
+    // this lane's K row (token of tile 0) and V token group in the chunk
+    const int tk = IL ? 8 * (r / 4) + (r % 4) : r;
+    const int tv = IL ? 8 * j : 4 * j;
+    const uint32_t kofs = (uint32_t)((j * BS + tk) * 16);
+    const uint32_t vofs = (uint32_t)((r * BS + tv) * 2);
     constexpr uint32_t kStepBytes = 4u * BS * 16;
     constexpr uint32_t kTileStep = 16u * BS * 2;
 
@@ -233,15 +242,24 @@ void decode_multi_kernel(DecodeParams p) {
 
         u32x4_t kraw[2][KSTEPS];
         u32x4_t vop[DC];
-        {
+        if constexpr (IL) {
+            // block 32: row tile t's K rows sit 4 t tokens (64 bytes) into the
+            // page, each V operand is one 16-byte load; every load covers whole
+            // 64-byte blocks, and tokens past the partition are masked below
+            const size_t tile = ((size_t)pg0 * kv_heads + g) * tile_elems;
+            const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + tile, kTileBytes);
+            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + tile, kTileBytes);
+            for (int t = 0; t < 2; ++t)
+                for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16<POLICY>(krs, kofs, 64u * t + s * kStepBytes);
+            for (int dc = 0; dc < DC; ++dc) vop[dc] = bload16<POLICY>(vrs, vofs, dc * kTileStep);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
             __amdgpu_buffer_rsrc_t krs[2], vrs[2];
             for (int t = 0; t < 2; ++t) {
-                const int page = t ? pg1 : pg0;
-                const int toff = BS == 32 ? kHalf * t : 0;
-                const size_t tile = ((size_t)page * kv_heads + g) * tile_elems;
+                const size_t tile = ((size_t)(t ? pg1 : pg0) * kv_heads + g) * tile_elems;
                 const bool half_live = t == 0 || valid > kHalf;
-                krs[t] = make_rsrc(kc + tile + toff * 8, half_live ? kTileBytes - toff * 16 : 0);
-                vrs[t] = make_rsrc(vc + tile + toff, half_live ? kTileBytes - toff * 2 : 0);
+                krs[t] = make_rsrc(kc + tile, half_live ? kTileBytes : 0);
+                vrs[t] = make_rsrc(vc + tile, half_live ? kTileBytes : 0);
             }
             for (int t = 0; t < 2; ++t)
                 for (int s = 0; s < KSTEPS; ++s) kraw[t][s] = bload16<POLICY>(krs[t], kofs, s * kStepBytes);
@@ -255,9 +273,10 @@ void decode_multi_kernel(DecodeParams p) {
         if (patch && cstart + kChunk > first_new) {          // wave-uniform: new rows in this chunk
             // One small group at a time (scheduling barriers between them), so the
             // patch never holds more than a few LDS values in registers.
-            // K: lane (r, j) holds token 16 t + r, 16-byte columns 4 s + j
+            // K: lane (r, j) holds token tk + (block 32: 4 t; block 16: 16 t),
+            // 16-byte columns 4 s + j
             for (int t = 0; t < 2; ++t) {
-                const int pos = cstart + kHalf * t + r;
+                const int pos = cstart + tk + (IL ? 4 : kHalf) * t;
                 const bool is_new = pos >= first_new && pos < end;
                 const uint16_t* src = s_new + (size_t)(is_new ? pos - first_new : 0) * 2 * D;
                 for (int s = 0; s < KSTEPS; ++s) {
@@ -266,10 +285,10 @@ void decode_multi_kernel(DecodeParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // V: dword q of vop[dc] holds tokens slot_token(q / 2, 2 (q % 2), j) and the next, dim 16 dc + r
+            // V: dword q of vop[dc] holds tokens slot_token<IL>(q / 2, 2 (q % 2), j) and the next, dim 16 dc + r
             for (int q = 0; q < 4; ++q) {
                 for (int hh = 0; hh < 2; ++hh) {
-                    const int pos = cstart + slot_token(q / 2, 2 * (q % 2) + hh, j);
+                    const int pos = cstart + slot_token<IL>(q / 2, 2 * (q % 2) + hh, j);
                     const bool is_new = pos >= first_new && pos < end;
                     const uint16_t* src = s_new + (size_t)(is_new ? pos - first_new : 0) * 2 * D + D;
                     const uint32_t sh = 16u * (uint32_t)hh;
@@ -300,7 +319,7 @@ void decode_multi_kernel(DecodeParams p) {
                 const int cut = min(valid, lim[nt] - cstart + 1);
                 for (int t = 0; t < 2; ++t)
                     for (int i = 0; i < 4; ++i)
-                        sc[4 * t + i] = slot_token(t, i, j) < cut ? sc[4 * t + i] : neg_inf();
+                        sc[4 * t + i] = slot_token<IL>(t, i, j) < cut ? sc[4 * t + i] : neg_inf();
             }
             float mx = sc[0];
             for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
@@ -330,7 +349,7 @@ void decode_multi_kernel(DecodeParams p) {
 
         if (valid < kChunk) {
             for (int q = 0; q < 4; ++q) {
-                const int tok = slot_token(q / 2, 2 * (q % 2), j);
+                const int tok = slot_token<IL>(q / 2, 2 * (q % 2), j);
                 const uint32_t lo = (tok < valid) ? 0x0000ffffu : 0u;
                 const uint32_t hi = (tok + 1 < valid) ? 0xffff0000u : 0u;
                 for (int dc = 0; dc < DC; ++dc) vop[dc][q] &= (lo | hi);
