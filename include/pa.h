@@ -411,8 +411,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
  *   partition_size    a multiple of 32 (0: 2048)
  *   workspace         >= pa_decode_shared_prefix_groups_workspace_size()
  * Each group's shared pages are read once per kv head and column group for
- * all its sequences' queries; the rest of every context per sequence; the
- * merge as in the split path.  Other arguments, preconditions and returns
+ * all its sequences' queries (with 64 or more query columns per group and kv
+ * head, by the LDS-staged prefix kernel in partitions of its own); the rest of
+ * every context per sequence; the merge as in the split path.  Other arguments, preconditions and returns
  * as for pa_decode_shared_prefix (context_lens[b] >= seq_shared_len[b], an
  * appended position past it); inconsistent group arrays give unspecified
  * output with memory accesses in bounds.
@@ -432,9 +433,13 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
 
 /*
  * Workspace bytes for pa_decode_shared_prefix_groups: the split path's
- * layout with one slot more per (sequence, head) row,
- * num_seqs * num_heads * (ceil(max_context_len / P) + 1) * (head_dim + 2) * 4
- * (P = partition_size, 0 meaning 2048).  0 for invalid arguments.
+ * layout with room for the prefix partials in front of each (sequence, head)
+ * row, num_seqs * num_heads * (ceil(max_context_len / P) + E) * (head_dim + 2)
+ * * 4 with E = max(1, ceil(max_context_len / 256)) (P = partition_size, 0
+ * meaning 2048; the prefix launch's partitions are at least 256 tokens).
+ * The call itself needs only ceil(max_context_len / P) + ceil(max_shared_len
+ * / Pp) slots (Pp its prefix partition), or + 1 on the multi-query prefix
+ * kernel.  0 for invalid arguments.
  */
 size_t pa_decode_shared_prefix_groups_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                                      int32_t max_context_len, int32_t partition_size);

@@ -140,7 +140,7 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     // positions below first_token are read by a shared-prefix launch
     const int first = p.seq_first ? p.seq_first[b] : p.first_token;
-    const int shift = p.seq_first ? (first % p.partition != 0 ? 1 : 0) : p.slot_shift;
+    const int shift = p.seq_first ? seq_slot_shift(first, p.partition, p.prefix_partition) : p.slot_shift;
     const int pstart = part * p.partition;
     if (pstart + p.partition <= first) return;
     const int start = max(pstart, first);

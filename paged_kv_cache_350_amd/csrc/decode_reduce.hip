@@ -110,7 +110,7 @@ void decode_reduce_kernel(ReduceParams p) {
 
     const int L = p.query_start ? token_context(p, b) : clamp_len(p.context_lens[b], p.max_context_len);
     int n = (L + p.partition - 1) / p.partition;
-    n += p.seq_first ? (p.seq_first[b] % p.partition != 0 ? 1 : 0) : p.slot_shift;
+    n += p.seq_first ? seq_slot_shift(p.seq_first[b], p.partition, p.prefix_partition) : p.slot_shift;
     n = n < 0 ? 0 : (n > p.max_parts ? p.max_parts : n);
 
     float M = lane < n ? m0 : neg_inf();

@@ -306,6 +306,7 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     p.seq_first = nullptr;
     p.table_rows_from_queries = 0;
     p.first_part = 0;
+    p.prefix_partition = 0;
     if (partition > 0) {
         p.partition = partition;
         p.max_parts = parts;
@@ -334,6 +335,7 @@ pa_status launch_reduce(const Plan& plan, const int32_t* context_lens, void* out
     r.max_query_len = 0;
     r.slot_shift = plan.p.slot_shift;
     r.seq_first = plan.p.seq_first;
+    r.prefix_partition = plan.p.prefix_partition;
     r.ws = plan.p.ws;
     r.context_lens = context_lens;
     r.out = out;
@@ -773,14 +775,22 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     return launch_reduce(plan, context_lens, out, stream);
 }
 
+// Grouped call: prefix slots per row beyond the split path's row.  A group's
+// prefix launch in partitions of P leaves one partly shared partition (one
+// slot more); the LDS-staged prefix launch writes ceil(S / Pp) partials of
+// its own partitions Pp >= 4 chunks, at most ceil(max_context_len / 256).
+int32_t groups_extra_slots(int32_t max_context_len) {
+    const int32_t wide = parts_for(max_context_len, 4 * pa_impl::decode_prefix_chunk());
+    return wide > 1 ? wide : 1;
+}
+
 size_t pa_decode_shared_prefix_groups_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                                      int32_t max_context_len, int32_t partition_size) {
     if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
     if (partition_size == 0) partition_size = kSharedPrefixPartition;
     if (partition_size < kChunk || partition_size % kChunk != 0) return 0;
-    // the split path's row plus one slot: a group whose shared length ends
-    // inside a partition reads that partition in two parts
-    return pa_impl::ws_rows(num_seqs, num_heads, parts_for(max_context_len, partition_size) + 1) *
+    return pa_impl::ws_rows(num_seqs, num_heads,
+                            parts_for(max_context_len, partition_size) + groups_extra_slots(max_context_len)) *
            (size_t)(head_dim + 2) * sizeof(float);
 }
 
@@ -814,19 +824,32 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_ARG;
     if (num_seqs == 0) return PA_OK;
     if (!seq_shared_len || (num_groups > 0 && (!group_start || !group_shared_len))) return PA_ERR_NULL;
-    const size_t need = pa_decode_shared_prefix_groups_workspace_size(num_seqs, num_heads, head_dim,
-                                                                      max_context_len, plan.partition);
-    if (!workspace) return PA_ERR_WORKSPACE;
-    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
     const int32_t P = plan.partition;
-    const int32_t row = parts_for(max_context_len, P) + 1;
+    const int32_t G = plan.p.group;
+    // 64 or more columns per group and kv head: the LDS-staged prefix kernel
+    // with partitions of its own (Pp), each sequence's slot shift following
+    // from its shared length; else the multi-query kernel in partitions of P
+    const int64_t cols = (int64_t)G * max_group_size;
+    const bool wide = num_groups > 0 && cols >= kPrefixWideMinCols;
+    const int32_t waves = cols > pa_impl::decode_prefix_columns(4) ? 8 : 4;
+    const int32_t wide_cg = (int32_t)((cols + pa_impl::decode_prefix_columns(waves) - 1) /
+                                      pa_impl::decode_prefix_columns(waves));
+    const int32_t Pp = wide ? prefix_wide_partition((int64_t)num_groups * num_kv_heads * wide_cg, waves,
+                                                    max_shared_len)
+                            : P;
+    const int32_t row = parts_for(max_context_len, P) + (wide ? parts_for(max_shared_len, Pp) : 1);
+    const size_t need = pa_impl::ws_rows(num_seqs, num_heads, row) * (size_t)(head_dim + 2) * sizeof(float);
+    if (!workspace) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ARG;
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
 
-    // Each group's shared positions: one multi-query launch whose virtual
-    // sequence g has query rows group_start[g] .. group_start[g + 1] - 1 (the
-    // group's decode queries, each seeing all group_shared_len[g]
-    // positions), reads the pages through its first member's table row and
-    // writes the partials of partitions 0 .. ceil(group_shared_len[g] / P) - 1
-    // to those slots of its members' rows.
+    // Each group's shared positions: one launch (the LDS-staged prefix kernel
+    // or the multi-query kernel) whose virtual sequence g has query rows
+    // group_start[g] .. group_start[g + 1] - 1 (the group's decode queries,
+    // each seeing all group_shared_len[g] positions), reads the pages through
+    // its first member's table row and writes the partials of partitions
+    // 0 .. ceil(group_shared_len[g] / Pp) - 1 to those slots of its members'
+    // rows.
     if (num_groups > 0 && max_shared_len > 0) {
         DecodeParams m{};
         m.q = q;
@@ -846,27 +869,35 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
         m.max_blocks_per_seq = max_blocks_per_seq;
         m.max_context_len = max_shared_len;
         m.num_blocks = num_blocks;
-        m.partition = P;
-        m.max_parts = parts_for(max_shared_len, P);
+        m.partition = Pp;
+        m.max_parts = parts_for(max_shared_len, Pp);
         m.ws_parts = row;
         m.split = 1;
-        m.waves = 4;
+        m.waves = wide ? waves : 4;
         m.query_start = group_start;
         m.num_tokens = num_seqs;
         m.max_query_len = max_group_size;
         m.stream_kv = 0;                      // ordinary loads: the pages are shared
         m.all_visible = 1;
         m.table_rows_from_queries = 1;
-        const int32_t tiles = multi_col_tiles(m.group, max_group_size);
-        m.col_groups = multi_col_groups(m.group, max_group_size);
-        if ((uint64_t)num_groups * num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid)
-            return PA_ERR_UNSUPPORTED;
-        st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
+        if (wide) {
+            m.col_groups = wide_cg;
+            if ((uint64_t)num_groups * num_kv_heads * m.col_groups * (m.max_parts + 8) >= kMaxGrid)
+                return PA_ERR_UNSUPPORTED;
+            st = hip_status(pa_impl::launch_decode_prefix(m, stream));
+        } else {
+            const int32_t tiles = multi_col_tiles(m.group, max_group_size);
+            m.col_groups = multi_col_groups(m.group, max_group_size);
+            if ((uint64_t)num_groups * num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid)
+                return PA_ERR_UNSUPPORTED;
+            st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
+        }
         if (st != PA_OK) return st;
     }
     // The rest of every context from its own shared length on, partitions
-    // shifted past its prefix slots, then the merge.
+    // shifted past its prefix slots (seq_slot_shift), then the merge.
     plan.p.seq_first = seq_shared_len;
+    plan.p.prefix_partition = Pp;
     plan.p.ws_parts = row;
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
@@ -1008,6 +1039,7 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
     r.max_query_len = max_query_len;
     r.slot_shift = 0;
     r.seq_first = nullptr;
+    r.prefix_partition = 0;
     return hip_status(pa_impl::launch_decode_reduce(r, dtype, stream));
 }
 

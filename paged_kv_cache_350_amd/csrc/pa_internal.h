@@ -60,6 +60,8 @@ struct DecodeParams {
     // below this one lie below first_token for every sequence; the grid
     // starts at it (0: every partition)
     int32_t first_part;
+    // with seq_first: the partition the prefix launch used (0: partition)
+    int32_t prefix_partition;
 };
 
 struct ReduceParams {
@@ -80,8 +82,18 @@ struct ReduceParams {
     // a row merges slots 0 .. ceil(L / partition) + slot_shift - 1 (a
     // shared prefix's partials come first, read in partitions of their own)
     int32_t slot_shift;
-    const int32_t* seq_first;   // or per sequence: 1 when its shared length ends inside a partition
+    const int32_t* seq_first;   // or per sequence (seq_slot_shift of its shared length)
+    int32_t prefix_partition;   // with seq_first: the prefix launch's partition (0: partition)
 };
+
+// Slot shift of a sequence whose own positions start at `first`, after a
+// prefix launch that wrote ceil(first / Pp) partials of its first positions
+// (Pp = prefix_partition, or P when 0) to slots 0 ..: its own partitions of P
+// tokens start with partition floor(first / P), which goes to the next slot.
+__host__ __device__ inline int seq_slot_shift(int first, int P, int prefix_partition) {
+    const int Pp = prefix_partition > 0 ? prefix_partition : P;
+    return (first + Pp - 1) / Pp - first / P;
+}
 
 // Workspace layout for the split path (all fp32):
 //   acc [num_seqs][num_heads][max_parts][head_dim]   unnormalised accumulator

@@ -372,5 +372,7 @@ def test_decode_shared_prefix_groups_validates(L, kw, status):
 
 def test_shared_prefix_groups_workspace_size(L):
     assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 256, 64) == 4 * 32 * 5 * 130 * 4
-    assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 10512, 0) == 4 * 32 * 7 * 130 * 4
+    # the split row (ceil(10512 / 2048) = 6) plus the prefix slots an LDS-staged
+    # prefix launch may write, partitions of at least 256 tokens: ceil(10512 / 256) = 42
+    assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 10512, 0) == 4 * 32 * 48 * 130 * 4
     assert L.pa_decode_shared_prefix_groups_workspace_size(4, 32, 128, 256, 48) == 0

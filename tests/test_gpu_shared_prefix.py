@@ -280,6 +280,47 @@ def test_prefix_groups_match_oracle(shape):
         check_close(out_f64(out), ref, "bf16", f"groups {shape} P={P}")
 
 
+@pytest.mark.parametrize("bs", [16, 32])
+def test_prefix_groups_wide_match_oracle(bs):
+    """Groups of 20, 17 and 16 sequences x 4 heads (64 to 80 columns per kv
+    head): the LDS-staged prefix kernel with partitions of its own, each
+    sequence's slot shift from its shared length (336 and 208 end inside a
+    64-token chunk at block 16), three sequences sharing nothing between the
+    groups and one in no group; with and without the fused append."""
+    pa = require_gpu()
+    groups = ([(20, 336), (3, 0), (17, 208), (16, 640)] if bs == 16 else
+              [(20, 320), (3, 0), (17, 224), (16, 640)])
+    w, t, arr = _grouped_batch(52 + bs, 32, 8, 128, bs, groups)
+    assert 4 * arr["max_group_size"] >= 64
+    say("prefix groups, wide", bs, groups, w.summary())
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    for P in (64, 256, 0):
+        out = pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                             t["context_lens"], w.scale, w.max_context_len, partition_size=P, **arr)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"groups wide bs {bs} P={P}")
+    B = w.num_seqs
+    k_new = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=t["k_new"].dtype, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    mask = np.full(B, -1, dtype=np.int64)
+    for i, b in enumerate(w.append_seq.tolist()):
+        k_new[b] = t["k_new"][i]
+        v_new[b] = t["v_new"][i]
+        mask[b] = w.append_slots[i]
+    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
+    rk, rv = oracle.kv_append(storage_np(k_new), storage_np(v_new), mask, kc0, vc0, w.block_size)
+    ref2 = oracle.decode(storage_np(t["q"]), rk, rv, w.block_tables, w.context_lens, w.scale, w.block_size,
+                         "bf16")
+    kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+    out = pa.decode_shared_prefix_groups(t["q"], kc, vc, t["block_tables"], t["context_lens"], w.scale,
+                                         w.max_context_len, partition_size=0, k_new=k_new, v_new=v_new,
+                                         slot_mapping=torch.from_numpy(mask).cuda(), **arr)
+    torch.cuda.synchronize()
+    assert np.array_equal(storage_np(kc).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(storage_np(vc).view(np.uint16), rv.view(np.uint16))
+    check_close(out_f64(out), ref2, "bf16", f"groups wide fused bs {bs}")
+
+
 def test_prefix_groups_fused_append():
     pa = require_gpu()
     w, t, arr = _grouped_batch(49, 32, 8, 128, 16, [(6, 256), (7, 160)])
