@@ -141,23 +141,27 @@ struct PrefixShape {
     int32_t row;     // slots per workspace row
     int32_t tiles;   // 16-column tiles per prefix workgroup
     int32_t col_groups;
-    bool wide;       // the LDS-staged prefix kernel (128 or 256 columns per workgroup)
-    int32_t waves;   // its waves per workgroup (4 or 8)
+    bool wide;       // the LDS-staged prefix kernel (128 columns per workgroup)
 };
 
 // Many query columns per kv head (a prompt forked to many sequences): the
-// LDS-staged prefix kernel, whose workgroups stage each chunk of shared
-// pages once for 128 columns (4 waves) or, beyond 128 columns, 256 (8
-// waves: half the staging per column; 100 sequences x 4 heads over a
-// 9,984-token prefix 63.6 -> 60.9 us per step).  Its partitions are
-// multiples of its 64-token chunk, sized so that the launch has about
-// kPrefixWideFill waves (two per SIMD; each workgroup holds 64 KiB of LDS).
+// LDS-staged prefix kernel, whose 4-wave workgroups stage each chunk of
+// shared pages once for 128 columns, in one launch with the rest of every
+// context (the two stages share the compute units).  Its partitions are
+// multiples of its 64-token chunk, sized so that the launch starts about one
+// prefix workgroup per compute unit (kPrefixWideFill waves), which leaves each
+// unit's second workgroup slot to the rest of the contexts.  Measured on
+// 100 sequences x 4 heads over a 9,984-token prefix and on 4 prompts x 25
+// sequences, step in us, fill 768 / 1024 / 1280 / 1536 / 2048 waves:
+// 58.8 / 51.8 / 51.1 / 51.2 / 57.3 and 39.4 / 41.5 / 42.8 / 43.9 / 48.6.
+// (The two stages as separate launches, 8-wave prefix workgroups two
+// waves per SIMD: 61.6 and 51.0.)
 constexpr int32_t kPrefixWideMinCols = 64;
-constexpr int64_t kPrefixWideFill = 2048;
+constexpr int64_t kPrefixWideFill = 1024;
 
-int32_t prefix_wide_partition(int64_t units_per_part, int32_t waves, int32_t shared_len) {
+int32_t prefix_wide_partition(int64_t units_per_part, int32_t shared_len) {
     const int32_t chunk = pa_impl::decode_prefix_chunk();
-    const int64_t wgs = kPrefixWideFill / waves;
+    const int64_t wgs = kPrefixWideFill / 4;
     const int64_t parts = (wgs + units_per_part - 1) / units_per_part;
     int64_t Pp = (shared_len + parts - 1) / parts;
     Pp = (Pp + chunk - 1) / chunk * chunk;
@@ -186,11 +190,10 @@ PrefixShape prefix_shape(int32_t num_seqs, int32_t group, int32_t num_kv_heads, 
     sh.col_groups = (int32_t)(((int64_t)group * num_seqs + 16 * sh.tiles - 1) / (16 * sh.tiles));
     sh.Pp = P;
     sh.wide = (int64_t)group * num_seqs >= kPrefixWideMinCols;
-    sh.waves = (int64_t)group * num_seqs > pa_impl::decode_prefix_columns(4) ? 8 : 4;
     if (sh.wide) {
-        const int32_t cols = pa_impl::decode_prefix_columns(sh.waves);
+        const int32_t cols = pa_impl::decode_prefix_columns();
         sh.col_groups = (int32_t)(((int64_t)group * num_seqs + cols - 1) / cols);
-        sh.Pp = prefix_wide_partition((int64_t)num_kv_heads * sh.col_groups, sh.waves, shared_len);
+        sh.Pp = prefix_wide_partition((int64_t)num_kv_heads * sh.col_groups, shared_len);
     }
     sh.np = shared_len > 0 ? (shared_len + sh.Pp - 1) / sh.Pp : 0;
     sh.shift = sh.np - shared_len / P;
@@ -722,8 +725,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     // whose query rows are all num_seqs decode queries, every row seeing all
     // shared_len positions, in partitions of sh.Pp written to slots
     // 0 .. sh.np - 1 of every row.
+    DecodeParams m{};
+    bool fused = false;                       // prefix stage in the launch of the rest
     if (sh.np > 0) {
-        DecodeParams m{};
         m.q = q;
         m.k_cache = k_cache;
         m.v_cache = v_cache;
@@ -745,7 +749,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.max_parts = sh.np;
         m.ws_parts = sh.row;
         m.split = 1;
-        m.waves = sh.wide ? sh.waves : 4;
+        m.waves = 4;
         m.query_start = nullptr;              // rows 0 .. num_seqs - 1
         m.num_tokens = num_seqs;
         m.max_query_len = num_seqs;
@@ -754,8 +758,8 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.all_visible = 1;
         m.uniform_len = shared_len;
         if ((uint64_t)num_kv_heads * m.col_groups * (m.max_parts + 8) >= kMaxGrid) return PA_ERR_UNSUPPORTED;
-        st = hip_status(sh.wide ? pa_impl::launch_decode_prefix(m, stream)
-                                : pa_impl::launch_decode_multi(m, sh.tiles, stream));
+        fused = sh.wide;
+        if (!fused) st = hip_status(pa_impl::launch_decode_multi(m, sh.tiles, stream));
         if (st != PA_OK) return st;
     }
     // The rest of every context, sequence by sequence, from shared_len on
@@ -770,7 +774,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
-    st = launch_plan(plan, stream);
+    st = fused ? hip_status(pa_impl::launch_decode_prefix_rest(m, plan.p, stream)) : launch_plan(plan, stream);
     if (st != PA_OK) return st;
     return launch_reduce(plan, context_lens, out, stream);
 }
@@ -828,14 +832,13 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
     const int32_t G = plan.p.group;
     // 64 or more columns per group and kv head: the LDS-staged prefix kernel
     // with partitions of its own (Pp), each sequence's slot shift following
-    // from its shared length; else the multi-query kernel in partitions of P
+    // from its shared length, in the launch of the rest of every context;
+    // else the multi-query kernel in partitions of P
     const int64_t cols = (int64_t)G * max_group_size;
     const bool wide = num_groups > 0 && cols >= kPrefixWideMinCols;
-    const int32_t waves = cols > pa_impl::decode_prefix_columns(4) ? 8 : 4;
-    const int32_t wide_cg = (int32_t)((cols + pa_impl::decode_prefix_columns(waves) - 1) /
-                                      pa_impl::decode_prefix_columns(waves));
-    const int32_t Pp = wide ? prefix_wide_partition((int64_t)num_groups * num_kv_heads * wide_cg, waves,
-                                                    max_shared_len)
+    const int32_t wide_cg = (int32_t)((cols + pa_impl::decode_prefix_columns() - 1) /
+                                      pa_impl::decode_prefix_columns());
+    const int32_t Pp = wide ? prefix_wide_partition((int64_t)num_groups * num_kv_heads * wide_cg, max_shared_len)
                             : P;
     const int32_t row = parts_for(max_context_len, P) + (wide ? parts_for(max_shared_len, Pp) : 1);
     const size_t need = pa_impl::ws_rows(num_seqs, num_heads, row) * (size_t)(head_dim + 2) * sizeof(float);
@@ -850,8 +853,9 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
     // its first member's table row and writes the partials of partitions
     // 0 .. ceil(group_shared_len[g] / Pp) - 1 to those slots of its members'
     // rows.
+    DecodeParams m{};
+    bool fused = false;                       // prefix stage in the launch of the rest
     if (num_groups > 0 && max_shared_len > 0) {
-        DecodeParams m{};
         m.q = q;
         m.k_cache = k_cache;
         m.v_cache = v_cache;
@@ -873,7 +877,7 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
         m.max_parts = parts_for(max_shared_len, Pp);
         m.ws_parts = row;
         m.split = 1;
-        m.waves = wide ? waves : 4;
+        m.waves = 4;
         m.query_start = group_start;
         m.num_tokens = num_seqs;
         m.max_query_len = max_group_size;
@@ -884,7 +888,7 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
             m.col_groups = wide_cg;
             if ((uint64_t)num_groups * num_kv_heads * m.col_groups * (m.max_parts + 8) >= kMaxGrid)
                 return PA_ERR_UNSUPPORTED;
-            st = hip_status(pa_impl::launch_decode_prefix(m, stream));
+            fused = true;
         } else {
             const int32_t tiles = multi_col_tiles(m.group, max_group_size);
             m.col_groups = multi_col_groups(m.group, max_group_size);
@@ -902,7 +906,7 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
-    st = launch_plan(plan, stream);
+    st = fused ? hip_status(pa_impl::launch_decode_prefix_rest(m, plan.p, stream)) : launch_plan(plan, stream);
     if (st != PA_OK) return st;
     return launch_reduce(plan, context_lens, out, stream);
 }

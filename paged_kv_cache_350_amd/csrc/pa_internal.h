@@ -118,10 +118,12 @@ hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype dtype, hipStream_t
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceParams& p, pa_dtype dtype, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeParams& p, int col_tiles, hipStream_t stream);
-// shared-prefix stage with LDS-staged K/V (p.waves 4 or 8): query columns
-// per workgroup, and the chunk its partition sizes must be a multiple of
-hipError_t launch_decode_prefix(const DecodeParams& p, hipStream_t stream);
-int decode_prefix_columns(int waves);
+// Shared-prefix stage with LDS-staged K/V (`pre`, 4-wave workgroups) and
+// the shared-page decode path over the rest of every context (`rest`, its
+// first_part and slot shifts set) in one launch; the stage's query columns
+// per workgroup, and the chunk its partition sizes must be a multiple of.
+hipError_t launch_decode_prefix_rest(const DecodeParams& pre, const DecodeParams& rest, hipStream_t stream);
+int decode_prefix_columns();
 int decode_prefix_chunk();
 
 }  // namespace pa_impl

@@ -325,13 +325,13 @@ def test_shared_prefix_workspace_size():
     assert pa.shared_prefix_workspace_size(3, 4, 4, 64, 33, 40, 32) == 0                 # past max_context_len
     assert pa.shared_prefix_workspace_size(-1, 4, 4, 64, 33, 0, 32) == 0
     # 100 sequences x 4 query heads per kv head = 400 columns: the LDS-staged
-    # prefix launch on 8-wave workgroups, 2 column groups of 256 x 8 kv heads
-    # = 16 workgroups per partition, so 16 partitions for about 2,048 waves,
-    # of ceil(9984 / 16) = 624 tokens rounded up to the 64-token chunk = 640:
-    # 16 prefix slots, then the per-sequence partitions 4 and 5 of the
-    # default 2048 -> 18 slots per row
+    # prefix stage on 4-wave workgroups, 4 column groups of 128 x 8 kv heads
+    # = 32 workgroups per partition, so 8 partitions for about 1,024 waves,
+    # of ceil(9984 / 8) = 1248 tokens rounded up to the 64-token chunk = 1280:
+    # 8 prefix slots, then the per-sequence partitions 4 and 5 of the
+    # default 2048 -> 10 slots per row
     assert pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 0) == \
-        pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 2048) == 100 * 32 * 18 * 130 * 4
+        pa.shared_prefix_workspace_size(100, 32, 8, 128, 10512, 9984, 2048) == 100 * 32 * 10 * 130 * 4
     # 24 sequences x 4 = 96 columns, one 4-wave column group: 8 workgroups per
     # partition would ask for 64 partitions, but they are at least 4 chunks
     # (256 tokens): 3 prefix slots; the per-sequence partitions of 32 start
