@@ -2,6 +2,7 @@
 // design in decode_prefix_body.h) together with the decode kernel's
 // shared-page path (decode_mfma_body.h) over the rest of every context.
 #include "decode_mfma_body.h"
+#include "decode_multi_body.h"
 #include "decode_prefix_body.h"
 
 namespace pa_impl {
@@ -45,6 +46,47 @@ hipError_t launch_fused_shape(const DecodeParams& pre, const DecodeParams& rest,
     return hipGetLastError();
 }
 
+// The same for a prefix stage of fewer columns: the multi-query kernel (one
+// or two 16-column tiles per workgroup, ordinary loads; each workgroup reads
+// its partition's pages itself) with the rest of every context beside it on
+// the compute units.  Workgroups n_pre .. n_pre_pad - 1 are idle padding to
+// a multiple of the XCD count.  One tile holds the kernel to three waves
+// per SIMD, so that two rest workgroups fit beside a prefix workgroup.
+template <int D, int BS, int NT>
+__global__ __launch_bounds__(4 * kWave, NT == 1 ? 3 : 2)
+void decode_multi_rest_kernel(DecodeParams pre, DecodeParams rest, uint32_t n_pre, uint32_t n_pre_pad) {
+    extern __shared__ float smem[];
+    if (blockIdx.x < n_pre_pad) {
+        if (blockIdx.x < n_pre)
+            multi_detail::decode_multi_body<D, BS, NT, kPolicyReuse, 4>(pre, blockIdx.x, smem);
+    } else {
+        mfma_detail::decode_mfma_body<D, BS, false, 4>(rest, blockIdx.x - n_pre_pad, smem);
+    }
+}
+
+template <int D, int BS, int NT>
+hipError_t launch_multi_fused_shape(const DecodeParams& pre, const DecodeParams& rest, hipStream_t stream) {
+    const uint64_t n_pre = (uint64_t)pre.num_seqs * pre.num_kv_heads * pre.col_groups * pre.max_parts;
+    const uint64_t n_pre_pad = (n_pre + kXcds - 1) / kXcds * kXcds;
+    const uint64_t n_rest = (uint64_t)rest.num_seqs * rest.num_kv_heads * (rest.max_parts - rest.first_part);
+    const size_t pre_smem = sizeof(float) * (2 * 4 * 16 + (size_t)4 * 16 * D);
+    const size_t rest_smem = sizeof(float) * (2 * 4 * 16 + (size_t)4 * rest.group * D);
+    const size_t smem = pre_smem > rest_smem ? pre_smem : rest_smem;
+    if (n_pre_pad + n_rest == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_multi_rest_kernel<D, BS, NT>), dim3((unsigned)(n_pre_pad + n_rest)), dim3(4 * kWave),
+                       smem, stream, pre, rest, (uint32_t)n_pre, (uint32_t)n_pre_pad);
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_multi_fused_tiles(const DecodeParams& pre, const DecodeParams& rest, hipStream_t stream) {
+    if (pre.head_dim == 64)
+        return pre.block_size == 16 ? launch_multi_fused_shape<64, 16, NT>(pre, rest, stream)
+                                    : launch_multi_fused_shape<64, 32, NT>(pre, rest, stream);
+    return pre.block_size == 16 ? launch_multi_fused_shape<128, 16, NT>(pre, rest, stream)
+                                : launch_multi_fused_shape<128, 32, NT>(pre, rest, stream);
+}
+
 }  // namespace
 
 // Query columns per prefix workgroup (the host sizes col_groups with it),
@@ -58,6 +100,12 @@ hipError_t launch_decode_prefix_rest(const DecodeParams& pre, const DecodeParams
                                     : launch_fused_shape<64, 32>(pre, rest, stream);
     return pre.block_size == 16 ? launch_fused_shape<128, 16>(pre, rest, stream)
                                 : launch_fused_shape<128, 32>(pre, rest, stream);
+}
+
+hipError_t launch_decode_multi_rest(const DecodeParams& pre, int col_tiles, const DecodeParams& rest,
+                                   hipStream_t stream) {
+    return col_tiles == 1 ? launch_multi_fused_tiles<1>(pre, rest, stream)
+                          : launch_multi_fused_tiles<2>(pre, rest, stream);
 }
 
 }  // namespace pa_impl

@@ -758,9 +758,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
         m.all_visible = 1;
         m.uniform_len = shared_len;
         if ((uint64_t)num_kv_heads * m.col_groups * (m.max_parts + 8) >= kMaxGrid) return PA_ERR_UNSUPPORTED;
-        fused = sh.wide;
-        if (!fused) st = hip_status(pa_impl::launch_decode_multi(m, sh.tiles, stream));
-        if (st != PA_OK) return st;
+        fused = true;
     }
     // The rest of every context, sequence by sequence, from shared_len on
     // (with the fused append of pa_decode_append when new rows are given:
@@ -774,7 +772,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
-    st = fused ? hip_status(pa_impl::launch_decode_prefix_rest(m, plan.p, stream)) : launch_plan(plan, stream);
+    if (!fused) st = launch_plan(plan, stream);
+    else if (sh.wide) st = hip_status(pa_impl::launch_decode_prefix_rest(m, plan.p, stream));
+    else st = hip_status(pa_impl::launch_decode_multi_rest(m, sh.tiles, plan.p, stream));
     if (st != PA_OK) return st;
     return launch_reduce(plan, context_lens, out, stream);
 }
@@ -855,6 +855,7 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
     // rows.
     DecodeParams m{};
     bool fused = false;                       // prefix stage in the launch of the rest
+    int32_t tiles = 1;                        // multi-query prefix stage: tiles per workgroup
     if (num_groups > 0 && max_shared_len > 0) {
         m.q = q;
         m.k_cache = k_cache;
@@ -888,15 +889,13 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
             m.col_groups = wide_cg;
             if ((uint64_t)num_groups * num_kv_heads * m.col_groups * (m.max_parts + 8) >= kMaxGrid)
                 return PA_ERR_UNSUPPORTED;
-            fused = true;
         } else {
-            const int32_t tiles = multi_col_tiles(m.group, max_group_size);
+            tiles = multi_col_tiles(m.group, max_group_size);
             m.col_groups = multi_col_groups(m.group, max_group_size);
             if ((uint64_t)num_groups * num_kv_heads * m.col_groups * m.max_parts >= kMaxGrid)
                 return PA_ERR_UNSUPPORTED;
-            st = hip_status(pa_impl::launch_decode_multi(m, tiles, stream));
         }
-        if (st != PA_OK) return st;
+        fused = true;
     }
     // The rest of every context from its own shared length on, partitions
     // shifted past its prefix slots (seq_slot_shift), then the merge.
@@ -906,7 +905,9 @@ pa_status pa_decode_shared_prefix_groups(const void* q, const void* k_cache, con
     plan.p.k_new = k_new;
     plan.p.v_new = v_new;
     plan.p.append_mask = k_new ? slot_mapping : nullptr;
-    st = fused ? hip_status(pa_impl::launch_decode_prefix_rest(m, plan.p, stream)) : launch_plan(plan, stream);
+    if (!fused) st = launch_plan(plan, stream);
+    else if (wide) st = hip_status(pa_impl::launch_decode_prefix_rest(m, plan.p, stream));
+    else st = hip_status(pa_impl::launch_decode_multi_rest(m, tiles, plan.p, stream));
     if (st != PA_OK) return st;
     return launch_reduce(plan, context_lens, out, stream);
 }

@@ -123,6 +123,10 @@ hipError_t launch_decode_multi(const DecodeParams& p, int col_tiles, hipStream_t
 // first_part and slot shifts set) in one launch; the stage's query columns
 // per workgroup, and the chunk its partition sizes must be a multiple of.
 hipError_t launch_decode_prefix_rest(const DecodeParams& pre, const DecodeParams& rest, hipStream_t stream);
+// the same with the multi-query kernel as the prefix stage (`pre` with
+// shared-page loads, 4-wave workgroups, col_tiles 16-column tiles each)
+hipError_t launch_decode_multi_rest(const DecodeParams& pre, int col_tiles, const DecodeParams& rest,
+                                    hipStream_t stream);
 int decode_prefix_columns();
 int decode_prefix_chunk();
 
