@@ -342,20 +342,23 @@ pa_status pa_decode_reduce(const void* workspace, size_t workspace_bytes,
  * after forking one prompt.  [Internals, "Copy-on-Write and Prefix
  * Sharing"; Glossary, "Copy-on-Write Memory Forking"]
  *
- * The shared pages are read once per kv head for up to 32 (sequence, query
- * head) pairs at a time -- a matrix-core launch whose columns are the
+ * The shared pages are read once per kv head for up to 128 (sequence,
+ * query head) pairs at a time -- a matrix-core stage whose columns are the
  * decode queries of several sequences, each seeing all shared_len
  * positions -- instead of once per sequence; the rest of every context is
  * read per sequence by the split decode kernel from position shared_len
- * on.  The prefix launch picks its own partition size; its partials take
- * the first slots of every (sequence, head) workspace row and the
- * per-sequence partitions follow, so the merge kernel combines one
+ * on, in the same launch (the two stages share the compute units), and a
+ * merge launch follows.  With 64 or more columns per kv head the prefix
+ * stage stages its pages in LDS and picks its own partition size; its
+ * partials take the first slots of every (sequence, head) workspace row and
+ * the per-sequence partitions follow, so the merge kernel combines one
  * contiguous run per row.  The result is the same attention as pa_decode,
  * within the same bounds.
  *
  *   shared_len      a multiple of block_size, 0 <= shared_len <=
  *                   max_context_len (0: the plain split path)
- *   partition_size  a multiple of 32, the partition of both launches; 0
+ *   partition_size  a multiple of 32, the partition of the per-sequence
+ *                   stage (and of the prefix stage below 64 columns); 0
  *                   picks 2048, measured best on a 100-sequence forked
  *                   prompt and on 8 beams
  *   workspace       >= pa_decode_shared_prefix_workspace_size(num_seqs,
@@ -412,8 +415,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
  *   workspace         >= pa_decode_shared_prefix_groups_workspace_size()
  * Each group's shared pages are read once per kv head and column group for
  * all its sequences' queries (with 64 or more query columns per group and kv
- * head, by the LDS-staged prefix kernel in partitions of its own); the rest of
- * every context per sequence; the merge as in the split path.  Other arguments, preconditions and returns
+ * head, by the LDS-staged prefix stage in partitions of its own); the rest of
+ * every context per sequence in the same launch; the merge as in the split
+ * path.  Other arguments, preconditions and returns
  * as for pa_decode_shared_prefix (context_lens[b] >= seq_shared_len[b], an
  * appended position past it); inconsistent group arrays give unspecified
  * output with memory accesses in bounds.
