@@ -596,15 +596,16 @@ pa_status pa_decode_append(const void* k_new, const void* v_new, const int64_t* 
     if (plan.use_mfma && plan.p.waves == pa_impl::kWideWaves && plan.partition == 0 && !plan.p.order_by_length) {
         // One pass of 12-wave workgroups over many rounds (a 70B-shaped
         // batch: 2,048 workgroups, eight rounds): the rows go to the cache in
-        // a launch of their own first (decode 372 + append 8 us), because
-        // the fused append measured 415 us there however it was done --
-        // storing the row alone and waiting for it, or patching the chunk's
-        // registers and writing whole 64-byte blocks, with ordinary or
-        // non-temporal stores.  Taking parts out in copies of the kernel: the
-        // K patch of the last chunk cost about 30 us and the stores about
-        // 10; loading the new row and patching V cost nothing.  The
-        // longest-first pass (two to four rounds) keeps the fused append
-        // (8B-shaped step 94.0 us).
+        // a launch of their own first (decode 373.4 + append 7.8 us), because
+        // stores inside this read stream slow every workgroup's reads.  The
+        // fused append measured 416.6 us however it was done -- storing the
+        // row alone and waiting for it, or patching the chunk's registers and
+        // writing whole 64-byte blocks, with ordinary or non-temporal stores
+        // -- and 374.5 us with the registers patched and the stores taken
+        // out.  The stores in workgroups of their own in the same launch,
+        // after the decode grid or before it, cost more than the separate
+        // launch (385.4 and 393.0 us).  The longest-first pass (two to four
+        // rounds) keeps the fused append (8B-shaped step 94.0 us).
         st = hip_status(pa_impl::launch_append_newest(plan.p, dtype, stream));
         if (st != PA_OK) return st;
         plan.p.k_new = nullptr;
