@@ -52,6 +52,7 @@ SHAPES = [  # (num_heads, num_kv_heads, head_dim, block_size)
     (32, 8, 128, 32),
     (64, 8, 128, 16),     # G = 8: 4 sequences per 32-column group
     (32, 2, 64, 16),      # G = 16: 2 sequences per group, D 64
+    (32, 2, 64, 32),      # the same at block 32
 ]
 
 
@@ -194,21 +195,26 @@ def test_fused_append():
         assert bits_equal(out, out2), f"fused != separate P={P}"
 
 
-@pytest.mark.parametrize("nseq", [8, 4, 1])
-def test_few_sequences(nseq):
-    """8 sequences x 4 heads fill one group of 32 columns (the prefix launch
-    then runs one 16-column tile per workgroup over two groups), 4 fit one
-    tile, and a single sequence shares a prefix with itself."""
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (32, 8, 64, 32)], ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("nseq", [12, 8, 4, 1])
+def test_few_sequences(nseq, shape):
+    """Fewer than 64 columns per kv head: the multi-query prefix stage.  12
+    sequences x 4 heads = 48 columns run two 16-column tiles per workgroup
+    over two groups; 8 fill one group of 32 columns (the prefix stage then
+    runs one tile per workgroup over two groups), 4 fit one tile, and a
+    single sequence shares a prefix with itself.  D 128 at block 16 and D 64
+    at block 32."""
     pa = require_gpu()
-    w, t = _shared_batch("shared_few", 45 + nseq, 32, 8, 128, 16, shared_tokens=768, nseq=nseq)
-    say("shared prefix,", nseq, "sequences", w.summary())
+    hq, hkv, d, bs = shape
+    w, t = _shared_batch("shared_few", 45 + nseq, hq, hkv, d, bs, shared_tokens=768, nseq=nseq)
+    say("shared prefix,", nseq, "sequences", shape, w.summary())
     ref = step_and_reference(pa, w, t, range(w.num_seqs))
-    S = pa.shared_prefix_len(w.block_tables, w.context_lens, 16)
+    S = pa.shared_prefix_len(w.block_tables, w.context_lens, bs)
     assert S == 768
     for P in (128, 256, 320):                         # 768 = 2 x 320 + 128: the extra slot
         out = _run(pa, w, t, S, P)
         torch.cuda.synchronize()
-        check_close(out_f64(out), ref, "bf16", f"shared {nseq} seqs P={P}")
+        check_close(out_f64(out), ref, "bf16", f"shared {nseq} seqs {shape} P={P}")
 
 
 def test_largest_batch():
@@ -260,12 +266,16 @@ def _grouped_batch(seed, hq, hkv, d, bs, groups, loner_len=300):
     return w, t, arrays
 
 
-@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32)], ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (64, 8, 128, 32), (32, 8, 128, 32), (32, 8, 64, 16)],
+                         ids=lambda s: "-".join(map(str, s)))
 def test_prefix_groups_match_oracle(shape):
     """Groups of 10, 5, 1 and 14 sequences, three sequences sharing nothing
     between the second and third, and one sequence in no group.  At block 16
     the shared lengths 336 and 208 end in the middle of a 32-token chunk and
-    of a partition; at block 32, 320 and 480 end on or inside partitions."""
+    of a partition; at block 32, 320 and 480 end on or inside partitions.
+    With 4 heads per kv head the groups have up to 56 columns: the
+    multi-query prefix stage with two 16-column tiles per workgroup (D 128
+    and 64, block 16 and 32); with 8, the LDS-staged stage."""
     pa = require_gpu()
     hq, hkv, d, bs = shape
     groups = ([(10, 336), (5, 96), (3, 0), (1, 640), (14, 208)] if bs == 16 else
