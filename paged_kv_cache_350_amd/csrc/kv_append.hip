@@ -78,14 +78,24 @@ void kv_append_kernel(const E* __restrict__ k, const E* __restrict__ v,
     store_row(k_cache, v_cache, tile, off, block_size, head_dim, lane, src);
 }
 
-// Bulk append.  A workgroup takes TG consecutive tokens of kv head
-// blockIdx.y.  Their K and V rows come in as 16-byte loads along each row
-// (coalesced) into LDS, one chunk of padding per row.  How they are stored
-// depends on the slots, decided once per workgroup:
+// Bulk append.  The tokens are cut into page segments: maximal runs of
+// tokens in consecutive slots of one page (a token whose slot is invalid is a
+// segment of its own).  A workgroup takes kv head blockIdx.y of the segments
+// that start among tokens TG * blockIdx.x .. + TG - 1 (TG = 32) -- the last
+// of them may run up to 31 tokens past that window -- so every page segment
+// is written by one workgroup: a prefill run that starts inside a page leaves
+// no page row split between two workgroups' partial stores.  Measured, bf16,
+// 8 kv heads, D 128, block 32: the prefix workload's suffix prefill (25,484
+// tokens in 100 runs starting at page offset 16) 70.3 us with fixed 64-token
+// windows, 42.4 us with segments over 64-token windows, 36.2 us over 32-token
+// ones (16: 50.9); a 32,768-token prompt 45.9, 47.2 and 40.9 us.
+// The rows come in as 16-byte loads along each row (coalesced) into LDS, one
+// chunk of padding per row.  How they are stored depends on the slots,
+// decided once per workgroup:
 //  * most neighbouring tokens in consecutive slots of one page (a prefill
 //    run): lane j of a lane group stores token j, so one store instruction
-//    writes the same K chunk or the same V dim of TG consecutive tokens --
-//    a V page row of block_size elements and a K run of block_size 16-byte
+//    writes the same K chunk or the same V dim of consecutive tokens -- a V
+//    page row of block_size elements and a K run of block_size 16-byte
 //    chunks land whole, where one row at a time leaves each 32-byte sector
 //    of a dim-major V page to block_size separate 2-byte writes (measured:
 //    32,768 prompt tokens, 8 kv heads, D 128, bf16, in 46-53 us against
@@ -96,6 +106,7 @@ void kv_append_kernel(const E* __restrict__ k, const E* __restrict__ v,
 //    scattered tokens lane by lane measured 3x slower than that).
 // Any slot mapping is handled by both; only the speed depends on it.
 constexpr int kTileThreads = 256;
+constexpr int kTileWindow = 32;
 
 template <typename E, int D>
 __global__ __launch_bounds__(kTileThreads)
@@ -106,54 +117,84 @@ void kv_append_tile_kernel(const E* __restrict__ k, const E* __restrict__ v,
                            int64_t num_blocks) {
     constexpr int X = 16 / (int)sizeof(E);         // elements per 16-byte chunk
     constexpr int CH = D / X;                      // chunks per row
-    constexpr int TG = 128 / (int)sizeof(E);       // tokens per workgroup: 64 bf16, 32 fp32
+    constexpr int TG = kTileWindow;                // tokens per window
+    constexpr int TGX = TG + 32;                   // the window and the rest of a segment (block_size <= 32)
     constexpr int RS = CH + 1;                     // LDS row stride in chunks
     constexpr int NG = kTileThreads / TG;          // lane groups over chunks / dims
-    __shared__ u32x4_t sk[TG * RS];
-    __shared__ u32x4_t sv[TG * RS];
-    __shared__ int64_t s_base[TG];                 // element offset of the token's (page, head) tile, -1: skip
-    __shared__ int s_off[TG];
+    static_assert(TGX <= kTileThreads && TGX <= 2 * kWave, "one thread of the first two waves per examined token");
+    __shared__ u32x4_t sk[TGX * RS];
+    __shared__ u32x4_t sv[TGX * RS];
+    __shared__ int64_t s_base[TGX];                // element offset of the token's (page, head) tile, -1: skip
+    __shared__ int s_off[TGX];
+    __shared__ uint64_t s_starts[2];               // per token of the first two waves: starts a segment
 
     const int tid = threadIdx.x;
     const int h = (int)blockIdx.y;
-    const int64_t tok0 = (int64_t)blockIdx.x * TG;
-    const int ntok = (int)min((int64_t)TG, (int64_t)num_tokens - tok0);
+    const int64_t w0 = (int64_t)blockIdx.x * TG;
     const int64_t nslots = num_blocks * block_size;
-    int adjacent = 0;                              // this token and the next in consecutive slots of one page
-    if (tid < TG) {
-        int64_t base = -1;
-        int off = 0;
-        if (tid < ntok) {
-            const int64_t slot = slot_mapping[tok0 + tid];
-            if (slot >= 0 && slot < nslots) {      // padding / out of range: skipped
-                off = (int)(slot % block_size);
-                base = (slot / block_size * num_kv_heads + h) * (int64_t)D * block_size;
-                if (tid + 1 < ntok && off + 1 < block_size)
-                    adjacent = slot_mapping[tok0 + tid + 1] == slot + 1;
-            }
-        }
-        s_base[tid] = base;
-        s_off[tid] = off;
+    // token w0 + tid (tid < TGX): its slot and its predecessor's, both loaded
+    // at once, and whether it starts a page segment (a token past the last
+    // counts as a start, so the last segment ends there)
+    const int64_t t = w0 + tid;
+    int64_t slot = -1, prev = -1;
+    if (tid < TGX && t < num_tokens) {
+        slot = slot_mapping[t];
+        if (t > 0) prev = slot_mapping[t - 1];
+    }
+    const bool valid = slot >= 0 && slot < nslots;            // padding / out of range: skipped
+    const bool starts = t >= num_tokens || !valid || t == 0 || slot % block_size == 0 || prev < 0 ||
+                        prev >= nslots || prev + 1 != slot;
+    if (tid < 2 * kWave) {                                     // whole waves: the ballot's lanes are all live
+        const uint64_t m = __builtin_amdgcn_ballot_w64(tid < TGX && starts);
+        if (tid % kWave == 0) s_starts[tid / kWave] = m;
+    }
+    __syncthreads();
+    const uint64_t m0 = s_starts[0];
+    const uint64_t m1 = s_starts[1];
+    // the starts among tokens [lo, hi) (hi - lo <= 64) as bits 0 .. hi - lo - 1
+    auto starts_in = [&](int lo, int hi) -> uint64_t {
+        const unsigned __int128 all = ((unsigned __int128)m1 << 64) | m0;
+        const uint64_t m = (uint64_t)(all >> lo);
+        return hi - lo >= 64 ? m : m & ((1ull << (hi - lo)) - 1);
+    };
+    // first start in [0, TG) and first start in [TG, TGX) (there is one when
+    // block_size <= 32: a segment is at most block_size tokens)
+    const uint64_t mb = starts_in(0, TG);
+    const uint64_t me = starts_in(TG, TGX);
+    const int begin = mb ? __builtin_ctzll(mb) : TG;
+    const int end = me ? TG + __builtin_ctzll(me) : TGX;
+    if (begin >= TG || w0 + begin >= num_tokens) return;      // no segment starts in this window
+    const int ntok = end - begin;                             // <= TGX
+    // pairs of neighbouring tokens in consecutive slots of one page: the
+    // tokens after the first that start no segment
+    const int runs = ntok - 1 - (int)__builtin_popcountll(starts_in(begin + 1, end > begin + 65 ? begin + 65 : end)) -
+                     (end > begin + 65 ? (int)__builtin_popcountll(starts_in(begin + 65, end)) : 0);
+    // token w0 + begin + j, j < ntok, in row j
+    if (tid >= begin && tid < end) {
+        const int j = tid - begin;
+        s_base[j] = valid ? (slot / block_size * num_kv_heads + h) * (int64_t)D * block_size : -1;
+        s_off[j] = valid ? (int)(slot % block_size) : 0;
     }
     for (int i = tid; i < ntok * CH; i += kTileThreads) {
         const int j = i / CH;
         const int c = i % CH;
-        const int64_t src = ((tok0 + j) * num_kv_heads + h) * (int64_t)D + (int64_t)c * X;
+        const int64_t src = ((w0 + begin + j) * num_kv_heads + h) * (int64_t)D + (int64_t)c * X;
         sk[j * RS + c] = ld16(k + src);
         sv[j * RS + c] = ld16(v + src);
     }
-    const int runs = __syncthreads_count(adjacent);          // also the barrier after the LDS writes
+    __syncthreads();
 
     if (2 * runs >= ntok - 1) {
-        const int j = tid % TG;
         const int g = tid / TG;
-        const int64_t base = s_base[j];
-        if (j >= ntok || base < 0) return;
-        const int off = s_off[j];
-        for (int c = g; c < CH; c += NG)
-            st16_nt(k_cache + base + ((int64_t)c * block_size + off) * X, sk[j * RS + c]);
-        const E* vrow = reinterpret_cast<const E*>(&sv[j * RS]);
-        for (int d = g; d < D; d += NG) st_nt(&v_cache[base + (int64_t)d * block_size + off], vrow[d]);
+        for (int j = tid % TG; j < ntok; j += TG) {
+            const int64_t base = s_base[j];
+            if (base < 0) continue;
+            const int off = s_off[j];
+            for (int c = g; c < CH; c += NG)
+                st16_nt(k_cache + base + ((int64_t)c * block_size + off) * X, sk[j * RS + c]);
+            const E* vrow = reinterpret_cast<const E*>(&sv[j * RS]);
+            for (int d = g; d < D; d += NG) st_nt(&v_cache[base + (int64_t)d * block_size + off], vrow[d]);
+        }
         return;
     }
     for (int i = tid; i < ntok * CH; i += kTileThreads) {
@@ -216,7 +257,7 @@ template <typename E, int D>
 hipError_t launch_tile(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
                        void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t block_size,
                        int64_t num_blocks, hipStream_t stream) {
-    constexpr int TG = 128 / (int)sizeof(E);
+    constexpr int TG = kTileWindow;
     const dim3 grid((unsigned)(((int64_t)num_tokens + TG - 1) / TG), (unsigned)num_kv_heads);
     hipLaunchKernelGGL((kv_append_tile_kernel<E, D>), grid, dim3(kTileThreads), 0, stream,
                        (const E*)k, (const E*)v, slot_mapping, (E*)k_cache, (E*)v_cache, num_tokens,
