@@ -724,10 +724,11 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     if (!aligned16(workspace)) return PA_ERR_ARG;
     if (workspace_bytes < need) return PA_ERR_WORKSPACE;
 
-    // Prefix positions: one multi-query launch over sequence 0's table row
-    // whose query rows are all num_seqs decode queries, every row seeing all
-    // shared_len positions, in partitions of sh.Pp written to slots
-    // 0 .. sh.np - 1 of every row.
+    // Prefix positions: a stage over sequence 0's table row whose query rows
+    // are all num_seqs decode queries, every row seeing all shared_len
+    // positions, in partitions of sh.Pp written to slots 0 .. sh.np - 1 of
+    // every row (the LDS-staged prefix body, or the multi-query body below 64
+    // columns), launched together with the rest of every context.
     DecodeParams m{};
     bool fused = false;                       // prefix stage in the launch of the rest
     if (sh.np > 0) {

@@ -217,6 +217,32 @@ def test_few_sequences(nseq, shape):
         check_close(out_f64(out), ref, "bf16", f"shared {nseq} seqs {shape} P={P}")
 
 
+@pytest.mark.parametrize("nseq", [24, 8])
+def test_sequences_ending_at_the_prefix(nseq):
+    """Sequences whose whole context is the shared prefix (their rest-of-
+    context work is empty: no positions, an empty partial) beside longer
+    ones, and a batch in which every sequence ends there (at P = 64 no rest
+    workgroup is launched at all); the LDS-staged prefix stage (24 sequences
+    x 4 heads) and the multi-query one (8)."""
+    pa = require_gpu()
+    S = 640
+    rng = np.random.default_rng(60 + nseq)
+    lens = S + 2 + rng.integers(0, 300, size=nseq)
+    lens[1::3] = S                                    # every third sequence ends at the prefix
+    for every in (False, True):
+        L = np.full(nseq, S) if every else lens
+        w = W.custom("shared_end", 61 + nseq, "bf16", L.tolist(), 32, 8, 128, 16)
+        t = W.make_tensors(w, "cuda")
+        _share_rows(w, t, S)
+        say("shared prefix, sequences ending at it", nseq, "every one" if every else "every third", w.summary())
+        ref = step_and_reference(pa, w, t, range(nseq))
+        assert pa.shared_prefix_len(w.block_tables, w.context_lens, 16) == S
+        for P in (64, 256, 0):
+            out = _run(pa, w, t, S, P)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, "bf16", f"ending at the prefix {nseq} every={every} P={P}")
+
+
 def test_largest_batch():
     """1,024 sequences, the most one call takes: 4,096 (sequence, head)
     columns in 128 groups over the shared prefix; sampled sequences, the
