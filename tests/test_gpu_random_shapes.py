@@ -1,0 +1,151 @@
+"""Randomised shapes on the GPU against the float64 oracle.
+
+The fixed-shape tests pin each path on purpose, one parameter at a time.
+This sweep crosses the parameters with each other: every seed draws one
+configuration -- block size, head dim, kv heads, query heads per kv head (1
+to 16), batch size, ragged context lengths from 1 token to a few thousand,
+partition sizes and load path -- and checks on it
+
+* pa_decode, both kernels where the dtype has them, every drawn partition
+  size and both load paths;
+* pa_decode_append: caches bit-identical to the oracle's append, the output
+  bit-identical to pa_kv_append + pa_decode and within tolerance of the
+  oracle;
+* pa_decode_multi with a random number of new tokens per sequence;
+* pa_decode_shared_prefix over a random shared length.
+
+Seeds are fixed, so every run checks the same cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, step_and_reference, storage_np
+from test_gpu_fused import newest_rows
+from test_gpu_multi import oracle_multi, prepare
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(30))
+GROUPS = [1, 2, 3, 4, 5, 6, 7, 8, 12, 16]
+PARTS = [-1, 0, 32, 64, 96, 160, 512, 2048]
+
+
+def _draw(seed):
+    """One configuration: (rng, block_size, head_dim, kv heads, group,
+    context lengths, three partition sizes)."""
+    rng = np.random.default_rng(9100 + seed)
+    bs = int(rng.choice([16, 32]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice(GROUPS))
+    nseq = int(rng.integers(1, 25))
+    longer = rng.random(nseq) < 0.7
+    lens = np.where(longer, rng.integers(1, 2500, size=nseq, endpoint=True),
+                    rng.integers(1, 70, size=nseq, endpoint=True))
+    parts = [int(x) for x in rng.choice(PARTS, size=3, replace=False)]
+    return rng, bs, d, hkv, g, lens, parts
+
+
+def _decode(pa, w, t, P, kernel, reuse):
+    return pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], w.scale,
+                     w.max_context_len, partition_size=P, kernel=kernel, reuse=reuse)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_decode(seed):
+    pa = require_gpu()
+    rng, bs, d, hkv, g, lens, parts = _draw(seed)
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    w = W.custom(f"random_decode_{seed}", 9100 + seed, dtype, lens.tolist(), g * hkv, hkv, d, bs)
+    say("random decode seed", seed, "partitions", parts, w.summary())
+    t = W.make_tensors(w, "cuda")
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    for kernel in (["valu", "mfma"] if dtype == "bf16" else ["valu"]):
+        for reuse in ("stream", "shared"):
+            for P in parts:
+                say("  kernel", kernel, "reuse", reuse, "partition", P)
+                out = _decode(pa, w, t, P, kernel, reuse)
+                torch.cuda.synchronize()
+                check_close(out_f64(out), ref, dtype, f"seed {seed} {kernel} {reuse} P={P}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_fused_append(seed):
+    pa = require_gpu()
+    rng, bs, d, hkv, g, lens, parts = _draw(seed)
+    w = W.custom(f"random_fused_{seed}", 9100 + seed, "bf16", lens.tolist(), g * hkv, hkv, d, bs)
+    say("random fused append seed", seed, "partitions", parts, w.summary())
+    t = W.make_tensors(w, "cuda")
+    k_new, v_new, mask, older = newest_rows(w, t)
+    assert not older
+    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
+    kc_ref, vc_ref = oracle.kv_append(storage_np(k_new)[mask >= 0], storage_np(v_new)[mask >= 0], mask[mask >= 0],
+                                      kc0, vc0, bs)
+    ref = oracle.decode(storage_np(t["q"]), kc_ref, vc_ref, w.block_tables, w.context_lens, w.scale, bs, "bf16")
+    mask_t = torch.from_numpy(mask).cuda()
+    for reuse in ("stream", "shared"):
+        for P in parts:
+            say("  reuse", reuse, "partition", P)
+            fused = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+            out = pa.decode_append(k_new, v_new, fused["q"], fused["k_cache"], fused["v_cache"],
+                                   fused["block_tables"], fused["context_lens"], w.scale, w.max_context_len,
+                                   slot_mapping=mask_t, partition_size=P, reuse=reuse)
+            apart = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+            pa.kv_append(k_new[mask_t >= 0].contiguous(), v_new[mask_t >= 0].contiguous(),
+                         mask_t[mask_t >= 0].contiguous(), apart["k_cache"], apart["v_cache"])
+            two = _decode(pa, w, apart, P, "auto", reuse)
+            torch.cuda.synchronize()
+            assert np.array_equal(storage_np(fused["k_cache"]), kc_ref), f"seed {seed} K cache P={P}"
+            assert np.array_equal(storage_np(fused["v_cache"]), vc_ref), f"seed {seed} V cache P={P}"
+            assert bits_equal(out, two), f"seed {seed} fused vs separate {reuse} P={P}"
+            check_close(out_f64(out), ref, "bf16", f"seed {seed} fused {reuse} P={P}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_multi_query(seed):
+    pa = require_gpu()
+    rng, bs, d, hkv, g, lens, parts = _draw(seed)
+    news = np.minimum(lens, rng.integers(0, 13, size=len(lens)))
+    w = W.multi_custom(f"random_multi_{seed}", 9100 + seed, lens.tolist(), news.tolist(), g * hkv, hkv, d, bs)
+    t, kc0, vc0, q = prepare(w)
+    say("random multi-query seed", seed, "new tokens", news.tolist(), "partitions", parts, w.summary())
+    ref = oracle_multi(w, kc0, vc0, q)
+    pa.kv_append(t["k_new"], t["v_new"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    for reuse in ("stream", "shared"):
+        for P in parts:
+            say("  reuse", reuse, "partition", P)
+            out = pa.decode_multi(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                  t["query_start"], w.scale, w.max_context_len, w.max_query_len,
+                                  partition_size=P, reuse=reuse)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, "bf16", f"seed {seed} multi {reuse} P={P}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_shared_prefix(seed):
+    """Every sequence reads row 0's pages for its first S positions; each
+    context goes at least one token past them (the appended row never lands
+    in a shared page)."""
+    pa = require_gpu()
+    rng, bs, d, hkv, g, _, parts = _draw(seed)
+    nseq = int(rng.integers(1, 41))
+    shared = bs * int(rng.integers(1, 2000 // bs))
+    lens = shared + 1 + rng.integers(0, 600, size=nseq)
+    w = W.custom(f"random_shared_{seed}", 9100 + seed, "bf16", lens.tolist(), g * hkv, hkv, d, bs)
+    t = W.make_tensors(w, "cuda")
+    tables = w.block_tables.copy()
+    tables[:, :shared // bs] = tables[0, :shared // bs]
+    w.block_tables = tables
+    t["block_tables"].copy_(torch.from_numpy(tables))
+    say("random shared prefix seed", seed, "shared", shared, "partitions", parts, w.summary())
+    ref = step_and_reference(pa, w, t, range(w.num_seqs))
+    assert pa.shared_prefix_len(w.block_tables, w.context_lens, bs) >= shared
+    for P in [0] + [p for p in parts if p > 0]:
+        say("  partition", P)
+        out = pa.decode_shared_prefix(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                      w.scale, w.max_context_len, shared, P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"seed {seed} shared prefix P={P}")
