@@ -12,7 +12,10 @@ partition sizes and load path -- and checks on it
   bit-identical to pa_kv_append + pa_decode and within tolerance of the
   oracle;
 * pa_decode_multi with a random number of new tokens per sequence;
-* pa_decode_shared_prefix over a random shared length.
+* pa_decode_shared_prefix over a random shared length;
+* pa_kv_append of a random slot pattern (prefill runs starting anywhere in
+  a page, scattered slots, padding, slots outside the pool), bit-exact on
+  the whole cache.
 
 Seeds are fixed, so every run checks the same cases."""
 
@@ -23,6 +26,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, step_and_reference, storage_np
+from test_gpu_cache_ops import _random_cache
 from test_gpu_fused import newest_rows
 from test_gpu_multi import oracle_multi, prepare
 
@@ -149,3 +153,60 @@ def test_random_shared_prefix(seed):
                                       w.scale, w.max_context_len, shared, P)
         torch.cuda.synchronize()
         check_close(out_f64(out), ref, "bf16", f"seed {seed} shared prefix P={P}")
+
+
+def append_slots(rng, T, bs):
+    """A slot pattern of T tokens and the pool it needs: prefill runs
+    (positions a .. a + n - 1 of a sequence whose pages come off a permuted
+    free list, so a run may start anywhere in its first page), single
+    scattered slots, padding (-1) and slots past the pool.  Every valid slot
+    is unique: each page serves one run or one scattered slot."""
+    nb = 3 * (T // bs) + 200
+    free = [int(x) for x in rng.permutation(nb)]
+    slots = []
+    while len(slots) < T:
+        kind = rng.random()
+        if kind < 0.6:
+            a = int(rng.integers(0, 3 * bs))
+            n = int(rng.integers(1, 300))
+            need = (a + n + bs - 1) // bs
+            if need > len(free):
+                slots.append(-1)
+                continue
+            pages = [free.pop() for _ in range(need)]
+            slots.extend(pages[p // bs] * bs + p % bs for p in range(a, a + n))
+        elif kind < 0.8 and free:
+            slots.append(free.pop() * bs + int(rng.integers(0, bs)))
+        elif kind < 0.9:
+            slots.append(-1)
+        else:
+            slots.append(nb * bs + int(rng.integers(0, 1000)))
+    return np.asarray(slots[:T], dtype=np.int64), nb
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_append(seed):
+    pa = require_gpu()
+    rng = np.random.default_rng(9400 + seed)
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    bs = int(rng.choice([16, 32]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    T = int(rng.integers(1, 512)) if rng.random() < 0.4 else int(rng.integers(512, 6000))
+    slots, nb = append_slots(rng, T, bs)
+    say("random append seed", seed, dtype, "bs", bs, "D", d, "kv heads", hkv, "tokens", T, "pages", nb)
+    x = W.chunk_elems(dtype)
+    kc, vc = _random_cache((nb, hkv, d // x, bs, x), (nb, hkv, d, bs), dtype, 9400 + seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9400 + seed)
+    td = W.torch_dtype(dtype)
+    k = torch.randn(T, hkv, d, generator=g, device="cuda").to(td)
+    v = torch.randn(T, hkv, d, generator=g, device="cuda").to(td)
+    k_before, v_before = storage_np(kc), storage_np(vc)
+    pa.kv_append(k, v, torch.from_numpy(slots).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    ref_slots = np.where(slots < nb * bs, slots, -1)         # slots past the pool write nothing
+    rk, rv = oracle.kv_append(storage_np(k), storage_np(v), ref_slots, k_before, v_before, bs)
+    view = np.uint16 if dtype == "bf16" else np.uint32
+    assert np.array_equal(storage_np(kc).view(view), rk.view(view)), f"seed {seed} K cache"
+    assert np.array_equal(storage_np(vc).view(view), rv.view(view)), f"seed {seed} V cache"
