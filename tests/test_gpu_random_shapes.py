@@ -12,7 +12,10 @@ partition sizes and load path -- and checks on it
   bit-identical to pa_kv_append + pa_decode and within tolerance of the
   oracle;
 * pa_decode_multi with a random number of new tokens per sequence;
-* pa_decode_shared_prefix over a random shared length;
+* pa_decode_shared_prefix over a random shared length, and
+  pa_decode_shared_prefix_groups over random groups (sizes, shared lengths,
+  groups that share nothing, a sequence in no group), plain and with the
+  fused append;
 * pa_kv_append of a random slot pattern (prefill runs starting anywhere in
   a page, scattered slots, padding, slots outside the pool), bit-exact on
   the whole cache.
@@ -29,6 +32,7 @@ from gpu_util import bits_equal, check_close, out_f64, require_gpu, say, step_an
 from test_gpu_cache_ops import _random_cache
 from test_gpu_fused import newest_rows
 from test_gpu_multi import oracle_multi, prepare
+from test_gpu_shared_prefix import _grouped_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -154,6 +158,41 @@ def test_random_shared_prefix(seed):
         torch.cuda.synchronize()
         check_close(out_f64(out), ref, "bf16", f"seed {seed} shared prefix P={P}")
 
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_prefix_groups(seed):
+    pa = require_gpu()
+    rng, bs, d, hkv, g, _, parts = _draw(seed)
+    groups = [(int(rng.integers(1, 31)), 0 if rng.random() < 0.2 else bs * int(rng.integers(1, 1500 // bs)))
+              for _ in range(int(rng.integers(1, 7)))]
+    w, t, arr = _grouped_batch(9700 + seed, g * hkv, hkv, d, bs, groups, loner_len=int(rng.integers(1, 900)))
+    say("random prefix groups seed", seed, groups, "partitions", parts, w.summary())
+    fused = rng.random() < 0.5
+    if not fused:
+        ref = step_and_reference(pa, w, t, range(w.num_seqs))
+        for P in [0] + [p for p in parts if p > 0]:
+            say("  partition", P)
+            out = pa.decode_shared_prefix_groups(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                                 t["context_lens"], w.scale, w.max_context_len, partition_size=P,
+                                                 **arr)
+            torch.cuda.synchronize()
+            check_close(out_f64(out), ref, "bf16", f"seed {seed} groups P={P}")
+        return
+    k_new, v_new, mask, older = newest_rows(w, t)
+    assert not older
+    kc0, vc0 = storage_np(t["k_cache"]), storage_np(t["v_cache"])
+    rk, rv = oracle.kv_append(storage_np(k_new), storage_np(v_new), mask, kc0, vc0, bs)
+    ref = oracle.decode(storage_np(t["q"]), rk, rv, w.block_tables, w.context_lens, w.scale, bs, "bf16")
+    for P in [0] + [p for p in parts if p > 0]:
+        say("  fused append, partition", P)
+        kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+        out = pa.decode_shared_prefix_groups(t["q"], kc, vc, t["block_tables"], t["context_lens"], w.scale,
+                                             w.max_context_len, partition_size=P, k_new=k_new, v_new=v_new,
+                                             slot_mapping=torch.from_numpy(mask).cuda(), **arr)
+        torch.cuda.synchronize()
+        assert np.array_equal(storage_np(kc).view(np.uint16), rk.view(np.uint16)), f"seed {seed} K cache P={P}"
+        assert np.array_equal(storage_np(vc).view(np.uint16), rv.view(np.uint16)), f"seed {seed} V cache P={P}"
+        check_close(out_f64(out), ref, "bf16", f"seed {seed} groups fused P={P}")
 
 def append_slots(rng, T, bs):
     """A slot pattern of T tokens and the pool it needs: prefill runs
