@@ -41,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published peak
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak, published
 METRIC = "paged-decode KV GB/s read (% of MI355X HBM peak) and decode seqs/sec"
 
 
@@ -82,6 +83,9 @@ def _args(argv=None):
                          "speculative-verification batch (5 queries per sequence); append_bulk: "
                          "pa_kv_append at prefill sizes; read_calib: streaming reads of a known "
                          "size with and without the non-temporal bit (to scale traffic counters)")
+    ap.add_argument("--multi-workload", default="spec_verify", choices=["spec_verify", "prompt_chunk"],
+                    help="multi mode: speculative verification (5 queries per sequence, HBM-bound) or a "
+                         "prompt chunk (512 queries per sequence over 3,584 cached tokens, matrix-bound)")
     ap.add_argument("--requests", type=int, default=2000, help="prefix mode: requests in the stream")
     ap.add_argument("--oracle-requests", type=int, default=400,
                     help="prefix mode: leading requests the oracle replays (CPU baseline sample)")
@@ -498,7 +502,8 @@ def multi_bench(a, torch, pa, W) -> int:
     whole pa_decode_multi call as the launch (one kernel in one pass; with a
     split the merge kernel too, which the rocprofv3 summary separates)."""
     import oracle
-    w = W.spec_verify()
+    chunk = a.multi_workload == "prompt_chunk"
+    w = W.prompt_chunk() if chunk else W.spec_verify()
     t = W.make_tensors(w, "cuda")
     reuse = a.reuse if a.reuse != "auto" else "stream"
     ps_req = 0 if a.partition_size is None else a.partition_size
@@ -540,6 +545,7 @@ def multi_bench(a, torch, pa, W) -> int:
         w.max_context_len, w.max_query_len, out=out, partition_size=P if P > 0 else -1, workspace=ws,
         reuse=reuse, **app), nloop)
     kv_bytes = w.algorithmic_kv_bytes()       # every context token once per kv head (one column group)
+    flops = w.multi_flops()
     ms_per_step = wall * 1e3 / a.steps
     achieved = kv_bytes / (multi_ms * 1e-3) / 1e9
     digest = _src_digest()
@@ -559,10 +565,40 @@ def multi_bench(a, torch, pa, W) -> int:
             nbytes += int(w.context_lens[b]) * w.kv_bytes_per_token()
             if elapsed >= a.cpu_seconds:
                 break
-        cpu = {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} whole sequences of the {w.name} batch, float64 numpy oracle, "
-                         f"{elapsed:.1f} s of CPU time"}
+        if chunk:       # the sequences are alike: flops in proportion
+            cpu = {"value": round(flops * done / w.num_seqs / elapsed / 1e9, 3), "unit": "GFLOP/s", "cores": 1,
+                   "kind": "oracle", "sample": f"{done} whole sequences of the {w.name} batch, float64 numpy "
+                                               f"oracle, {elapsed:.1f} s of CPU time"}
+        else:
+            cpu = {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{done} whole sequences of the {w.name} batch, float64 numpy oracle, "
+                             f"{elapsed:.1f} s of CPU time"}
     kname = "decode_multi" + ("_single" if P <= 0 else " partition + merge")
+    if chunk:
+        # matrix-bound: 512 queries per sequence make the product dense
+        tflops = flops / (multi_ms * 1e-3) / 1e12
+        rec = {
+            "metric": "multi-query paged attention TFLOP/s (chunked prefill)",
+            "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "prompt_tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+            "config": {"workload": w.name, "description": w.description, "num_seqs": w.num_seqs,
+                       "query_tokens": T, "max_query_len": w.max_query_len,
+                       "sum_context_tokens": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
+                       "partition_size": P, "flops_per_step": flops, "kv_bytes_per_step": kv_bytes,
+                       "step": a.step},
+            "kernels_avg_us": {"kv_append": None if fused else round(append_ms * 1e3, 2),
+                               kname: round(multi_ms * 1e3, 2)},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": kname, "avg_launch_us": round(multi_ms * 1e3, 2),
+                         "algorithmic_flops_per_launch": flops, "source_digest": digest},
+            "cpu_baseline": cpu,
+        }
+        print(json.dumps(rec), flush=True)
+        return 0
     rec = {
         "metric": "multi-query paged attention KV GB/s read (speculative verification)",
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,

@@ -497,6 +497,14 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  *   workspace      pa_decode_multi_workspace_size() bytes when the split
  *                  path runs (else ignored); caller-owned
  *
+ * Two kernels serve the call, chosen on the host from the head group G =
+ * num_heads / num_kv_heads and max_query_len: below 64 query columns
+ * (G * max_query_len) per (sequence, kv head), as in speculative
+ * verification, each wave reads its chunks of K/V for up to 32 columns;
+ * from 64 on (a prompt chunk), each K/V chunk is staged once in LDS for 128
+ * columns, the product being dense enough for the matrix cores.  Either
+ * gives the same result up to rounding order.
+ *
  * Out-of-range device values are clamped (rows to [0, num_tokens), n_b to
  * max_query_len and to L_b); rows no sequence covers are not part of the
  * result (unspecified).  bf16 only: PA_ERR_UNSUPPORTED for fp32.  Returns
@@ -514,7 +522,9 @@ pa_status pa_decode_multi(const void* q, const void* k_cache, const void* v_cach
 
 /*
  * pa_decode_multi_append -- the step's append and pa_decode_multi in one
- * launch (no separate pa_kv_append).  k_new, v_new (device,
+ * call (no separate pa_kv_append; one launch below 64 query columns per
+ * (sequence, kv head), where the attention kernel stores the rows itself,
+ * and an append launch before the attention from 64 on).  k_new, v_new (device,
  * [num_tokens][num_kv_heads][head_dim] bf16, 16-byte aligned, read) are the
  * new tokens' K and V rows, row for row aligned with q: row
  * query_start[b] + j goes to position L_b - n_b + j of sequence b, i.e. to

@@ -87,6 +87,28 @@ hipError_t launch_multi_fused_tiles(const DecodeParams& pre, const DecodeParams&
                                 : launch_multi_fused_shape<128, 32, NT>(pre, rest, stream);
 }
 
+// The LDS-staged body on its own as the multi-query kernel of many columns
+// (a prompt chunk): causal rows, one pass or partials for the merge.
+// Workgroups take (sequence, kv head, partition) units spread over the XCDs
+// with every column group of a unit on one XCD, so the groups that stage the
+// same pages share its L2.
+template <int D, int BS>
+__global__ __launch_bounds__(4 * kWave, 2)
+void decode_multi_wide_kernel(DecodeParams p) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    decode_prefix_body<D, BS, 4, true>(p, blockIdx.x, lds);
+}
+
+template <int D, int BS>
+hipError_t launch_wide_shape(const DecodeParams& p, hipStream_t stream) {
+    constexpr size_t kBuf = (size_t)(D / 8) * kTok * 16 + (size_t)D * kTok * 2;
+    const uint64_t units = (uint64_t)p.num_seqs * p.num_kv_heads * p.max_parts;
+    const uint64_t n = (units + kXcds - 1) / kXcds * kXcds * (uint64_t)p.col_groups;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_multi_wide_kernel<D, BS>), dim3((unsigned)n), dim3(4 * kWave), 2 * kBuf, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Query columns per prefix workgroup (the host sizes col_groups with it),
@@ -100,6 +122,12 @@ hipError_t launch_decode_prefix_rest(const DecodeParams& pre, const DecodeParams
                                     : launch_fused_shape<64, 32>(pre, rest, stream);
     return pre.block_size == 16 ? launch_fused_shape<128, 16>(pre, rest, stream)
                                 : launch_fused_shape<128, 32>(pre, rest, stream);
+}
+
+hipError_t launch_decode_multi_wide(const DecodeParams& p, hipStream_t stream) {
+    if (p.head_dim == 64)
+        return p.block_size == 16 ? launch_wide_shape<64, 16>(p, stream) : launch_wide_shape<64, 32>(p, stream);
+    return p.block_size == 16 ? launch_wide_shape<128, 16>(p, stream) : launch_wide_shape<128, 32>(p, stream);
 }
 
 hipError_t launch_decode_multi_rest(const DecodeParams& pre, int col_tiles, const DecodeParams& rest,

@@ -31,6 +31,20 @@
 // read spread over the banks); K keeps the page's [16-byte chunk][token]
 // order over 64 tokens.  Two chunk buffers take 64 KiB of LDS.
 //
+// The same body serves multi-query calls with many query columns per
+// (sequence, kv head) -- a chunk of a prompt, whose n new tokens attend
+// causally [PagedAttention Internals, "The Mathematical Cause of KV Cache
+// Fragmentation", closing link; paging and attention as in "How
+// PagedAttention Works" items 1-3]: with CAUSAL, column c (new token c / G
+// of the sequence's n) sees positions <= L - n + c / G.  A workgroup's
+// partition ends at the last position any of its columns sees, a wave skips
+// the chunks none of its columns sees, and scores past a column's last
+// position are masked.  The context's last page may hold stale values past
+// L, so in a chunk that ends early the V slots past it are zeroed as well
+// (a shared prefix always ends on a page boundary).  A single pass (no
+// split) writes the normalised output rows directly: each wave owns its
+// columns for the whole partition, so no merge across waves is needed.
+//
 // Online softmax in log2 units with the lazy rescale of the decode kernel
 // (the running max moves only when a score exceeds it by more than 8).
 // Each wave writes its columns' split-path partials (running max, running
@@ -56,7 +70,7 @@ constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // One workgroup's work: `bid` is its index in the grid of (unit, column
 // group) workgroups that launch_shape sizes, `lds` two chunk buffers.
-template <int D, int BS, int WAVES>
+template <int D, int BS, int WAVES, bool CAUSAL = false>
 __device__ __forceinline__ void decode_prefix_body(const DecodeParams& p, uint32_t bid, unsigned char* lds) {
     constexpr int kWaves = WAVES;
     constexpr int kThreads = kWaves * kWave;
@@ -99,19 +113,30 @@ __device__ __forceinline__ void decode_prefix_body(const DecodeParams& p, uint32
     int L = p.uniform_len > 0 ? p.uniform_len : p.context_lens[gi];
     const int cap = min(p.max_context_len, p.max_blocks_per_seq * BS);
     L = L < 0 ? 0 : (L > cap ? cap : L);
-    const QueryRows qr = query_rows(p.query_start, gi, INT_MAX, p.num_tokens, p.max_query_len);
+    const QueryRows qr = query_rows(p.query_start, gi, CAUSAL ? L : INT_MAX, p.num_tokens, p.max_query_len);
     const int ncols = G * qr.n;
     const int col0 = (int)cg * kCols;
     if (col0 >= ncols) return;
     const int start = part * p.partition;
-    if (start >= L) return;
-    const int end = min(start + p.partition, L);
+    // last position any column of the workgroup sees
+    const int hi_lim = CAUSAL ? L - qr.n + min(qr.n - 1, (col0 + kCols - 1) / G) : L - 1;
+    if (start > hi_lim) return;
+    const int end = min(start + p.partition, hi_lim + 1);
     const int nch = (end - start + kTok - 1) / kTok;
 
     // this wave's 32 columns (none when past the group's queries: the wave
     // still stages chunks for the others)
     const int wc0 = col0 + 32 * w;
     const bool has_cols = wc0 < ncols;                       // wave-uniform
+    // causal: the last position this lane's column sees (-1: a padding
+    // column), and the smallest and largest over the wave's live columns
+    int lim[2];
+    for (int nt = 0; nt < 2; ++nt) {
+        const int c = wc0 + 16 * nt + hl;
+        lim[nt] = c < ncols ? L - qr.n + c / G : -1;
+    }
+    const int wave_lo = L - qr.n + wc0 / G;
+    const int wave_hi = L - qr.n + min(qr.n - 1, (wc0 + 31) / G);
     bf16x8_t qf[2][KSTEPS];
     for (int nt = 0; nt < 2; ++nt) {
         const int c = wc0 + 16 * nt + hl;
@@ -222,7 +247,7 @@ __device__ __forceinline__ void decode_prefix_body(const DecodeParams& p, uint32
     for (int ci = 0; ci < nch; ++ci) {
         const int buf = ci & 1;
         if (ci + 1 < nch) load_chunk(ci + 1);                // in flight during the compute below
-        if (has_cols) {
+        if (has_cols && (!CAUSAL || start + ci * kTok <= wave_hi)) {
             const unsigned char* kb = lds + buf * (KBUF + VBUF);
             const unsigned char* vb = kb + KBUF;
             const int valid = min(kTok, end - (start + ci * kTok));
@@ -248,14 +273,19 @@ __device__ __forceinline__ void decode_prefix_body(const DecodeParams& p, uint32
             // max, and weight 0); the row sums add the bf16 weights the P.V
             // product uses, two per dot2.
             const bool partial = valid < kTok;                       // wave-uniform
+            // causal: some column of the wave stops inside this chunk
+            const bool cut_cols = CAUSAL && start + ci * kTok + kTok - 1 > wave_lo;
             bf16x8_t pf[2][kTok / 32];
-            if (partial) {
-                // drop the missing tokens' scores from the max (-inf) and their
-                // weights (0) once, here, so the common path below has no selects
-                for (int nt = 0; nt < 2; ++nt)
+            if (partial || cut_cols) {
+                // drop the missing (or, causal, unseen) tokens' scores from the
+                // max (-inf) and their weights (0) once, here, so the common
+                // path below has no selects
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int cut = CAUSAL ? min(valid, lim[nt] - (start + ci * kTok) + 1) : valid;
                     for (int rt = 0; rt < kTok / 16; ++rt)
                         for (int i = 0; i < 4; ++i)
-                            st[nt][rt][i] = 16 * rt + 4 * j + i < valid ? st[nt][rt][i] : neg_inf();
+                            st[nt][rt][i] = 16 * rt + 4 * j + i < cut ? st[nt][rt][i] : neg_inf();
+                }
             }
             for (int nt = 0; nt < 2; ++nt) {
                 float mx = st[nt][0][0];
@@ -295,8 +325,17 @@ __device__ __forceinline__ void decode_prefix_body(const DecodeParams& p, uint32
             // ---- P.V: V^T operands from LDS, one 16-byte read per lane and tile
             for (int s2 = 0; s2 < kTok / 32; ++s2)
                 for (int dc = 0; dc < DC; ++dc) {
-                    const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
+                    u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
                         vb + (16 * dc + r) * VROW + (((4 * s2 + j) ^ (r & 7)) * 16));
+                    if (CAUSAL && partial) {
+                        // dword q holds tokens 32 s2 + 16 (q / 2) + 4 j + 2 (q % 2) and the
+                        // next; past the context they may hold anything: zeroed, never
+                        // multiplied by a zero weight
+                        for (int q = 0; q < 4; ++q) {
+                            const int tok = 32 * s2 + 16 * (q / 2) + 4 * j + 2 * (q % 2);
+                            vf[q] &= (tok < valid ? 0x0000ffffu : 0u) | (tok + 1 < valid ? 0xffff0000u : 0u);
+                        }
+                    }
                     for (int nt = 0; nt < 2; ++nt)
                         acc[nt][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), pf[nt][s2],
                                                                               acc[nt][dc], 0, 0, 0);
@@ -306,6 +345,31 @@ __device__ __forceinline__ void decode_prefix_body(const DecodeParams& p, uint32
         __syncthreads();
     }
     if (!has_cols) return;
+
+    if (CAUSAL && !p.split) {
+        // ---- one pass: the output rows of this wave's columns, normalised;
+        // lane (c, j) holds dims 16 dc + 4 j + i
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+        for (int nt = 0; nt < 2; ++nt) {
+            float l = l_run[nt];
+            l = sum_xor16(l);
+            l = sum_xor32(l);
+            const int c = wc0 + 16 * nt + hl;
+            if (c >= ncols) continue;
+            const size_t orow = (size_t)(qr.row0 + c / G) * p.num_heads + (size_t)g * G + c % G;
+            for (int dc = 0; dc < DC; ++dc) {
+                uint32_t h2[2];
+                for (int k = 0; k < 2; ++k) {
+                    const uint32_t lo = f32_to_bf16(l > 0.f ? acc[nt][dc][2 * k] / l : 0.f);
+                    const uint32_t hi = f32_to_bf16(l > 0.f ? acc[nt][dc][2 * k + 1] / l : 0.f);
+                    h2[k] = lo | (hi << 16);
+                }
+                typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+                *reinterpret_cast<u32x2_t*>(out + orow * D + 16 * dc + 4 * j) = u32x2_t{h2[0], h2[1]};
+            }
+        }
+        return;
+    }
 
     // ---- partials of this wave's columns: lane (c, j) holds dims 16 dc + 4 j + i
     const int wsp = p.ws_parts > 0 ? p.ws_parts : p.max_parts;

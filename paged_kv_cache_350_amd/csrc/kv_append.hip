@@ -242,6 +242,52 @@ void append_newest_kernel(DecodeParams p) {
 
 }  // namespace
 
+// The new tokens' rows of a multi-query call (k_new / v_new [num_tokens]
+// [num_kv_heads][head_dim], aligned with the query rows) to positions
+// L - n .. L - 1 of their sequences: row t belongs to the last sequence b
+// with query_start[b] <= t, and goes in only if it is one of b's n rows (n
+// clamped as the multi-query kernel clamps it).  A page id outside the pool
+// writes nothing -- the multi-query kernel's own fused append exactly.
+template <typename E>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void append_multi_rows_kernel(DecodeParams p) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    if (row >= (int64_t)p.num_tokens * p.num_kv_heads) return;
+    const int t = (int)(row / p.num_kv_heads);
+    const int h = (int)(row % p.num_kv_heads);
+    const int bs = p.block_size;
+    const int D = p.head_dim;
+    const SourceRow<E> src = load_source(reinterpret_cast<const E*>(p.k_new) + row * D,
+                                         reinterpret_cast<const E*>(p.v_new) + row * D, lane, D);
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (p.query_start[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo;
+    const int cap = min(p.max_context_len, p.max_blocks_per_seq * bs);
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const QueryRows qr = query_rows(p.query_start, b, L, p.num_tokens, p.max_query_len);
+    if (t < qr.row0 || t >= qr.row0 + qr.n) return;
+    const int pos = L - qr.n + (t - qr.row0);
+    const int page = p.block_tables[(size_t)b * p.max_blocks_per_seq + pos / bs];
+    if ((uint32_t)page >= (uint64_t)p.num_blocks) return;
+    const int64_t tile = ((int64_t)page * p.num_kv_heads + h) * (int64_t)D * bs;
+    store_row(const_cast<E*>(reinterpret_cast<const E*>(p.k_cache)), const_cast<E*>(reinterpret_cast<const E*>(p.v_cache)),
+              tile, pos % bs, bs, D, lane, src);
+}
+
+hipError_t launch_append_multi_rows(const DecodeParams& p, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.num_tokens * p.num_kv_heads;
+    if (rows == 0 || p.num_seqs == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    hipLaunchKernelGGL(append_multi_rows_kernel<uint16_t>, grid, dim3(kRowsPerBlock * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_append_newest(const DecodeParams& p, pa_dtype dtype, hipStream_t stream) {
     const int64_t rows = (int64_t)p.num_seqs * p.num_kv_heads;
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));

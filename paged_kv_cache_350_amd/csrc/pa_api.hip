@@ -1024,13 +1024,33 @@ pa_status decode_multi_impl(const void* k_new, const void* v_new, const void* q,
         p.max_parts = 1;
         p.split = 0;
     }
-    // 4-wave workgroups.  8 (one per compute unit at this kernel's two waves
-    // per SIMD) measured faster without the fused append (speculative
-    // verification, 64 sequences x 5 queries: 104.6 against 108.2 us) and
-    // slower with it (116.9 against 114.9); pa_decode_multi_append must stay
-    // bit-identical to pa_kv_append + pa_decode_multi, so both keep 4.
-    p.waves = 4;
-    st = hip_status(pa_impl::launch_decode_multi(p, tiles, stream));
+    if ((int64_t)group * max_query_len >= kPrefixWideMinCols) {
+        // Many query columns per (sequence, kv head) -- a prompt chunk: the
+        // LDS-staged kernel stages each K/V chunk once for 128 columns, where
+        // the kernel below reads it once per 32 (and the product is dense
+        // enough for the matrix cores to matter).  The fused append stores
+        // the new rows in a launch of its own first, so it stays bit-identical
+        // to pa_kv_append + pa_decode_multi.
+        if (k_new) {
+            st = hip_status(pa_impl::launch_append_multi_rows(p, stream));
+            if (st != PA_OK) return st;
+        }
+        p.k_new = nullptr;
+        p.v_new = nullptr;
+        p.order_by_length = 0;
+        p.col_groups = (int32_t)(((int64_t)group * max_query_len + pa_impl::decode_prefix_columns() - 1) /
+                                 pa_impl::decode_prefix_columns());
+        st = hip_status(pa_impl::launch_decode_multi_wide(p, stream));
+    } else {
+        // 4-wave workgroups.  8 (one per compute unit at this kernel's two
+        // waves per SIMD) measured faster without the fused append
+        // (speculative verification, 64 sequences x 5 queries: 104.6 against
+        // 108.2 us) and slower with it (116.9 against 114.9);
+        // pa_decode_multi_append must stay bit-identical to pa_kv_append +
+        // pa_decode_multi, so both keep 4.
+        p.waves = 4;
+        st = hip_status(pa_impl::launch_decode_multi(p, tiles, stream));
+    }
     if (st != PA_OK || partition == 0) return st;
 
     ReduceParams r;

@@ -127,6 +127,12 @@ hipError_t launch_decode_prefix_rest(const DecodeParams& pre, const DecodeParams
 // shared-page loads, 4-wave workgroups, col_tiles 16-column tiles each)
 hipError_t launch_decode_multi_rest(const DecodeParams& pre, int col_tiles, const DecodeParams& rest,
                                     hipStream_t stream);
+// The LDS-staged kernel as the multi-query kernel of many columns per
+// (sequence, kv head): causal rows, col_groups groups of
+// decode_prefix_columns() columns, one pass (split 0) or partials.
+hipError_t launch_decode_multi_wide(const DecodeParams& p, hipStream_t stream);
+// A multi-query call's new rows (bf16) into their slots, before that kernel.
+hipError_t launch_append_multi_rows(const DecodeParams& p, hipStream_t stream);
 int decode_prefix_columns();
 int decode_prefix_chunk();
 

@@ -5,7 +5,12 @@ Every case appends the new tokens' K/V rows with pa_kv_append and then runs
 pa_decode_multi.  The oracle takes the caches as generated (before the
 append), applies its own append of the same rows and computes
 oracle.decode_multi in float64, so no oracle input comes from the device.
-Tolerances are the decode ones (bf16: max-abs 2e-2, relative L2 5e-3)."""
+Tolerances are the decode ones (bf16: max-abs 2e-2, relative L2 5e-3).
+
+Two kernels serve the call: below 64 query columns per (sequence, kv head)
+(G heads x n new tokens) the per-wave-loads multi-query kernel, from 64 on
+(a prompt chunk) the LDS-staged kernel with causal rows.  Each has tests of
+its own below; the shared ones cover whichever the shape picks."""
 
 import numpy as np
 import pytest
@@ -53,6 +58,29 @@ def prepare(w):
     t = W.make_tensors(w, "cuda")
     w._k_new, w._v_new = storage_np(t["k_new"]), storage_np(t["v_new"])
     return t, storage_np(t["k_cache"]), storage_np(t["v_cache"]), storage_np(t["q"])
+
+
+def narrow_news(group):
+    """NEWS capped so that group x n stays below 64 columns: the per-wave
+    kernel, whatever the head shape."""
+    return [min(n, max(1, 63 // group)) for n in NEWS]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_multi_narrow_matches_oracle(shape):
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    news = narrow_news(hq // hkv)
+    assert (hq // hkv) * max(news) < 64
+    w = W.multi_custom("narrow_multi", 47, LENS, news, hq, hkv, d, bs)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    for P in PARTS:
+        t2 = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("narrow multi", shape, "partition", P, w.summary())
+        out = run_gpu(pa, w, t2, partition_size=P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"narrow {shape} P={P}")
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
@@ -176,12 +204,13 @@ def test_fused_append_equals_append_then_multi(shape):
 
 
 def test_fused_append_many_new_rows():
-    """More new rows per workgroup than one wave's LDS slice holds (17 to
-    32: the workgroup copies them to LDS before its loop) and more than that
-    (stored first): bit-identical to pa_kv_append + pa_decode_multi and
-    within tolerance of the oracle."""
+    """The per-wave kernel (one head per kv head, so 40 new tokens stay
+    below 64 columns) with more new rows per workgroup than one wave's LDS
+    slice holds (17 to 32: the workgroup copies them to LDS before its loop)
+    and more than that (stored first): bit-identical to pa_kv_append +
+    pa_decode_multi and within tolerance of the oracle."""
     pa = require_gpu()
-    w = W.multi_custom("many_new", 50, [20, 45, 300, 700, 33], [20, 33, 17, 40, 32], 32, 8, 128, 16)
+    w = W.multi_custom("many_new", 50, [20, 45, 300, 700, 33], [20, 33, 17, 40, 32], 8, 8, 128, 16)
     t, kc0, vc0, q = prepare(w)
     ref = oracle_multi(w, kc0, vc0, q)
     for P in (-1, 64):
@@ -271,3 +300,65 @@ def test_one_pass_order_by_length_either_side_of_the_limit(nseq):
     rows = np.concatenate([np.arange(w.query_start[b], w.query_start[b + 1]) for b in seqs])
     check_close(out_f64(out)[rows], ref[rows], "bf16", f"order {nseq}")
     assert np.isfinite(out_f64(out)).all()
+
+
+# Prompt chunks: many new tokens per sequence (up to all of its context, a
+# whole prompt), some sequences with none, several 128-column groups.
+CHUNK_LENS = [300, 1, 97, 640, 129, 1000, 512, 64]
+CHUNK_NEWS = [300, 1, 0, 200, 64, 333, 17, 64]
+CHUNK_SHAPES = [  # (block_size, num_heads, num_kv_heads, head_dim)
+    (16, 32, 8, 128),
+    (32, 32, 8, 128),
+    (16, 64, 8, 128),
+    (32, 16, 2, 64),
+    (16, 8, 8, 64),
+]
+
+
+@pytest.mark.parametrize("shape", CHUNK_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_prompt_chunks_match_oracle(shape):
+    """The LDS-staged kernel with causal rows: chunks that end inside a page
+    (its stale tail zeroed), columns that stop inside a chunk, waves whose
+    columns see nothing of a partition, one pass and split."""
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    assert (hq // hkv) * max(CHUNK_NEWS) >= 64
+    w = W.multi_custom("prompt_chunks", 48, CHUNK_LENS, CHUNK_NEWS, hq, hkv, d, bs)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    for P in (-1, 0, 64, 256):
+        t2 = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("prompt chunks", shape, "partition", P, w.summary())
+        out = run_gpu(pa, w, t2, partition_size=P)
+        torch.cuda.synchronize()
+        check_close(out_f64(out), ref, "bf16", f"prompt chunks {shape} P={P}")
+        again = run_gpu(pa, w, {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()},
+                        partition_size=P)
+        torch.cuda.synchronize()
+        assert bits_equal(out, again), f"repeat {shape} P={P}"
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 8, 128), (32, 16, 2, 64)], ids=lambda s: "-".join(map(str, s)))
+def test_prompt_chunk_fused_append(shape):
+    """pa_decode_multi_append on the LDS-staged kernel (its rows stored by a
+    launch of their own first) = pa_kv_append + pa_decode_multi, bit for bit
+    (outputs and whole caches), and within tolerance of the oracle."""
+    pa = require_gpu()
+    bs, hq, hkv, d = shape
+    w = W.multi_custom("prompt_chunk_fused", 49, CHUNK_LENS, CHUNK_NEWS, hq, hkv, d, bs)
+    t, kc0, vc0, q = prepare(w)
+    ref = oracle_multi(w, kc0, vc0, q)
+    kc_ref, vc_ref = oracle.kv_append(w._k_new, w._v_new, w.append_slots, kc0, vc0, bs)
+    for P in (-1, 128):
+        a = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        b = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+        say("prompt chunk fused append", shape, "partition", P)
+        out_a = run_gpu(pa, w, a, partition_size=P)
+        out_b = pa.decode_multi(b["q"], b["k_cache"], b["v_cache"], b["block_tables"], b["context_lens"],
+                                b["query_start"], w.scale, w.max_context_len, w.max_query_len, partition_size=P,
+                                k_new=b["k_new"], v_new=b["v_new"])
+        torch.cuda.synchronize()
+        assert bits_equal(out_a, out_b), P
+        assert np.array_equal(storage_np(b["k_cache"]), kc_ref), P
+        assert np.array_equal(storage_np(b["v_cache"]), vc_ref), P
+        check_close(out_f64(out_b), ref, "bf16", f"prompt chunk fused {shape} P={P}")

@@ -118,3 +118,21 @@ def test_make_tensors_poisons_non_resident_slots():
     # same seed, same values
     t2 = W.make_tensors(w, "cpu")
     assert torch.equal(t["q"], t2["q"])
+
+
+def test_prompt_chunk_and_multi_flops():
+    """The chunked-prefill workload's shape, and the multi-query flop count
+    against positions counted one by one: query j of a sequence with n new
+    tokens sees L - n + j + 1 positions, each costing 4 D flops per head."""
+    w = W.prompt_chunk()
+    assert (w.num_seqs, w.max_query_len, w.max_context_len) == (8, 512, 4096)
+    assert (w.num_heads, w.num_kv_heads, w.head_dim, w.block_size) == (32, 8, 128, 16)
+    assert len(w.append_slots) == 8 * 512
+    small = W.multi_custom("flops", 1, [5, 3, 7], [2, 3, 0], 8, 2, 64, 16)
+    seen = 0
+    for L, n in ((5, 2), (3, 3), (7, 0)):
+        for j in range(n):
+            seen += L - n + j + 1
+    assert seen == (4 + 5) + (1 + 2 + 3)
+    assert small.multi_flops() == 4 * 64 * 8 * seen
+    assert w.multi_flops() == 4 * 128 * 32 * 8 * sum(3584 + j + 1 for j in range(512))

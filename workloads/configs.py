@@ -135,6 +135,18 @@ class Workload:
         """K/V bytes one decode step must read: every context token once per kv head."""
         return int(self.context_lens.astype(np.int64).sum()) * self.kv_bytes_per_token()
 
+    def multi_flops(self) -> int:
+        """Multiply-adds x 2 of the attention a multi-query step computes: each
+        query row j of a sequence with n new tokens sees L - n + j + 1
+        positions, and costs 2 D flops per position for Q.K^T and 2 D for
+        P.V, for every query head."""
+        total = 0
+        news = np.ones(self.num_seqs, dtype=np.int64) if self.query_lens is None else self.query_lens
+        for L, n in zip(self.context_lens.astype(np.int64), np.asarray(news, dtype=np.int64)):
+            n = min(int(n), int(L))
+            total += n * (int(L) - n) + n * (n + 1) // 2
+        return 4 * self.head_dim * self.num_heads * total
+
     def unique_kv_bytes(self) -> int:
         """Bytes of distinct (page, offset) slots read, for shared-page workloads."""
         bs = self.block_size
@@ -479,6 +491,22 @@ def spec_verify(seed: int = 5, num_seqs: int = 64, len_range: Tuple[int, int] = 
                   seed, lens, news, 32, 8, 128, 16, rng, manager=manager,
                   description=f"{num_seqs} seqs, L~U[{len_range[0]},{len_range[1]}], {drafts + 1} queries "
                               f"each (verify {drafts} drafts), 32/8 heads, D 128, bs 16, bf16")
+
+
+def prompt_chunk(seed: int = 6, num_seqs: int = 8, context: int = 4096, chunk: int = 512,
+                 manager=None) -> Workload:
+    """Chunked prefill on the Llama-3-8B-shaped heads: every sequence holds
+    ``context - chunk`` tokens and appends the next ``chunk`` tokens of its
+    prompt, whose queries attend causally (n = chunk queries each); 32 q / 8
+    kv heads, head_dim 128, block 16, bf16."""
+    rng = np.random.default_rng(seed)
+    lens = np.full(num_seqs, context)
+    news = np.full(num_seqs, chunk)
+    return _multi("prompt_chunk" if (num_seqs, context, chunk) == (8, 4096, 512) else
+                  f"prompt_chunk_b{num_seqs}_l{context}_c{chunk}",
+                  seed, lens, news, 32, 8, 128, 16, rng, manager=manager,
+                  description=f"{num_seqs} seqs x {chunk} prompt tokens over {context - chunk} cached "
+                              f"(chunked prefill), 32/8 heads, D 128, bs 16, bf16")
 
 
 def multi_custom(name: str, seed: int, lens, news, num_heads: int, num_kv_heads: int, head_dim: int,
