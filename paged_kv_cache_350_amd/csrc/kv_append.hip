@@ -108,10 +108,45 @@ void kv_append_kernel(const E* __restrict__ k, const E* __restrict__ v,
 constexpr int kTileThreads = 256;
 constexpr int kTileWindow = 32;
 
-template <typename E, int D>
+// Where token t's rows go, as its slot (page * block_size + offset; negative
+// or past the pool: nowhere): pa_kv_append's slot mapping ...
+struct SlotsFromMapping {
+    const int64_t* slots;
+    __device__ int64_t operator()(int64_t t) const { return slots[t]; }
+};
+
+// ... or a multi-query call's new rows: row t belongs to the last sequence b
+// with query_start[b] <= t and goes to position L - n + (t - row0) if it is
+// one of b's n rows (n clamped as the multi-query kernels clamp it), through
+// b's table row; a page id outside the pool writes nothing.
+struct SlotsFromQueries {
+    const int32_t* query_start;
+    const int32_t* context_lens;
+    const int32_t* block_tables;
+    int32_t num_seqs, num_tokens, max_query_len, max_blocks_per_seq, max_context_len, block_size;
+    int64_t num_blocks;
+    __device__ int64_t operator()(int64_t t) const {
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (query_start[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const int cap = min(max_context_len, max_blocks_per_seq * block_size);
+        int L = context_lens[lo];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        const QueryRows qr = query_rows(query_start, lo, L, num_tokens, max_query_len);
+        if (t < qr.row0 || t >= qr.row0 + qr.n) return -1;
+        const int pos = L - qr.n + (int)(t - qr.row0);
+        const int page = block_tables[(size_t)lo * max_blocks_per_seq + pos / block_size];
+        if ((uint32_t)page >= (uint64_t)num_blocks) return -1;
+        return (int64_t)page * block_size + pos % block_size;
+    }
+};
+
+template <typename E, int D, typename Slots>
 __global__ __launch_bounds__(kTileThreads)
-void kv_append_tile_kernel(const E* __restrict__ k, const E* __restrict__ v,
-                           const int64_t* __restrict__ slot_mapping,
+void kv_append_tile_kernel(const E* __restrict__ k, const E* __restrict__ v, Slots slot_of,
                            E* __restrict__ k_cache, E* __restrict__ v_cache,
                            int32_t num_tokens, int32_t num_kv_heads, int32_t block_size,
                            int64_t num_blocks) {
@@ -138,8 +173,8 @@ void kv_append_tile_kernel(const E* __restrict__ k, const E* __restrict__ v,
     const int64_t t = w0 + tid;
     int64_t slot = -1, prev = -1;
     if (tid < TGX && t < num_tokens) {
-        slot = slot_mapping[t];
-        if (t > 0) prev = slot_mapping[t - 1];
+        slot = slot_of(t);
+        if (t > 0) prev = slot_of(t - 1);
     }
     const bool valid = slot >= 0 && slot < nslots;            // padding / out of range: skipped
     const bool starts = t >= num_tokens || !valid || t == 0 || slot % block_size == 0 || prev < 0 ||
@@ -178,6 +213,9 @@ void kv_append_tile_kernel(const E* __restrict__ k, const E* __restrict__ v,
     for (int i = tid; i < ntok * CH; i += kTileThreads) {
         const int j = i / CH;
         const int c = i % CH;
+        // rows past the last token (one-token segments of their own) are
+        // never stored: nothing to load for them
+        if (w0 + begin + j >= num_tokens) continue;
         const int64_t src = ((w0 + begin + j) * num_kv_heads + h) * (int64_t)D + (int64_t)c * X;
         sk[j * RS + c] = ld16(k + src);
         sv[j * RS + c] = ld16(v + src);
@@ -242,52 +280,6 @@ void append_newest_kernel(DecodeParams p) {
 
 }  // namespace
 
-// The new tokens' rows of a multi-query call (k_new / v_new [num_tokens]
-// [num_kv_heads][head_dim], aligned with the query rows) to positions
-// L - n .. L - 1 of their sequences: row t belongs to the last sequence b
-// with query_start[b] <= t, and goes in only if it is one of b's n rows (n
-// clamped as the multi-query kernel clamps it).  A page id outside the pool
-// writes nothing -- the multi-query kernel's own fused append exactly.
-template <typename E>
-__global__ __launch_bounds__(kRowsPerBlock * kWave)
-void append_multi_rows_kernel(DecodeParams p) {
-    const int lane = threadIdx.x % kWave;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-    if (row >= (int64_t)p.num_tokens * p.num_kv_heads) return;
-    const int t = (int)(row / p.num_kv_heads);
-    const int h = (int)(row % p.num_kv_heads);
-    const int bs = p.block_size;
-    const int D = p.head_dim;
-    const SourceRow<E> src = load_source(reinterpret_cast<const E*>(p.k_new) + row * D,
-                                         reinterpret_cast<const E*>(p.v_new) + row * D, lane, D);
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (p.query_start[mid] <= t) lo = mid;
-        else hi = mid - 1;
-    }
-    const int b = lo;
-    const int cap = min(p.max_context_len, p.max_blocks_per_seq * bs);
-    int L = p.context_lens[b];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    const QueryRows qr = query_rows(p.query_start, b, L, p.num_tokens, p.max_query_len);
-    if (t < qr.row0 || t >= qr.row0 + qr.n) return;
-    const int pos = L - qr.n + (t - qr.row0);
-    const int page = p.block_tables[(size_t)b * p.max_blocks_per_seq + pos / bs];
-    if ((uint32_t)page >= (uint64_t)p.num_blocks) return;
-    const int64_t tile = ((int64_t)page * p.num_kv_heads + h) * (int64_t)D * bs;
-    store_row(const_cast<E*>(reinterpret_cast<const E*>(p.k_cache)), const_cast<E*>(reinterpret_cast<const E*>(p.v_cache)),
-              tile, pos % bs, bs, D, lane, src);
-}
-
-hipError_t launch_append_multi_rows(const DecodeParams& p, hipStream_t stream) {
-    const int64_t rows = (int64_t)p.num_tokens * p.num_kv_heads;
-    if (rows == 0 || p.num_seqs == 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    hipLaunchKernelGGL(append_multi_rows_kernel<uint16_t>, grid, dim3(kRowsPerBlock * kWave), 0, stream, p);
-    return hipGetLastError();
-}
-
 hipError_t launch_append_newest(const DecodeParams& p, pa_dtype dtype, hipStream_t stream) {
     const int64_t rows = (int64_t)p.num_seqs * p.num_kv_heads;
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
@@ -299,14 +291,14 @@ hipError_t launch_append_newest(const DecodeParams& p, pa_dtype dtype, hipStream
     return hipGetLastError();
 }
 
-template <typename E, int D>
-hipError_t launch_tile(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+template <typename E, int D, typename Slots = SlotsFromMapping>
+hipError_t launch_tile(const void* k, const void* v, Slots slots, void* k_cache,
                        void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t block_size,
                        int64_t num_blocks, hipStream_t stream) {
     constexpr int TG = kTileWindow;
     const dim3 grid((unsigned)(((int64_t)num_tokens + TG - 1) / TG), (unsigned)num_kv_heads);
-    hipLaunchKernelGGL((kv_append_tile_kernel<E, D>), grid, dim3(kTileThreads), 0, stream,
-                       (const E*)k, (const E*)v, slot_mapping, (E*)k_cache, (E*)v_cache, num_tokens,
+    hipLaunchKernelGGL((kv_append_tile_kernel<E, D, Slots>), grid, dim3(kTileThreads), 0, stream,
+                       (const E*)k, (const E*)v, slots, (E*)k_cache, (E*)v_cache, num_tokens,
                        num_kv_heads, block_size, num_blocks);
     return hipGetLastError();
 }
@@ -317,13 +309,13 @@ hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slot_ma
                             int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
     if (num_tokens >= kTileMinTokens && num_kv_heads <= 65535) {
         if (dtype == PA_BF16)
-            return head_dim == 128 ? launch_tile<uint16_t, 128>(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+            return head_dim == 128 ? launch_tile<uint16_t, 128>(k, v, SlotsFromMapping{slot_mapping}, k_cache, v_cache, num_tokens,
                                                                num_kv_heads, block_size, num_blocks, stream)
-                                   : launch_tile<uint16_t, 64>(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+                                   : launch_tile<uint16_t, 64>(k, v, SlotsFromMapping{slot_mapping}, k_cache, v_cache, num_tokens,
                                                               num_kv_heads, block_size, num_blocks, stream);
-        return head_dim == 128 ? launch_tile<uint32_t, 128>(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+        return head_dim == 128 ? launch_tile<uint32_t, 128>(k, v, SlotsFromMapping{slot_mapping}, k_cache, v_cache, num_tokens,
                                                            num_kv_heads, block_size, num_blocks, stream)
-                               : launch_tile<uint32_t, 64>(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+                               : launch_tile<uint32_t, 64>(k, v, SlotsFromMapping{slot_mapping}, k_cache, v_cache, num_tokens,
                                                           num_kv_heads, block_size, num_blocks, stream);
     }
     const int64_t rows = (int64_t)num_tokens * num_kv_heads;
@@ -341,6 +333,24 @@ hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slot_ma
                            num_kv_heads, head_dim, block_size, num_blocks);
     }
     return hipGetLastError();
+}
+
+// A multi-query call's new rows (bf16, k_new / v_new aligned with the query
+// rows) into their slots: the page-segment tile kernel, each row's slot
+// found from query_start and the block table, so a prompt chunk's rows --
+// runs of consecutive positions -- land in whole page rows.
+hipError_t launch_append_multi_rows(const DecodeParams& p, hipStream_t stream) {
+    if (p.num_tokens == 0 || p.num_seqs == 0) return hipSuccess;
+    const SlotsFromQueries slots{p.query_start, p.context_lens, p.block_tables, p.num_seqs, p.num_tokens,
+                                 p.max_query_len, p.max_blocks_per_seq, p.max_context_len, p.block_size,
+                                 p.num_blocks};
+    return p.head_dim == 128
+               ? launch_tile<uint16_t, 128>(p.k_new, p.v_new, slots, const_cast<void*>(p.k_cache),
+                                            const_cast<void*>(p.v_cache), p.num_tokens, p.num_kv_heads,
+                                            p.block_size, p.num_blocks, stream)
+               : launch_tile<uint16_t, 64>(p.k_new, p.v_new, slots, const_cast<void*>(p.k_cache),
+                                           const_cast<void*>(p.v_cache), p.num_tokens, p.num_kv_heads,
+                                           p.block_size, p.num_blocks, stream);
 }
 
 }  // namespace pa_impl
