@@ -24,6 +24,7 @@ constexpr int32_t kMaxGroup = 16;            // query heads per kv head
 constexpr uint64_t kMaxGrid = 1ull << 31;    // workgroups per launch
 constexpr int32_t kMaxQueryLen = 1024;       // multi-query: new tokens per sequence
 constexpr int64_t kMultiFill = 256;          // multi-query: workgroups that keep every CU busy
+constexpr int64_t kMultiWideFill = 512;      // the same for the LDS-staged kernel (two per CU)
 constexpr int32_t kMultiMaxPartition = 8192;
 constexpr int64_t kPrefixFill = 512;         // shared-prefix launch: workgroups that fill the chip (two per CU)
 // shared-prefix call, partition_size 0: measured best on 100 sequences over a
@@ -371,11 +372,11 @@ int32_t multi_col_groups(int32_t group, int32_t max_query_len) {
 // full: one pass when (sequence, column group, kv head) units alone fill it,
 // else the longest power-of-two partition in [kMinPartition,
 // kMultiMaxPartition] that does (kMinPartition when none does).
-int32_t default_multi_partition(int64_t units, int32_t max_context_len) {
-    if (max_context_len <= kSplitAbove || units >= kMultiFill) return 0;
+int32_t default_multi_partition(int64_t units, int32_t max_context_len, int64_t fill) {
+    if (max_context_len <= kSplitAbove || units >= fill) return 0;
     for (int32_t P = kMultiMaxPartition; P >= kMinPartition; P /= 2) {
         if (P >= max_context_len) continue;         // one partition: a single pass does it without the merge
-        if (units * parts_for(max_context_len, P) >= kMultiFill) return P;
+        if (units * parts_for(max_context_len, P) >= fill) return P;
     }
     return kMinPartition;
 }
@@ -387,9 +388,18 @@ int32_t resolve_multi_partition(int32_t num_seqs, int32_t num_heads, int32_t num
     if (partition_size != 0)
         return resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size, true);
     if (max_context_len < 0) return -1;
-    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) *
-                          multi_col_groups(num_heads / num_kv_heads, max_query_len) * num_kv_heads;
-    return default_multi_partition(units, max_context_len);
+    // From kPrefixWideMinCols columns per (sequence, kv head) the LDS-staged
+    // kernel runs, with 128-column groups and two workgroups per compute
+    // unit.  Measured, 16 sequences x L U[512, 4096], 4 heads per kv head,
+    // n = 16 / 32 / 64 new tokens: one pass (128 / 128 / 256 workgroups)
+    // 135 / 138 / 142 us, split to reach 512 workgroups 62 / 72 / 123 us
+    // (the per-wave kernel: 62 / 110 / 207 us).
+    const int32_t group = num_heads / num_kv_heads;
+    const bool wide = (int64_t)group * max_query_len >= kPrefixWideMinCols;
+    const int64_t cols_per_group = wide ? pa_impl::decode_prefix_columns() : 16 * multi_col_tiles(group, max_query_len);
+    const int64_t col_groups = ((int64_t)group * max_query_len + cols_per_group - 1) / cols_per_group;
+    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * col_groups * num_kv_heads;
+    return default_multi_partition(units, max_context_len, wide ? kMultiWideFill : kMultiFill);
 }
 
 }  // namespace

@@ -251,7 +251,11 @@ def test_decode_multi_partition_policy(L):
     assert f(4, 32, 8, 8192, 8, 0) == 1024        # 32 units x 8 partitions
     assert f(8, 32, 8, 32768, 5, 0) == 8192       # long contexts: 64 units x 4
     assert f(2, 32, 8, 600, 5, 0) == 256          # nothing fills the chip: the shortest partition
-    assert f(16, 32, 8, 4094, 16, 0) == 0         # 4 x 16 = 64 columns: two column groups, 256 units
+    # from 64 columns (4 x 16) the LDS-staged kernel: one 128-column group, 128 units, four partitions
+    # reach its fill of 512 workgroups
+    assert f(16, 32, 8, 4094, 16, 0) == 1024
+    assert f(64, 32, 8, 4096, 16, 0) == 0         # 512 units: one pass
+    assert f(8, 32, 8, 4096, 512, 0) == 0         # a prompt chunk: 16 column groups, 1,024 units
     # workspace rows are query tokens
     want = 320 * 32 * (-(-4096 // 256)) * (128 + 2) * 4
     assert pa.decode_multi_workspace_size(64, 320, 32, 8, 128, 4096, 5, 256) == want
