@@ -8,8 +8,8 @@ namespace {
 
 using namespace mfma_detail;
 
-// (6-wave workgroups are held to three waves per SIMD; they still run one per
-// compute unit at a time)
+// (5-wave workgroups are held to three waves per SIMD, so two of them fit on
+// one compute unit: 3 + 3 + 2 + 2 waves over its four SIMDs)
 template <int D, int BS, bool SPLIT, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave, WAVES == kPairWaves ? 3 : 1)
 void decode_mfma_kernel(DecodeParams p) {
@@ -42,7 +42,7 @@ hipError_t launch_path(const DecodeParams& p, hipStream_t stream) {
 // workgroups share a compute unit, so one's set-up and merge overlap the
 // others' streaming), 12 waves (one workgroup fills a compute unit, three
 // times the bytes in flight for one (sequence, kv head, partition), which
-// drains long and ragged work units faster) and 6 waves (for a
+// drains long and ragged work units faster) and 5 waves (for a
 // longest-first single pass).  Shared-page loads always use 4.
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
     if (!p.stream_kv) return launch_path<false, 4>(p, stream);

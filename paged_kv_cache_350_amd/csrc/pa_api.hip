@@ -288,12 +288,12 @@ pa_status make_plan(const void* q, const void* k_cache, const void* v_cache,
     // 12-wave workgroups for long streaming work units: partitions of
     // kWidePartition tokens or more, or a single pass over enough pairs.  A
     // longest-first single pass (two to four rounds of 12 waves) runs
-    // 6-wave workgroups instead (8B-shaped step, 512 pairs: 94.4 -> 93.4 us;
-    // 4-wave workgroups capped at three per SIMD 100.3).  They run one per
-    // compute unit at a time -- a per-workgroup timeline shows 256 resident,
-    // the second of a pair of workgroups finding no SIMD with room for its
-    // waves -- so the 512 pairs go in two rounds, longest first, and the
-    // stream holds 7.0 TB/s between the ramp and the tail.
+    // 5-wave workgroups instead (8B-shaped launch, 512 pairs: 12 waves 94.4,
+    // 8 waves 94.2, 6 waves 93.8, 5 waves 93.4 us; 4-wave workgroups capped
+    // at three per SIMD 100.3).  Held to three waves per SIMD, two 5-wave
+    // workgroups fit on one compute unit where two 6-wave ones do not (a
+    // per-workgroup timeline of the 6-wave kernel shows 256 resident), so
+    // the pairs go longest first with twice as many in flight.
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
     const bool ordered = p.stream_kv && partition == 0 && ordered_one_pass(num_seqs, num_kv_heads, max_context_len);
     p.waves = p.stream_kv && (partition >= kWidePartition ||

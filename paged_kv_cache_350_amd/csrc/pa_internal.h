@@ -11,7 +11,7 @@ namespace pa_impl {
 
 // Everything a decode launch needs, resolved and validated on the host.
 constexpr int kWideWaves = 12;   // decode workgroup that fills a compute unit (3 waves per SIMD)
-constexpr int kPairWaves = 6;    // decode workgroup of the longest-first single pass
+constexpr int kPairWaves = 5;    // decode workgroup of the longest-first single pass
 constexpr int kSortMax = 256;    // sequences the kernels rank for longest-first order
 
 struct DecodeParams {
