@@ -131,7 +131,14 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeParams& p, uint32_t
     int L = p.context_lens[b];
     const int cap = min(p.max_context_len, p.max_blocks_per_seq * BS);
     L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int part = partition_of(slot, p.max_parts, L, p.partition, SPLIT);
+    // With a shared length per sequence (the grouped call, shared-page loads)
+    // slot s is the s-th partition from the one holding the sequence's first
+    // private position: the host knows no lower bound on those lengths, so
+    // the grid keeps every slot, and this order puts each sequence's own
+    // work first and the slots past its end (which return at once) last.
+    const int part = (!SPLIT && p.seq_first)
+                         ? own_partition(slot, p.seq_first[b], L, p.partition)
+                         : partition_of(slot, p.max_parts, L, p.partition, SPLIT);
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     const size_t head0 = (size_t)b * p.num_heads + (size_t)g * G;
     if (part < 0) {

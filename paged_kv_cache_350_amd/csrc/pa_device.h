@@ -181,6 +181,14 @@ __device__ __forceinline__ int partition_of(int slot, int max_parts, int L, int 
     return k < nparts ? nparts - 1 - k : -1;
 }
 
+// Partition handled by slot `slot` when positions below `first` are read by
+// another launch: slots count from the partition that holds `first`; -1 past
+// the sequence's end.
+__device__ __forceinline__ int own_partition(int slot, int first, int L, int P) {
+    const int part = (first > 0 ? first : 0) / P + slot;
+    return (int64_t)part * P < L ? part : -1;
+}
+
 // Multi-query launches: the query rows of sequence b are row0 .. row0 + n - 1,
 // taken from query_start[b] and query_start[b + 1] (or, with no query_start,
 // rows b * max_query_len onwards) and clamped so that every row lies in
